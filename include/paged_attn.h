@@ -1,0 +1,173 @@
+/*
+ * paged_attn.h: C ABI of the MI355X (gfx950) paged-KV grouped-query decode
+ * attention library, libpaged_attn.so.
+ *
+ * The operation is the one the docs.rs source page "onnxruntime-ep-mlx 0.31.1:
+ * src/ops/paged_attention.rs" implements for Apple GPUs (kernel text
+ * VECTOR_BODY, VECTOR_REDUCE, VECTOR_PARTIALS, PARTIALS_REDUCE; host launcher
+ * vector()). For every sequence b, query head h and new row r:
+ *
+ *   kh       = h / (H / KV)                         (GQA: a group of H/KV query
+ *                                                    heads shares KV head kh)
+ *   visible  = cached positions i < L_b, read through the block table, then
+ *              new rows j of this step: j <= r when causal, all NQ otherwise
+ *   s_i      = scale * <q[b,h,r,:], k_i>
+ *   out      = sum_i softmax(s)_i * v_i             (0 if nothing is visible)
+ *
+ * computed with an fp32 online softmax (running max and sum), optionally split
+ * into key partitions whose partial states are merged by a second kernel.
+ *
+ * Conventions shared by every entry point
+ *   - All pointers to tensors are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees, copies to the host or synchronises in
+ *     paged_attn_decode / paged_attn_combine. Tensors are contiguous row-major.
+ *   - Element type of q, pools, new_k, new_v and out: pa_problem.dtype.
+ *   - Layouts:
+ *       q, out        [batch, num_heads, nq, head_dim]
+ *       k_pool/v_pool [num_blocks, block_size, num_kv_heads, head_dim]
+ *       block_table   int32 [batch, max_blocks_per_seq]; entry [b, n] is the
+ *                     physical block holding cached positions n*block_size ..
+ *       context_lens  int32 [batch]: cached (past) length of each sequence,
+ *                     the nq new rows NOT included
+ *       new_k/new_v   [batch, num_kv_heads, nq, head_dim]: this step's rows,
+ *                     attended directly (they are not read from the pool)
+ *   - Alignment: tensor pointers 16-byte aligned, block_table/context_lens
+ *     4-byte aligned, workspace 16-byte aligned.
+ *   - Device-side contract (not checked on the hot path):
+ *       0 <= context_lens[b] <= max_context_len <= max_blocks_per_seq*block_size
+ *       0 <= block_table[b, n] < num_blocks for n < ceil(context_lens[b]/block_size)
+ *     Table entries past a sequence's last page and the unused slots of its
+ *     last page are never read. Pools are read-only, so one physical block may
+ *     appear in several sequences' tables.
+ *   - Errors: every call returns a pa_status; on failure a thread-local
+ *     message (paged_attn_last_error) says what was wrong and what to verify.
+ *     Argument checks run on the host before any HIP call.
+ *   - Supported shapes: head_dim 64 or 128; block_size 16 or 32; nq >= 1;
+ *     (num_heads/num_kv_heads)*nq <= 128; dtype PA_F32, PA_F16 or PA_BF16.
+ *     Device: gfx950 (MI355X) only.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. NULL selects the null stream of the current device. */
+typedef struct ihipStream_t* pa_stream_t;
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, inconsistent sizes */
+    PA_ERR_UNSUPPORTED = 2, /* well-formed but outside the supported shapes */
+    PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    PA_ERR_DEVICE = 4,      /* no usable device, or the device is not gfx950 */
+    PA_ERR_LAUNCH = 5       /* the HIP runtime reported a launch failure */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Kernel family for pass 1 (pa_problem.kernel and pa_plan_ex output). */
+typedef enum {
+    PA_KERNEL_AUTO = 0, /* chosen by the launch heuristic */
+    PA_KERNEL_VALU = 1, /* vector-ALU scores and PV, DPP reductions */
+    PA_KERNEL_MFMA = 2  /* matrix-core scores and PV (16-bit dtypes only) */
+} pa_kernel;
+
+/*
+ * Problem description. The fields mirror the compile-time constants of the
+ * page's vector() launcher (H, KV, D, BLOCK, MAX_BLOCKS, NQ, CAUSAL and the
+ * `length` the partition count is chosen from), plus a batch dimension.
+ */
+typedef struct {
+    int32_t batch;              /* B >= 0 (0: nothing to do) */
+    int32_t num_heads;          /* H >= 1 */
+    int32_t num_kv_heads;       /* KV >= 1, H % KV == 0 */
+    int32_t head_dim;           /* D: 64 or 128 */
+    int32_t block_size;         /* BS: tokens per page, 16 or 32 */
+    int32_t num_blocks;         /* pool capacity (dim 0 of k_pool/v_pool), >= 1 */
+    int32_t max_blocks_per_seq; /* block_table row stride, >= 0 */
+    int32_t nq;                 /* new rows per sequence, >= 1 */
+    int32_t causal;             /* 1: new row r sees new rows 0..r; 0: all nq */
+    int32_t dtype;              /* pa_dtype */
+    int32_t max_context_len;    /* host-side upper bound of context_lens, >= 0 */
+    int32_t num_partitions;     /* 0: heuristic; 1: single pass; > 1: at most this many
+                                   key partitions per sequence (tests, tuning) */
+    int32_t kernel;             /* pa_kernel; PA_KERNEL_AUTO unless forcing a family */
+} pa_problem;
+
+/*
+ * Launch plan, a pure host function of the problem and the number of compute
+ * units of the device (the page's partitions() plays this role: it picks the
+ * partition count from the context length and the number of query rows).
+ * Outputs: partitions = key partitions per sequence (1 = single pass, no
+ * workspace, no combine), chunk_tokens = cached tokens per partition (a
+ * multiple of block_size), kernel = pa_kernel family used for pass 1.
+ * Any output pointer may be NULL. No HIP call is made.
+ */
+int pa_plan_ex(const pa_problem* problem, int32_t num_cus, int32_t* partitions,
+               int32_t* chunk_tokens, int32_t* kernel);
+
+/* pa_plan_ex for the current HIP device (its compute-unit count is queried once
+ * per device and cached). Fails with PA_ERR_DEVICE if the device is not gfx950. */
+int pa_plan(const pa_problem* problem, int32_t* partitions, int32_t* chunk_tokens,
+            int32_t* kernel);
+
+/*
+ * Workspace bytes paged_attn_decode needs on the current device: 0 for a
+ * single-pass plan, else rows * partitions * (head_dim + 2) * 4 with
+ * rows = batch * num_heads * nq. Layout (fp32), row = (b*H + h)*nq + r:
+ *   o[row][p][head_dim]  unnormalised partial output  sum_i 2^(t_i - m) v_i
+ *   ml[row][p][2]        (m, l): m = max_i t_i, l = sum_i 2^(t_i - m)
+ * where t_i = s_i * log2(e), over the keys of partition p of that row: the
+ * page's VECTOR_PARTIALS state in base-2 units. Partitions past a sequence's
+ * last one are not written, and neither are the rows of a sequence whose keys
+ * fit in one partition (pass 1 writes their final output directly).
+ * pa_workspace_size_ex is the same for a device with num_cus compute units
+ * (pure host).
+ */
+int pa_workspace_size(const pa_problem* problem, size_t* bytes);
+int pa_workspace_size_ex(const pa_problem* problem, int32_t num_cus, size_t* bytes);
+
+/*
+ * One decode-attention step (page: vector(), which issues pass 1 and, when
+ * partitioned, the merge). Enqueues pass 1 on `stream` and, when the plan has
+ * more than one partition, paged_attn_combine's kernel after it. Asynchronous:
+ * returns once the work is enqueued. `scale` multiplies q.k (binary32, as the
+ * page passes the scale's fp32 bits). `workspace` may be NULL when
+ * pa_workspace_size reports 0. q/new_k/new_v/pools/tables are only read; `out`
+ * and the workspace are written. Buffers must not overlap `out`.
+ */
+int paged_attn_decode(const pa_problem* problem, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_table,
+                      const int32_t* context_lens, const void* new_k, const void* new_v,
+                      float scale, void* out, void* workspace, size_t workspace_bytes,
+                      pa_stream_t stream);
+
+/*
+ * Merge step alone (page: PARTIALS_REDUCE). Reads the partial states a
+ * partitioned paged_attn_decode left in `workspace` for the same problem and
+ * context_lens, and writes out = (sum_p 2^(m_p - M) o_p) / (sum_p 2^(m_p - M) l_p)
+ * with M = max_p m_p over each row's partitions (0 when that sum is 0), rounded
+ * to nearest-even in the I/O dtype. Rows of sequences that fit in one partition
+ * were already written by pass 1 and are left untouched. For a single-pass plan
+ * it does nothing and returns PA_OK.
+ */
+int paged_attn_combine(const pa_problem* problem, const int32_t* context_lens,
+                       const void* workspace, size_t workspace_bytes, void* out,
+                       pa_stream_t stream);
+
+/* Message of the last failing call on this thread ("" if none). Valid until the
+ * next call on this thread. */
+const char* paged_attn_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int paged_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGED_ATTN_H */

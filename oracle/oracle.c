@@ -1,0 +1,277 @@
+/*
+ * Reference oracle for paged-KV grouped-query decode attention (plain C, double).
+ *
+ * TEST INFRASTRUCTURE ONLY: used by the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark; never by the product path. It shares no
+ * code with the HIP library.
+ *
+ * Source of the definition: docs.rs source page "onnxruntime-ep-mlx 0.31.1:
+ * src/ops/paged_attention.rs".
+ *   - GQA head mapping, visible-key window, block-table address and the
+ *     widening of stored elements to fp32: VECTOR_BODY.
+ *   - Empty rows produce zeros (division skipped when the sum is zero):
+ *     VECTOR_REDUCE and PARTIALS_REDUCE.
+ *   - Chunk merge with weights exp(m_c - M): VECTOR_PARTIALS + PARTIALS_REDUCE.
+ * The same head grouping (query head h = kh*G + g) appears on the docs.rs page
+ * "onnxruntime-ep-mlx 0.31.1: src/ops/attention_vjp/dense.rs", execute().
+ *
+ * Readings taken where the page is silent:
+ *   - context_lens[b] is the cached length only; row r additionally sees new
+ *     rows 0..r when causal, all NQ new rows otherwise (VECTOR_BODY's `total`).
+ *   - The softmax scale is the binary32 value passed in, widened to double
+ *     (the page passes the fp32 bit pattern of the scale to the kernel).
+ *   - The page's slot-patching of cached positions is not part of this
+ *     operation: the pool is read-only and new rows never alias pool slots.
+ * No blocking, fusion or reordering beyond gathering one (sequence, KV head)
+ * once and reusing it for the G*NQ query rows that read it.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* IEEE binary16 -> double, exact (sign, 5-bit exponent, 10-bit fraction). */
+static double half_bits_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int exponent = (h >> 10) & 0x1f;
+    int fraction = h & 0x3ff;
+    double value;
+    if (exponent == 0)
+        value = ldexp((double)fraction, -24); /* subnormal: fraction * 2^-24 */
+    else if (exponent == 31)
+        value = fraction ? NAN : INFINITY;
+    else
+        value = ldexp((double)(fraction + 1024), exponent - 25);
+    return sign ? -value : value;
+}
+
+/* bfloat16 -> double, exact: the 16 bits are the top half of a binary32. */
+static double bf16_bits_to_double(uint16_t b)
+{
+    uint32_t bits = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+double oracle_widen(const void* base, int64_t index, int dtype)
+{
+    const unsigned char* p = (const unsigned char*)base;
+    if (dtype == 0) {
+        float f;
+        memcpy(&f, p + index * 4, 4);
+        return (double)f;
+    }
+    uint16_t bits;
+    memcpy(&bits, p + index * 2, 2);
+    return dtype == 1 ? half_bits_to_double(bits) : bf16_bits_to_double(bits);
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static int check_args(int B, int H, int KV, int D, int BS, int max_blocks, int NQ,
+                      int dtype, const int32_t* context_lens)
+{
+    if (B < 0 || H <= 0 || KV <= 0 || D <= 0 || BS <= 0 || max_blocks < 0 || NQ < 0)
+        return -1;
+    if (H % KV != 0)
+        return -2;
+    if (dtype < 0 || dtype > 2)
+        return -3;
+    for (int b = 0; b < B; ++b)
+        if (context_lens[b] < 0 || context_lens[b] > (int64_t)max_blocks * BS)
+            return -4;
+    return 0;
+}
+
+/*
+ * Gather the logical key/value sequence of (b, kh): cached positions i < L in
+ * order through the block table, then the NQ new rows. Rows are D doubles.
+ */
+static void gather(int b, int kh, int KV, int D, int BS, int max_blocks, int NQ, int dtype,
+                   const void* k_pool, const void* v_pool, const int32_t* block_table,
+                   int L, const void* new_k, const void* new_v, double* K, double* V)
+{
+    for (int i = 0; i < L; ++i) {
+        int64_t physical = block_table[(int64_t)b * max_blocks + i / BS];
+        int64_t row = ((physical * BS + i % BS) * KV + kh) * (int64_t)D;
+        for (int d = 0; d < D; ++d) {
+            K[(int64_t)i * D + d] = oracle_widen(k_pool, row + d, dtype);
+            V[(int64_t)i * D + d] = oracle_widen(v_pool, row + d, dtype);
+        }
+    }
+    for (int j = 0; j < NQ; ++j) {
+        int64_t row = (((int64_t)b * KV + kh) * NQ + j) * D;
+        for (int d = 0; d < D; ++d) {
+            K[(int64_t)(L + j) * D + d] = oracle_widen(new_k, row + d, dtype);
+            V[(int64_t)(L + j) * D + d] = oracle_widen(new_v, row + d, dtype);
+        }
+    }
+}
+
+/* s_i = scale * <q, K_i> for the first n keys. */
+static void scores(const double* qrow, const double* K, int n, int D, double scale, double* s)
+{
+    for (int i = 0; i < n; ++i) {
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d)
+            dot += qrow[d] * K[(int64_t)i * D + d];
+        s[i] = scale * dot;
+    }
+}
+
+static int decode_impl(int B, int H, int KV, int D, int BS, int max_blocks, int NQ, int causal,
+                       int dtype, const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_table, const int32_t* context_lens,
+                       const void* new_k, const void* new_v, float scale, int chunk,
+                       int max_chunks, double* part_m, double* part_z, double* part_o,
+                       double* out)
+{
+    int rc = check_args(B, H, KV, D, BS, max_blocks, NQ, dtype, context_lens);
+    if (rc)
+        return rc;
+    if (chunk < 0 || (chunk > 0 && max_chunks <= 0))
+        return -5;
+    const int G = H / KV;
+    const double sc = (double)scale;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t unit = 0; unit < (int64_t)B * KV; ++unit) {
+        const int b = (int)(unit / KV), kh = (int)(unit % KV);
+        const int L = context_lens[b];
+        const int64_t n_all = (int64_t)L + NQ;
+        double* K = (double*)malloc(sizeof(double) * (size_t)(n_all > 0 ? n_all : 1) * D);
+        double* V = (double*)malloc(sizeof(double) * (size_t)(n_all > 0 ? n_all : 1) * D);
+        double* s = (double*)malloc(sizeof(double) * (size_t)(n_all > 0 ? n_all : 1));
+        double* qrow = (double*)malloc(sizeof(double) * (size_t)D);
+        double* acc = (double*)malloc(sizeof(double) * (size_t)D);
+        if (!K || !V || !s || !qrow || !acc) {
+#pragma omp atomic write
+            failed = 1;
+            free(K); free(V); free(s); free(qrow); free(acc);
+            continue;
+        }
+        gather(b, kh, KV, D, BS, max_blocks, NQ, dtype, k_pool, v_pool, block_table, L, new_k,
+               new_v, K, V);
+        for (int g = 0; g < G; ++g) {
+            const int h = kh * G + g; /* query head h reads KV head h / G */
+            for (int r = 0; r < NQ; ++r) {
+                const int64_t orow = ((int64_t)b * H + h) * NQ + r;
+                const int n = L + (causal ? r + 1 : NQ);
+                for (int d = 0; d < D; ++d)
+                    qrow[d] = oracle_widen(q, orow * D + d, dtype);
+                scores(qrow, K, n, D, sc, s);
+                double* o = out + orow * D;
+                if (chunk == 0) {
+                    /* textbook softmax: m = max s, w = exp(s - m), out = sum w V / sum w */
+                    double m = -INFINITY, Z = 0.0;
+                    for (int i = 0; i < n; ++i)
+                        if (s[i] > m)
+                            m = s[i];
+                    for (int d = 0; d < D; ++d)
+                        acc[d] = 0.0;
+                    for (int i = 0; i < n; ++i) {
+                        double w = exp(s[i] - m);
+                        Z += w;
+                        for (int d = 0; d < D; ++d)
+                            acc[d] += w * V[(int64_t)i * D + d];
+                    }
+                    for (int d = 0; d < D; ++d)
+                        o[d] = Z != 0.0 ? acc[d] / Z : 0.0;
+                } else {
+                    /* per-chunk states, then the merge */
+                    const int n_chunks = (n + chunk - 1) / chunk;
+                    double M = -INFINITY, Z = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        acc[d] = 0.0;
+                    for (int c = 0; c < max_chunks; ++c) {
+                        double* po = part_o ? part_o + (orow * max_chunks + c) * D : NULL;
+                        if (part_m) part_m[orow * max_chunks + c] = -INFINITY;
+                        if (part_z) part_z[orow * max_chunks + c] = 0.0;
+                        if (po)
+                            for (int d = 0; d < D; ++d) po[d] = 0.0;
+                    }
+                    for (int c = 0; c < n_chunks; ++c) {
+                        const int lo = c * chunk, hi = lo + chunk < n ? lo + chunk : n;
+                        double mc = -INFINITY;
+                        for (int i = lo; i < hi; ++i)
+                            if (s[i] > mc)
+                                mc = s[i];
+                        if (mc > M)
+                            M = mc;
+                    }
+                    for (int c = 0; c < n_chunks; ++c) {
+                        const int lo = c * chunk, hi = lo + chunk < n ? lo + chunk : n;
+                        double mc = -INFINITY, zc = 0.0;
+                        for (int i = lo; i < hi; ++i)
+                            if (s[i] > mc)
+                                mc = s[i];
+                        const double weight = exp(mc - M);
+                        double* po = (part_o && c < max_chunks)
+                                         ? part_o + (orow * max_chunks + c) * D
+                                         : NULL;
+                        for (int i = lo; i < hi; ++i) {
+                            const double w = exp(s[i] - mc);
+                            zc += w;
+                            for (int d = 0; d < D; ++d) {
+                                const double contribution = w * V[(int64_t)i * D + d];
+                                acc[d] += weight * contribution;
+                                if (po)
+                                    po[d] += contribution;
+                            }
+                        }
+                        Z += weight * zc;
+                        if (c < max_chunks) {
+                            if (part_m) part_m[orow * max_chunks + c] = mc;
+                            if (part_z) part_z[orow * max_chunks + c] = zc;
+                        }
+                    }
+                    for (int d = 0; d < D; ++d)
+                        o[d] = Z != 0.0 ? acc[d] / Z : 0.0;
+                }
+            }
+        }
+        free(K); free(V); free(s); free(qrow); free(acc);
+    }
+    return failed ? -6 : 0;
+}
+
+int oracle_paged_decode(int B, int H, int KV, int D, int BS, int max_blocks, int NQ,
+                        int causal, int dtype, const void* q, const void* k_pool,
+                        const void* v_pool, const int32_t* block_table,
+                        const int32_t* context_lens, const void* new_k,
+                        const void* new_v, float scale, double* out)
+{
+    return decode_impl(B, H, KV, D, BS, max_blocks, NQ, causal, dtype, q, k_pool, v_pool,
+                       block_table, context_lens, new_k, new_v, scale, 0, 0, NULL, NULL,
+                       NULL, out);
+}
+
+int oracle_paged_decode_partitioned(int B, int H, int KV, int D, int BS, int max_blocks,
+                                    int NQ, int causal, int dtype, const void* q,
+                                    const void* k_pool, const void* v_pool,
+                                    const int32_t* block_table,
+                                    const int32_t* context_lens, const void* new_k,
+                                    const void* new_v, float scale, int chunk,
+                                    int max_chunks, double* part_m, double* part_z,
+                                    double* part_o, double* out)
+{
+    if (chunk <= 0)
+        return -5;
+    return decode_impl(B, H, KV, D, BS, max_blocks, NQ, causal, dtype, q, k_pool, v_pool,
+                       block_table, context_lens, new_k, new_v, scale, chunk, max_chunks,
+                       part_m, part_z, part_o, out);
+}

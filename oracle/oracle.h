@@ -1,0 +1,70 @@
+/*
+ * Reference oracle for paged-KV grouped-query decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path links, loads or calls
+ * this library: only the test suite, the smoke check and the CPU-baseline leg of
+ * the benchmark do. It shares no code, header or constant with the HIP library.
+ *
+ * What it computes is the plain definition of the operation described on the
+ * docs.rs source page "onnxruntime-ep-mlx 0.31.1: src/ops/paged_attention.rs"
+ * (the VECTOR_BODY kernel text and the vector() launcher): for every sequence b,
+ * query head h and new row r, gather the visible keys and values in logical
+ * order (cached positions through the block table, then the step's new rows),
+ * then apply a textbook max-subtracted softmax, all in double precision.
+ *
+ * Element types are given by a code: 0 = IEEE binary32, 1 = IEEE binary16,
+ * 2 = bfloat16. Every stored element is widened exactly to double.
+ *
+ * Layouts (all row-major, contiguous):
+ *   q, out       [B, H, NQ, D]
+ *   k/v pool     [num_blocks, BS, KV, D]
+ *   block_table  int32 [B, max_blocks]
+ *   context_lens int32 [B]   cached (past) length, new rows excluded
+ *   new_k/new_v  [B, KV, NQ, D]
+ * Return value: 0 on success, a negative number on a malformed argument (no
+ * partial output is guaranteed in that case).
+ */
+#ifndef PAGED_DECODE_ORACLE_H
+#define PAGED_DECODE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Single-pass definition: gather, then softmax in double. out is double [B,H,NQ,D]. */
+int oracle_paged_decode(int B, int H, int KV, int D, int BS, int max_blocks, int NQ,
+                        int causal, int dtype, const void* q, const void* k_pool,
+                        const void* v_pool, const int32_t* block_table,
+                        const int32_t* context_lens, const void* new_k,
+                        const void* new_v, float scale, double* out);
+
+/*
+ * Partitioned form: the visible keys of each row are cut into consecutive
+ * chunks of `chunk` keys; each chunk yields (max m_c, sum Z_c, unnormalised
+ * o_c); the chunks are merged with weights exp(m_c - M). Same output layout.
+ * If part_m/part_z/part_o are non-NULL they receive each chunk's state, for
+ * row index ((b*H + h)*NQ + r) and chunk c at [row*max_chunks + c] (part_o
+ * additionally times D); chunks that do not exist are written as m = -inf,
+ * Z = 0, o = 0.
+ */
+int oracle_paged_decode_partitioned(int B, int H, int KV, int D, int BS, int max_blocks,
+                                    int NQ, int causal, int dtype, const void* q,
+                                    const void* k_pool, const void* v_pool,
+                                    const int32_t* block_table,
+                                    const int32_t* context_lens, const void* new_k,
+                                    const void* new_v, float scale, int chunk,
+                                    int max_chunks, double* part_m, double* part_z,
+                                    double* part_o, double* out);
+
+/* Exact widening of one stored element (exported so tests can pin it). */
+double oracle_widen(const void* base, int64_t index, int dtype);
+
+/* Number of OpenMP threads the oracle uses (1 when built without OpenMP). */
+int oracle_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

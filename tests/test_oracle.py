@@ -1,0 +1,286 @@
+"""Pins of the CPU oracle to things other than itself (no GPU).
+
+The oracle follows the definition on the docs.rs source page "onnxruntime-ep-mlx
+0.31.1: src/ops/paged_attention.rs" (VECTOR_BODY: head mapping h / (H/KV),
+visible window past + (causal ? r + 1 : NQ), block-table address; VECTOR_REDUCE
+and PARTIALS_REDUCE: merge of partial states). The pins are:
+  * brute force: a dense float64 formulation and torch's SDPA on tiny inputs,
+  * closed forms: one key returns v exactly; equal scores return the mean of the
+    visible values; two keys give the logistic mix,
+  * invariants: physical block order, block size, partitioning and causality
+    do not change the result,
+  * exact widening of stored binary16 / bfloat16 bit patterns,
+  * mutation check: plausible mistakes planted in a copy of the oracle's C
+    source each make at least one of these pins fail.
+"""
+import math
+import os
+import shutil
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import problems as P
+
+ORACLE_DIR = os.path.dirname(os.path.abspath(oracle.__file__))
+
+
+def _ora(w, lib=None, **kw):
+    return oracle.paged_decode(*P.args(w), causal=w.spec.causal, lib=lib, **kw)
+
+
+SWEEP = [
+    # (B, H, KV, D, BS, NQ, causal, dtype, lens)
+    (1, 4, 2, 64, 16, 1, True, "f32", (100,)),
+    (2, 4, 4, 64, 16, 1, True, "f32", (0, 1)),          # MHA, empty and one-token past
+    (3, 8, 1, 64, 16, 3, True, "f32", (15, 16, 17)),     # MQA, page boundaries
+    (2, 8, 2, 128, 32, 3, False, "f16", (31, 64)),       # non-causal multi-row
+    (2, 16, 2, 128, 16, 8, True, "bf16", (0, 33)),       # G = 8, NQ = 8
+    (1, 2, 1, 64, 32, 2, True, "bf16", (100,)),
+    (2, 4, 2, 128, 16, 1, True, "f16", (1, 48)),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: "-".join(map(str, c[:8])))
+def test_oracle_matches_dense_and_sdpa(case):
+    B, H, KV, D, BS, NQ, causal, dtype, lens = case
+    w = P.small(B=B, H=H, KV=KV, D=D, BS=BS, NQ=NQ, causal=causal, dtype=dtype, lens=lens,
+                seed=11 + B + NQ)
+    ref = _ora(w)
+    dense = oracle.dense_reference(*P.args(w), causal=causal)
+    sdpa = oracle.sdpa_reference(*P.args(w), causal=causal)
+    assert np.abs(ref - dense).max() < 1e-12
+    assert np.abs(ref - sdpa).max() < 1e-12
+
+
+def test_single_key_returns_new_v_exactly():
+    # No past and one new row: the only visible key has weight exactly 1.
+    w = P.small(B=2, H=8, KV=2, D=64, NQ=1, lens=(0, 0), dtype="bf16")
+    out = _ora(w)
+    G = w.spec.H // w.spec.KV
+    nv = w.new_v.double().numpy()
+    for b in range(2):
+        for h in range(w.spec.H):
+            assert np.array_equal(out[b, h, 0], nv[b, h // G, 0])
+
+
+def test_causal_row0_without_past_is_new_v0():
+    w = P.small(B=1, H=4, KV=2, D=64, NQ=4, causal=True, lens=(0,), dtype="f16")
+    out = _ora(w)
+    nv = w.new_v.double().numpy()
+    for h in range(4):
+        assert np.array_equal(out[0, h, 0], nv[0, h // 2, 0])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_equal_scores_give_mean_of_visible_values(causal):
+    w = P.small(B=2, H=4, KV=2, D=64, NQ=3, causal=causal, lens=(21, 7), dtype="f32")
+    w.q.zero_()
+    out = _ora(w)
+    for b in range(2):
+        for h in range(4):
+            for r in range(3):
+                _, vs = P.logical_rows(w, b, h // 2, r)
+                mean = [sum(col) / len(vs) for col in zip(*vs)]
+                assert np.allclose(out[b, h, r], mean, rtol=0, atol=1e-14)
+
+
+def test_zero_scale_gives_mean():
+    w = P.small(B=1, H=2, KV=1, D=64, NQ=2, causal=True, lens=(9,), dtype="f32")
+    w.scale = 0.0
+    out = _ora(w)
+    for r in range(2):
+        _, vs = P.logical_rows(w, 0, 0, r)
+        mean = [sum(col) / len(vs) for col in zip(*vs)]
+        assert np.allclose(out[0, 0, r], mean, rtol=0, atol=1e-14)
+
+
+def test_two_keys_logistic_mix():
+    # One cached key (through the table) and one new key.
+    w = P.small(B=1, H=2, KV=1, D=64, NQ=1, lens=(1,), dtype="f32", pool_extra=5)
+    out = _ora(w)
+    (k0, k1), (v0, v1) = P.logical_rows(w, 0, 0, 0)
+    for h in range(2):
+        qv = [float(x) for x in w.q[0, h, 0].double()]
+        s0 = w.scale * sum(a * b for a, b in zip(qv, k0))
+        s1 = w.scale * sum(a * b for a, b in zip(qv, k1))
+        a0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        a1 = 1.0 / (1.0 + math.exp(s0 - s1))
+        expect = [a0 * x + a1 * y for x, y in zip(v0, v1)]
+        assert np.allclose(out[0, h, 0], expect, rtol=0, atol=1e-13)
+
+
+def test_argmax_probe_selects_each_logical_position():
+    # Make logical key t dominate: out must equal v_t.
+    w = P.small(B=1, H=2, KV=1, D=64, NQ=1, lens=(40,), dtype="f32", pool_extra=4)
+    for t in (0, 15, 16, 39):
+        w2 = P.relayout(w, shuffle_seed=3 + t)
+        phys = int(w2.block_table[0, t // 16])
+        q = w2.q[0, 0, 0].clone()
+        w2.k_pool[phys, t % 16, 0] = q * 40.0
+        out = _ora(w2)
+        expect = w2.v_pool[phys, t % 16, 0].double().numpy()
+        assert np.allclose(out[0, 0, 0], expect, atol=1e-9)
+
+
+def test_block_order_and_block_size_do_not_change_the_result():
+    w = P.small(B=3, H=8, KV=2, D=64, BS=16, NQ=2, causal=True, lens=(70, 16, 33), dtype="f16")
+    base = _ora(w)
+    for kw in (dict(shuffle_seed=1), dict(shuffle_seed=2, extra_blocks=5),
+               dict(new_bs=32, shuffle_seed=4)):
+        w2 = P.relayout(w, **kw)
+        assert np.array_equal(_ora(w2), base), kw
+
+
+def test_unused_pool_space_is_never_read():
+    w = P.small(B=2, H=4, KV=2, D=64, BS=16, NQ=1, lens=(45, 3), dtype="bf16")
+    w2 = P.relayout(w, shuffle_seed=9, extra_blocks=4, fill=float("nan"))
+    out = _ora(w2)
+    assert np.isfinite(out).all()
+    assert np.array_equal(out, _ora(w))
+
+
+@pytest.mark.parametrize("chunk", [1, 5, 16, 64, 1000])
+def test_partitioned_equals_single_pass(chunk):
+    w = P.small(B=2, H=8, KV=2, D=128, BS=16, NQ=3, causal=True, lens=(130, 17), dtype="bf16")
+    single = _ora(w)
+    part, m, z, o = oracle.paged_decode_partitioned(*P.args(w), chunk=chunk, causal=True,
+                                                    want_parts=True)
+    assert np.abs(part - single).max() < 1e-12
+    # chunk states, merged by hand with weights exp(m_c - M), give the same rows
+    for b, h, r in ((0, 0, 0), (1, 7, 2)):
+        ok = np.isfinite(m[b, h, r])
+        M = m[b, h, r][ok].max()
+        wts = np.exp(m[b, h, r][ok] - M)
+        merged = (wts[:, None] * o[b, h, r][ok]).sum(0) / (wts * z[b, h, r][ok]).sum()
+        assert np.abs(merged - single[b, h, r]).max() < 1e-12
+
+
+def test_causality_new_rows_after_r_do_not_matter():
+    w = P.small(B=1, H=4, KV=2, D=64, NQ=4, causal=True, lens=(10,), dtype="f32")
+    base = _ora(w)
+    for j in range(1, 4):
+        w2 = P.small(B=1, H=4, KV=2, D=64, NQ=4, causal=True, lens=(10,), dtype="f32")
+        w2.new_k[0, :, j] += 3.0
+        w2.new_v[0, :, j] -= 2.0
+        out = _ora(w2)
+        assert np.array_equal(out[:, :, :j], base[:, :, :j])
+        assert not np.allclose(out[:, :, j:], base[:, :, j:])
+
+
+def test_non_causal_rows_all_see_every_new_row():
+    w = P.small(B=1, H=2, KV=1, D=64, NQ=3, causal=False, lens=(4,), dtype="f32")
+    base = _ora(w)
+    w.new_v[0, 0, 2] += 1.0
+    out = _ora(w)
+    assert (np.abs(out - base).reshape(2, 3, -1).max(-1) > 0).all()
+
+
+def test_widen_is_exact():
+    f16 = torch.from_numpy(np.array([0x3C00, 0x0001, 0x7BFF, 0x8400, 0x7C00, 0x3555],
+                                    dtype=np.uint16).view(np.int16).copy())
+    expect = [1.0, 2.0 ** -24, 65504.0, -(2.0 ** -14), math.inf, 0.333251953125]
+    for i, e in enumerate(expect):
+        assert oracle.widen(f16.view(torch.float16), i) == e
+    u = np.array([0x3F80, 0x0001, 0xC2F7, 0x7F80], dtype=np.uint16).view(np.int16)
+    bf = torch.from_numpy(u.copy()).view(torch.bfloat16)
+    expect = [1.0, 2.0 ** -133, -123.5, math.inf]
+    for i, e in enumerate(expect):
+        assert oracle.widen(bf, i) == e
+    f32 = torch.tensor([1.5, -2.0 ** -149], dtype=torch.float32)
+    assert oracle.widen(f32, 0) == 1.5 and oracle.widen(f32, 1) == -(2.0 ** -149)
+
+
+def test_rejects_malformed_arguments():
+    w = P.small(B=1, H=4, KV=2, D=64, lens=(20,))
+    bad = w.context_lens.copy()
+    bad[0] = 10 ** 6  # beyond max_blocks * BS
+    with pytest.raises(ValueError):
+        oracle.paged_decode(w.q, w.k_pool, w.v_pool, w.block_table, bad, w.new_k, w.new_v,
+                            w.scale)
+
+
+# --------------------------------------------------------------------------
+# Mutation check: each planted mistake must trip at least one pin.
+# --------------------------------------------------------------------------
+def _pins(lib):
+    """Compact pin suite; returns the names of the pins that fail with `lib`."""
+    failed = []
+    try:
+        for case in (SWEEP[2], SWEEP[4], SWEEP[3]):
+            B, H, KV, D, BS, NQ, causal, dtype, lens = case
+            w = P.small(B=B, H=H, KV=KV, D=D, BS=BS, NQ=NQ, causal=causal, dtype=dtype,
+                        lens=lens, seed=5)
+            if np.abs(_ora(w, lib) - oracle.sdpa_reference(*P.args(w), causal=causal)).max() > 1e-12:
+                failed.append("sdpa")
+                break
+        w = P.small(B=2, H=4, KV=2, D=64, NQ=3, causal=True, lens=(21, 7), dtype="f32")
+        w.q.zero_()
+        out = _ora(w, lib)
+        _, vs = P.logical_rows(w, 1, 1, 2)
+        mean = np.array([sum(c) / len(vs) for c in zip(*vs)])
+        if np.abs(out[1, 3, 2] - mean).max() > 1e-13:
+            failed.append("mean")
+        w = P.small(B=2, H=8, KV=2, D=128, BS=16, NQ=3, causal=True, lens=(130, 17), dtype="bf16")
+        single = _ora(w, lib)
+        part = oracle.paged_decode_partitioned(*P.args(w), chunk=7, causal=True, lib=lib)
+        if np.abs(part - single).max() > 1e-12:
+            failed.append("partition")
+        bf = torch.from_numpy(np.array([0x3F80, 0xC2F7], dtype=np.uint16).view(np.int16).copy())
+        h16 = torch.tensor([0x3C00, 0x0001], dtype=torch.int16)
+        if (oracle.widen(bf.view(torch.bfloat16), 1, lib) != -123.5
+                or oracle.widen(h16.view(torch.float16), 1, lib) != 2.0 ** -24
+                or oracle.widen(h16.view(torch.float16), 0, lib) != 1.0):
+            failed.append("widen")
+    except ValueError:
+        failed.append("rejected")
+    return failed
+
+
+MUTATIONS = {
+    "gqa_head_mapping": ("const int h = kh * G + g;", "const int h = g * KV + kh;"),
+    "drop_causal_window": ("(causal ? r + 1 : NQ)", "(causal ? NQ : NQ)"),
+    "table_index_uses_slot": ("block_table[(int64_t)b * max_blocks + i / BS]",
+                              "block_table[(int64_t)b * max_blocks + i % BS]"),
+    "slot_off_by_one": ("((physical * BS + i % BS) * KV + kh)", "((physical * BS + (i + 1) % BS) * KV + kh)"),
+    "drop_kv_head_offset": ("((physical * BS + i % BS) * KV + kh)", "((physical * BS + i % BS) * KV)"),
+    "drop_scale": ("s[i] = scale * dot;", "s[i] = dot;"),
+    "flip_exponent_sign": ("double w = exp(s[i] - m);", "double w = exp(m - s[i]);"),
+    "drop_normalisation": ("o[d] = Z != 0.0 ? acc[d] / Z : 0.0;\n                } else {",
+                           "o[d] = acc[d];\n                } else {"),
+    "values_from_keys": ("acc[d] += w * V[(int64_t)i * D + d];", "acc[d] += w * K[(int64_t)i * D + d];"),
+    "merge_weight_sign": ("const double weight = exp(mc - M);", "const double weight = exp(M - mc);"),
+    "bf16_shift": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
+    "half_exponent_bias": ("exponent - 25", "exponent - 24"),
+    "new_rows_from_wrong_head": ("(((int64_t)b * KV + kh) * NQ + j) * D", "(((int64_t)b * KV) * NQ + j) * D"),
+}
+
+
+def test_pins_pass_on_the_oracle():
+    assert _pins(None) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = open(os.path.join(ORACLE_DIR, "oracle.c")).read()
+    old, new = MUTATIONS[name]
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    (tmp_path / "oracle.c").write_text(src.replace(old, new))
+    shutil.copy(os.path.join(ORACLE_DIR, "oracle.h"), tmp_path / "oracle.h")
+    so = tmp_path / f"liboracle_{name}.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", str(tmp_path / "oracle.c"),
+                    "-o", str(so), "-lm"], check=True)
+    # The mutant may read out of bounds, so its pins run in a child process; a
+    # crash of that process also counts as caught.
+    root = os.path.dirname(ORACLE_DIR)
+    code = ("import sys, oracle; from tests.test_oracle import _pins; "
+            f"sys.exit(3 if _pins(oracle.load_library({str(so)!r})) else 0)")
+    res = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                         timeout=300)
+    assert res.returncode != 0, f"no pin caught the planted mistake {name}: {res.stderr[-500:]}"
