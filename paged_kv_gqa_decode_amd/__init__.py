@@ -1,0 +1,217 @@
+"""MI355X-native paged-KV grouped-query decode attention.
+
+Thin ctypes binding of libpaged_attn.so (built from csrc/ with hipcc for
+gfx950). Every step of the computation runs in the library's HIP kernels; this
+module only marshals arguments: torch tensors -> device pointers, the current
+HIP stream, and the pa_problem struct. The entry points keep the C names
+declared in include/paged_attn.h.
+
+There is no fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpaged_attn.so")
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_DEVICE, PA_ERR_LAUNCH = range(6)
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
+
+EXPORTED = ("pa_plan_ex", "pa_plan", "pa_workspace_size", "pa_workspace_size_ex",
+            "paged_attn_decode", "paged_attn_combine", "paged_attn_last_error",
+            "paged_attn_version")
+
+
+class PaProblem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "num_heads", "num_kv_heads", "head_dim", "block_size", "num_blocks",
+        "max_blocks_per_seq", "nq", "causal", "dtype", "max_context_len", "num_partitions",
+        "kernel")]
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[pa_status {code}] {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def library(path: Optional[str] = None):
+    """Load libpaged_attn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built: run `python -m paged_kv_gqa_decode_amd.build` "
+                           "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(p)
+    P, vp, i32p = ctypes.POINTER(PaProblem), ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+    szp = ctypes.POINTER(ctypes.c_size_t)
+    lib.pa_plan_ex.argtypes = [P, ctypes.c_int32, i32p, i32p, i32p]
+    lib.pa_plan.argtypes = [P, i32p, i32p, i32p]
+    lib.pa_workspace_size.argtypes = [P, szp]
+    lib.pa_workspace_size_ex.argtypes = [P, ctypes.c_int32, szp]
+    lib.paged_attn_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
+                                      ctypes.c_size_t, vp]
+    lib.paged_attn_combine.argtypes = [P, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.paged_attn_last_error.argtypes = []
+    lib.paged_attn_last_error.restype = ctypes.c_char_p
+    lib.paged_attn_version.argtypes = []
+    for name in ("pa_plan_ex", "pa_plan", "pa_workspace_size", "pa_workspace_size_ex",
+                 "paged_attn_decode", "paged_attn_combine", "paged_attn_version"):
+        getattr(lib, name).restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def paged_attn_last_error() -> str:
+    return library().paged_attn_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != PA_OK:
+        raise PagedAttnError(rc, paged_attn_last_error())
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(stream) -> Optional[int]:
+    """None -> the null stream; a torch stream -> its HIP handle; an int -> itself."""
+    if stream is None:
+        return None
+    return getattr(stream, "cuda_stream", stream)
+
+
+# ---------------------------------------------------------------------------
+# C entry points, same names (return the pa_status; raise=True turns errors
+# into PagedAttnError).
+# ---------------------------------------------------------------------------
+def pa_plan_ex(problem: PaProblem, num_cus: int, raise_on_error: bool = True):
+    parts, chunk, kern = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    rc = library().pa_plan_ex(ctypes.byref(problem), num_cus, ctypes.byref(parts),
+                              ctypes.byref(chunk), ctypes.byref(kern))
+    if raise_on_error:
+        _check(rc)
+    return rc, parts.value, chunk.value, kern.value
+
+
+def pa_plan(problem: PaProblem, raise_on_error: bool = True):
+    parts, chunk, kern = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    rc = library().pa_plan(ctypes.byref(problem), ctypes.byref(parts), ctypes.byref(chunk),
+                           ctypes.byref(kern))
+    if raise_on_error:
+        _check(rc)
+    return rc, parts.value, chunk.value, kern.value
+
+
+def pa_workspace_size(problem: PaProblem, raise_on_error: bool = True):
+    n = ctypes.c_size_t()
+    rc = library().pa_workspace_size(ctypes.byref(problem), ctypes.byref(n))
+    if raise_on_error:
+        _check(rc)
+    return rc, n.value
+
+
+def pa_workspace_size_ex(problem: PaProblem, num_cus: int, raise_on_error: bool = True):
+    n = ctypes.c_size_t()
+    rc = library().pa_workspace_size_ex(ctypes.byref(problem), num_cus, ctypes.byref(n))
+    if raise_on_error:
+        _check(rc)
+    return rc, n.value
+
+
+def paged_attn_decode(problem: PaProblem, q, k_pool, v_pool, block_table, context_lens, new_k,
+                      new_v, scale: float, out, workspace=None, workspace_bytes: int = 0,
+                      stream=None, raise_on_error: bool = True) -> int:
+    rc = library().paged_attn_decode(
+        ctypes.byref(problem), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+        _ptr(context_lens), _ptr(new_k), _ptr(new_v), ctypes.c_float(scale), _ptr(out),
+        _ptr(workspace), ctypes.c_size_t(workspace_bytes), _stream(stream))
+    if raise_on_error:
+        _check(rc)
+    return rc
+
+
+def paged_attn_combine(problem: PaProblem, context_lens, workspace, workspace_bytes: int, out,
+                       stream=None, raise_on_error: bool = True) -> int:
+    rc = library().paged_attn_combine(ctypes.byref(problem), _ptr(context_lens), _ptr(workspace),
+                                      ctypes.c_size_t(workspace_bytes), _ptr(out),
+                                      _stream(stream))
+    if raise_on_error:
+        _check(rc)
+    return rc
+
+
+def paged_attn_version() -> int:
+    return library().paged_attn_version()
+
+
+# ---------------------------------------------------------------------------
+# Torch convenience layer: builds the problem from tensor shapes, allocates
+# out/workspace with torch, launches on the current stream.
+# ---------------------------------------------------------------------------
+def _dtype_code(t) -> int:
+    import torch
+    return {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}[t.dtype]
+
+
+def make_problem(q, k_pool, block_table, *, max_context_len: int, causal: bool = True,
+                 num_partitions: int = 0, kernel: int = PA_KERNEL_AUTO) -> PaProblem:
+    B, H, NQ, D = q.shape
+    NB, BS, KV, D2 = k_pool.shape
+    assert D == D2, "head_dim of q and the pools differ"
+    return PaProblem(batch=B, num_heads=H, num_kv_heads=KV, head_dim=D, block_size=BS,
+                     num_blocks=NB, max_blocks_per_seq=block_table.shape[1] if block_table.dim() == 2 else 0,
+                     nq=NQ, causal=int(causal), dtype=_dtype_code(q),
+                     max_context_len=int(max_context_len), num_partitions=int(num_partitions),
+                     kernel=int(kernel))
+
+
+class Decoder:
+    """Holds the problem, workspace and output of one decode shape for repeated calls."""
+
+    def __init__(self, q, k_pool, block_table, *, max_context_len: int, causal: bool = True,
+                 num_partitions: int = 0, kernel: int = PA_KERNEL_AUTO):
+        import torch
+        self.problem = make_problem(q, k_pool, block_table, max_context_len=max_context_len,
+                                    causal=causal, num_partitions=num_partitions, kernel=kernel)
+        _, self.partitions, self.chunk_tokens, self.kernel = pa_plan(self.problem)
+        _, self.workspace_bytes = pa_workspace_size(self.problem)
+        dev = q.device
+        self.workspace = (torch.empty(self.workspace_bytes, dtype=torch.uint8, device=dev)
+                          if self.workspace_bytes else None)
+        self.out = torch.empty_like(q)
+
+    def __call__(self, q, k_pool, v_pool, block_table, context_lens, new_k, new_v, scale,
+                 out=None, stream=None):
+        import torch
+        out = self.out if out is None else out
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        paged_attn_decode(self.problem, q, k_pool, v_pool, block_table, context_lens, new_k,
+                          new_v, scale, out, self.workspace, self.workspace_bytes, stream)
+        return out
+
+
+def decode(q, k_pool, v_pool, block_table, context_lens, new_k, new_v, scale: float, *,
+           max_context_len: int, causal: bool = True, num_partitions: int = 0,
+           kernel: int = PA_KERNEL_AUTO, out=None, stream=None):
+    """One decode-attention step; returns out [B, H, NQ, D] in q's dtype."""
+    dec = Decoder(q, k_pool, block_table, max_context_len=max_context_len, causal=causal,
+                  num_partitions=num_partitions, kernel=kernel)
+    return dec(q, k_pool, v_pool, block_table, context_lens, new_k, new_v, scale, out=out,
+               stream=stream)

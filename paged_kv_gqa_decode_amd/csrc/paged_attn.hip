@@ -1,0 +1,399 @@
+// Host side of libpaged_attn.so: argument validation, launch plan, kernel
+// selection and the extern "C" entry points declared in paged_attn.h.
+//
+// The plan plays the role of partitions() and the launch shapes of vector() on
+// the docs.rs page "onnxruntime-ep-mlx 0.31.1: src/ops/paged_attention.rs"; its
+// constants are chosen for MI355X (256 compute units in 8 XCDs) rather than for
+// Apple GPUs.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "paged_attn.h"
+#include "combine.hpp"
+#include "decode_valu.hpp"
+
+namespace {
+
+thread_local std::string t_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[640];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    t_error = buf;
+    return code;
+}
+
+int succeed() {
+    t_error.clear();
+    return PA_OK;
+}
+
+constexpr int kMaxRows = 128;         // G * nq
+constexpr int kGroupsPerCu = 8;       // workgroups per CU the heuristic aims to keep busy
+constexpr int kMinChunkTokens = 256;  // below this, partial-state traffic outweighs balance
+constexpr int kMaxChunkTokens = 2048; // above this, ragged batches leave CUs idle
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+int validate_problem(const pa_problem* p) {
+    if (!p) return fail(PA_ERR_INVALID_ARG, "problem is NULL; verify the pa_problem pointer");
+    if (p->batch < 0)
+        return fail(PA_ERR_INVALID_ARG, "batch = %d is negative; verify pa_problem.batch", p->batch);
+    if (p->batch > 65535)
+        return fail(PA_ERR_UNSUPPORTED, "batch = %d exceeds 65535 sequences per call; verify "
+                    "pa_problem.batch or split the batch", p->batch);
+    if (p->num_heads < 1 || p->num_kv_heads < 1)
+        return fail(PA_ERR_INVALID_ARG, "num_heads = %d, num_kv_heads = %d must be >= 1; verify "
+                    "the head counts", p->num_heads, p->num_kv_heads);
+    if (p->num_heads % p->num_kv_heads != 0)
+        return fail(PA_ERR_INVALID_ARG, "num_heads = %d is not a multiple of num_kv_heads = %d; "
+                    "verify the GQA grouping", p->num_heads, p->num_kv_heads);
+    if (p->head_dim != 64 && p->head_dim != 128)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim = %d is not supported (64 or 128); verify "
+                    "pa_problem.head_dim", p->head_dim);
+    if (p->block_size != 16 && p->block_size != 32)
+        return fail(PA_ERR_UNSUPPORTED, "block_size = %d is not supported (16 or 32); verify "
+                    "the page size of the KV pools", p->block_size);
+    if (p->nq < 1)
+        return fail(PA_ERR_INVALID_ARG, "nq = %d must be >= 1; verify the number of new rows",
+                    p->nq);
+    if (p->causal != 0 && p->causal != 1)
+        return fail(PA_ERR_INVALID_ARG, "causal = %d must be 0 or 1", p->causal);
+    if (p->dtype != PA_F32 && p->dtype != PA_F16 && p->dtype != PA_BF16)
+        return fail(PA_ERR_INVALID_ARG, "dtype = %d is not a pa_dtype; verify pa_problem.dtype",
+                    p->dtype);
+    const int64_t rows = (int64_t)(p->num_heads / p->num_kv_heads) * p->nq;
+    if (rows > kMaxRows)
+        return fail(PA_ERR_UNSUPPORTED, "(num_heads/num_kv_heads)*nq = %lld exceeds %d query rows "
+                    "per KV head; verify nq and the GQA group size", (long long)rows, kMaxRows);
+    if (p->num_blocks < 1)
+        return fail(PA_ERR_INVALID_ARG, "num_blocks = %d must be >= 1; verify the pool shape",
+                    p->num_blocks);
+    if (p->max_blocks_per_seq < 0)
+        return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq = %d is negative",
+                    p->max_blocks_per_seq);
+    if (p->max_context_len < 0)
+        return fail(PA_ERR_INVALID_ARG, "max_context_len = %d is negative", p->max_context_len);
+    if ((int64_t)p->max_context_len > (int64_t)p->max_blocks_per_seq * p->block_size)
+        return fail(PA_ERR_INVALID_ARG, "max_context_len = %d exceeds the block-table capacity "
+                    "max_blocks_per_seq*block_size = %lld; verify the table shape",
+                    p->max_context_len, (long long)p->max_blocks_per_seq * p->block_size);
+    if (p->num_partitions < 0)
+        return fail(PA_ERR_INVALID_ARG, "num_partitions = %d is negative", p->num_partitions);
+    if (p->kernel != PA_KERNEL_AUTO && p->kernel != PA_KERNEL_VALU && p->kernel != PA_KERNEL_MFMA)
+        return fail(PA_ERR_INVALID_ARG, "kernel = %d is not a pa_kernel", p->kernel);
+    if (p->kernel == PA_KERNEL_MFMA)
+        return fail(PA_ERR_UNSUPPORTED, "the matrix-core kernel family is not available in this "
+                    "build; verify pa_problem.kernel");
+    return PA_OK;
+}
+
+struct Plan {
+    int parts;    // partitions per sequence
+    int chunk;    // cached tokens per partition (multiple of block_size)
+    int kernel;   // pa_kernel
+    int rt;       // query rows per workgroup (VALU: power of two <= 8)
+    int n_tiles;  // row tiles per KV head
+};
+
+int plan_impl(const pa_problem* p, int num_cus, Plan* pl) {
+    if (int rc = validate_problem(p)) return rc;
+    if (num_cus < 1) return fail(PA_ERR_INVALID_ARG, "num_cus = %d must be >= 1", num_cus);
+    const int R = (p->num_heads / p->num_kv_heads) * p->nq;
+    pl->kernel = PA_KERNEL_VALU;
+    int rt = 1;
+    while (rt < R && rt < 8) rt *= 2;
+    pl->rt = rt;
+    pl->n_tiles = (R + rt - 1) / rt;
+    const int BS = p->block_size;
+    const int64_t ctx = p->max_context_len;
+    const int64_t full = round_up(ctx > 0 ? ctx : 1, BS);  // one chunk covering everything
+    int64_t chunk;
+    if (p->num_partitions == 1) {
+        chunk = full;
+    } else if (p->num_partitions > 1) {
+        chunk = round_up(ceil_div(ctx > 0 ? ctx : 1, p->num_partitions), BS);
+    } else {
+        const int64_t units = (int64_t)p->batch * p->num_kv_heads * pl->n_tiles;
+        const int64_t target = (int64_t)num_cus * kGroupsPerCu;
+        const int64_t want = units > 0 ? ceil_div(target, units) : 1;
+        chunk = round_up(ceil_div(ctx > 0 ? ctx : 1, want > 1 ? want : 1), BS);
+        if (chunk < kMinChunkTokens) chunk = round_up(kMinChunkTokens, BS);
+        if (chunk > kMaxChunkTokens) chunk = kMaxChunkTokens;
+    }
+    if (chunk > full) chunk = full;
+    if (p->kernel == PA_KERNEL_VALU || p->kernel == PA_KERNEL_AUTO) pl->kernel = PA_KERNEL_VALU;
+    int64_t parts = ctx > 0 ? ceil_div(ctx, chunk) : 1;
+    if (parts > 65535 * 32767LL)
+        return fail(PA_ERR_UNSUPPORTED, "too many partitions (%lld)", (long long)parts);
+    pl->chunk = (int)chunk;
+    pl->parts = (int)parts;
+    return PA_OK;
+}
+
+size_t workspace_bytes_for(const pa_problem* p, const Plan& pl) {
+    if (pl.parts <= 1) return 0;
+    const size_t rows = (size_t)p->batch * p->num_heads * p->nq;
+    return rows * (size_t)pl.parts * (size_t)(p->head_dim + 2) * sizeof(float);
+}
+
+// Per-device property cache (compute units, gfx950 or not), filled once.
+struct DeviceInfo {
+    bool known = false;
+    bool gfx950 = false;
+    int cus = 0;
+    char arch[64] = {0};
+};
+std::mutex g_device_mutex;
+DeviceInfo g_devices[64];
+
+int current_device_cus(int* cus) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return fail(PA_ERR_DEVICE, "no HIP device is available; verify that a gfx950 GPU is "
+                    "visible to this process");
+    if (dev >= 64) return fail(PA_ERR_DEVICE, "device ordinal %d is out of range", dev);
+    std::lock_guard<std::mutex> lock(g_device_mutex);
+    DeviceInfo& info = g_devices[dev];
+    if (!info.known) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return fail(PA_ERR_DEVICE, "cannot read properties of device %d; verify the HIP "
+                        "runtime", dev);
+        info.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        info.cus = prop.multiProcessorCount;
+        std::snprintf(info.arch, sizeof info.arch, "%s", prop.gcnArchName);
+        info.known = true;
+    }
+    if (!info.gfx950)
+        return fail(PA_ERR_DEVICE, "device %d is %s, not gfx950 (MI355X); verify the selected "
+                    "device", dev, info.arch);
+    *cus = info.cus;
+    return PA_OK;
+}
+
+bool misaligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) != 0; }
+
+int validate_tensors(const pa_problem* p, const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_table, const int32_t* context_lens, const void* new_k,
+                     const void* new_v, const void* out) {
+    if (!q || !k_pool || !v_pool || !context_lens || !new_k || !new_v || !out)
+        return fail(PA_ERR_INVALID_ARG, "a tensor pointer is NULL (q %p, k_pool %p, v_pool %p, "
+                    "context_lens %p, new_k %p, new_v %p, out %p); verify the arguments", q,
+                    k_pool, v_pool, (const void*)context_lens, new_k, new_v, out);
+    if (!block_table && p->max_blocks_per_seq > 0)
+        return fail(PA_ERR_INVALID_ARG, "block_table is NULL; verify the arguments");
+    const void* t16[] = {q, k_pool, v_pool, new_k, new_v, out};
+    const char* n16[] = {"q", "k_pool", "v_pool", "new_k", "new_v", "out"};
+    for (int i = 0; i < 6; ++i)
+        if (misaligned(t16[i], 16))
+            return fail(PA_ERR_INVALID_ARG, "%s (%p) is not 16-byte aligned; verify the tensor "
+                        "storage offset", n16[i], t16[i]);
+    if (misaligned(block_table, 4) || misaligned(context_lens, 4))
+        return fail(PA_ERR_INVALID_ARG, "block_table/context_lens must be 4-byte aligned");
+    return PA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel dispatch over the compile-time shapes.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int BS>
+void launch_valu(const Plan& pl, dim3 grid, hipStream_t s, const pa::DecodeArgs<T>& a) {
+    switch (pl.rt) {
+        case 1: hipLaunchKernelGGL((pa::decode_valu<T, D, BS, 1>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((pa::decode_valu<T, D, BS, 2>), grid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((pa::decode_valu<T, D, BS, 4>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((pa::decode_valu<T, D, BS, 8>), grid, dim3(256), 0, s, a); break;
+    }
+}
+
+template <typename T>
+void launch_pass1(const pa_problem* p, const Plan& pl, hipStream_t s, const pa::DecodeArgs<T>& a) {
+    const dim3 grid(pl.parts, p->num_kv_heads * pl.n_tiles, p->batch);
+    if (p->head_dim == 64) {
+        if (p->block_size == 16) launch_valu<T, 64, 16>(pl, grid, s, a);
+        else launch_valu<T, 64, 32>(pl, grid, s, a);
+    } else {
+        if (p->block_size == 16) launch_valu<T, 128, 16>(pl, grid, s, a);
+        else launch_valu<T, 128, 32>(pl, grid, s, a);
+    }
+}
+
+template <typename T>
+void launch_combine(const pa_problem* p, const Plan& pl, hipStream_t s, const float* ws,
+                    const int32_t* lens, void* out) {
+    pa::CombineArgs<T> c;
+    const int64_t rows = (int64_t)p->batch * p->num_heads * p->nq;
+    c.ws_o = ws;
+    c.ws_ml = ws + rows * pl.parts * p->head_dim;
+    c.context_lens = lens;
+    c.out = static_cast<T*>(out);
+    c.rows = rows;
+    c.rows_per_seq = p->num_heads * p->nq;
+    c.n_parts = pl.parts;
+    c.chunk = pl.chunk;
+    const dim3 grid((unsigned)ceil_div(rows, 4));
+    if (p->head_dim == 64)
+        hipLaunchKernelGGL((pa::combine_partitions<T, 64>), grid, dim3(256), 0, s, c);
+    else
+        hipLaunchKernelGGL((pa::combine_partitions<T, 128>), grid, dim3(256), 0, s, c);
+}
+
+template <typename T>
+int run_decode(const pa_problem* p, const Plan& pl, const void* q, const void* k_pool,
+               const void* v_pool, const int32_t* block_table, const int32_t* context_lens,
+               const void* new_k, const void* new_v, float scale, void* out, void* workspace,
+               hipStream_t s) {
+    pa::DecodeArgs<T> a;
+    const int64_t rows = (int64_t)p->batch * p->num_heads * p->nq;
+    a.q = static_cast<const T*>(q);
+    a.k_pool = static_cast<const T*>(k_pool);
+    a.v_pool = static_cast<const T*>(v_pool);
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.new_k = static_cast<const T*>(new_k);
+    a.new_v = static_cast<const T*>(new_v);
+    a.out = static_cast<T*>(out);
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = workspace ? static_cast<float*>(workspace) + rows * pl.parts * p->head_dim : nullptr;
+    a.H = p->num_heads;
+    a.KV = p->num_kv_heads;
+    a.NQ = p->nq;
+    a.causal = p->causal;
+    a.max_blocks = p->max_blocks_per_seq;
+    a.chunk = pl.chunk;
+    a.n_parts = pl.parts;
+    a.n_tiles = pl.n_tiles;
+    a.qscale = (float)((double)scale * 1.4426950408889634);
+    launch_pass1<T>(p, pl, s, a);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess)
+        return fail(PA_ERR_LAUNCH, "pass-1 launch failed: %s; verify the device state",
+                    hipGetErrorString(e));
+    if (pl.parts > 1) {
+        launch_combine<T>(p, pl, s, static_cast<const float*>(workspace), context_lens, out);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess)
+            return fail(PA_ERR_LAUNCH, "combine launch failed: %s; verify the device state",
+                        hipGetErrorString(e));
+    }
+    return succeed();
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_plan_ex(const pa_problem* problem, int32_t num_cus, int32_t* partitions,
+               int32_t* chunk_tokens, int32_t* kernel) {
+    Plan pl;
+    if (int rc = plan_impl(problem, num_cus, &pl)) return rc;
+    if (partitions) *partitions = pl.parts;
+    if (chunk_tokens) *chunk_tokens = pl.chunk;
+    if (kernel) *kernel = pl.kernel;
+    return succeed();
+}
+
+int pa_plan(const pa_problem* problem, int32_t* partitions, int32_t* chunk_tokens,
+            int32_t* kernel) {
+    if (int rc = validate_problem(problem)) return rc;
+    int cus = 0;
+    if (int rc = current_device_cus(&cus)) return rc;
+    return pa_plan_ex(problem, cus, partitions, chunk_tokens, kernel);
+}
+
+int pa_workspace_size_ex(const pa_problem* problem, int32_t num_cus, size_t* bytes) {
+    if (!bytes) return fail(PA_ERR_INVALID_ARG, "bytes is NULL");
+    Plan pl;
+    if (int rc = plan_impl(problem, num_cus, &pl)) return rc;
+    *bytes = workspace_bytes_for(problem, pl);
+    return succeed();
+}
+
+int pa_workspace_size(const pa_problem* problem, size_t* bytes) {
+    if (!bytes) return fail(PA_ERR_INVALID_ARG, "bytes is NULL");
+    if (int rc = validate_problem(problem)) return rc;
+    int cus = 0;
+    if (int rc = current_device_cus(&cus)) return rc;
+    return pa_workspace_size_ex(problem, cus, bytes);
+}
+
+int paged_attn_decode(const pa_problem* problem, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_table,
+                      const int32_t* context_lens, const void* new_k, const void* new_v,
+                      float scale, void* out, void* workspace, size_t workspace_bytes,
+                      pa_stream_t stream) {
+    if (int rc = validate_problem(problem)) return rc;
+    if (problem->batch == 0) return succeed();
+    if (int rc = validate_tensors(problem, q, k_pool, v_pool, block_table, context_lens, new_k,
+                                  new_v, out))
+        return rc;
+    if (workspace && misaligned(workspace, 16))
+        return fail(PA_ERR_INVALID_ARG, "workspace (%p) is not 16-byte aligned", workspace);
+    int cus = 0;
+    if (int rc = current_device_cus(&cus)) return rc;
+    Plan pl;
+    if (int rc = plan_impl(problem, cus, &pl)) return rc;
+    const size_t need = workspace_bytes_for(problem, pl);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes at %p is smaller than the %zu bytes "
+                    "this plan needs (%d partitions); verify pa_workspace_size",
+                    workspace_bytes, workspace, need, pl.parts);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    switch (problem->dtype) {
+        case PA_F32:
+            return run_decode<float>(problem, pl, q, k_pool, v_pool, block_table, context_lens,
+                                     new_k, new_v, scale, out, workspace, s);
+        case PA_F16:
+            return run_decode<_Float16>(problem, pl, q, k_pool, v_pool, block_table,
+                                        context_lens, new_k, new_v, scale, out, workspace, s);
+        default:
+            return run_decode<pa::bf16_t>(problem, pl, q, k_pool, v_pool, block_table,
+                                          context_lens, new_k, new_v, scale, out, workspace, s);
+    }
+}
+
+int paged_attn_combine(const pa_problem* problem, const int32_t* context_lens,
+                       const void* workspace, size_t workspace_bytes, void* out,
+                       pa_stream_t stream) {
+    if (int rc = validate_problem(problem)) return rc;
+    if (problem->batch == 0) return succeed();
+    if (!context_lens || !out)
+        return fail(PA_ERR_INVALID_ARG, "context_lens or out is NULL; verify the arguments");
+    if (misaligned(out, 16) || misaligned(context_lens, 4))
+        return fail(PA_ERR_INVALID_ARG, "out must be 16-byte and context_lens 4-byte aligned");
+    int cus = 0;
+    if (int rc = current_device_cus(&cus)) return rc;
+    Plan pl;
+    if (int rc = plan_impl(problem, cus, &pl)) return rc;
+    if (pl.parts <= 1) return succeed();
+    const size_t need = workspace_bytes_for(problem, pl);
+    if (!workspace || workspace_bytes < need || misaligned(workspace, 16))
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes at %p does not hold the %zu bytes "
+                    "of partial states this plan uses; verify pa_workspace_size",
+                    workspace_bytes, workspace, need);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const float* ws = static_cast<const float*>(workspace);
+    switch (problem->dtype) {
+        case PA_F32: launch_combine<float>(problem, pl, s, ws, context_lens, out); break;
+        case PA_F16: launch_combine<_Float16>(problem, pl, s, ws, context_lens, out); break;
+        default: launch_combine<pa::bf16_t>(problem, pl, s, ws, context_lens, out); break;
+    }
+    if (hipError_t e = hipGetLastError(); e != hipSuccess)
+        return fail(PA_ERR_LAUNCH, "combine launch failed: %s; verify the device state",
+                    hipGetErrorString(e));
+    return succeed();
+}
+
+const char* paged_attn_last_error(void) { return t_error.c_str(); }
+
+int paged_attn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+"""C-ABI boundary on the CPU: the library loads, exports what the header
+declares, validates arguments on the host and plans launches (no GPU calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_gqa_decode_amd as pa
+from paged_kv_gqa_decode_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.LIB_PATH):
+        pytest.fail("libpaged_attn.so is not built; run __graft_entry__.build()")
+    return pa.library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) == set(pa.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert pa.paged_attn_version() == 100
+
+
+def spec_problem(spec: W.Spec, max_ctx: int, **kw) -> pa.PaProblem:
+    d = dict(batch=spec.B, num_heads=spec.H, num_kv_heads=spec.KV, head_dim=spec.D,
+             block_size=spec.BS, num_blocks=1000, max_blocks_per_seq=spec.max_blocks,
+             nq=spec.NQ, causal=int(spec.causal), dtype=W.DTYPES[spec.dtype][1],
+             max_context_len=max_ctx, num_partitions=0, kernel=0)
+    d.update(kw)
+    return pa.PaProblem(**d)
+
+
+# (config index, max_context_len) -> (partitions, chunk_tokens) on a 256-CU device
+PLAN_TABLE = [
+    (0, 100, 1, 112),
+    (1, 4096, 8, 512),
+    (2, 131072, 64, 2048),
+    (4, 16384, 8, 2048),
+    (4, 1000, 1, 1024),
+]
+
+
+@pytest.mark.parametrize("cfg,ctx,parts,chunk", PLAN_TABLE)
+def test_plan_table(lib, cfg, ctx, parts, chunk):
+    rc, p, c, k = pa.pa_plan_ex(spec_problem(W.CONFIGS[cfg], ctx), 256)
+    assert (p, c) == (parts, chunk)
+    assert c % W.CONFIGS[cfg].BS == 0 and p * c >= ctx
+    assert k in (pa.PA_KERNEL_VALU, pa.PA_KERNEL_MFMA)
+
+
+@pytest.mark.parametrize("forced", [1, 2, 3, 7, 64])
+def test_forced_partitions_cover_the_context(lib, forced):
+    prob = spec_problem(W.CONFIGS[1], 4000, num_partitions=forced)
+    _, p, c, _ = pa.pa_plan_ex(prob, 256)
+    assert 1 <= p <= forced and p * c >= 4000 and (p - 1) * c < 4000 and c % 16 == 0
+
+
+def test_workspace_size(lib):
+    prob = spec_problem(W.CONFIGS[1], 4096)
+    _, nbytes = pa.pa_workspace_size_ex(prob, 256)
+    _, p, _, _ = pa.pa_plan_ex(prob, 256)
+    assert nbytes == 32 * 32 * 1 * p * (128 + 2) * 4
+    _, single = pa.pa_workspace_size_ex(spec_problem(W.CONFIGS[0], 100), 256)
+    assert single == 0
+
+
+BAD = [
+    (dict(head_dim=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(block_size=8), pa.PA_ERR_UNSUPPORTED),
+    (dict(nq=0), pa.PA_ERR_INVALID_ARG),
+    (dict(num_heads=6, num_kv_heads=4), pa.PA_ERR_INVALID_ARG),
+    (dict(num_kv_heads=0), pa.PA_ERR_INVALID_ARG),
+    (dict(dtype=7), pa.PA_ERR_INVALID_ARG),
+    (dict(causal=2), pa.PA_ERR_INVALID_ARG),
+    (dict(max_context_len=10 ** 6), pa.PA_ERR_INVALID_ARG),
+    (dict(max_context_len=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(batch=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(num_blocks=0), pa.PA_ERR_INVALID_ARG),
+    (dict(num_partitions=-2), pa.PA_ERR_INVALID_ARG),
+    (dict(kernel=9), pa.PA_ERR_INVALID_ARG),
+    (dict(nq=64, num_heads=32), pa.PA_ERR_UNSUPPORTED),  # G*nq = 256 rows > 128
+]
+
+
+@pytest.mark.parametrize("override,code", BAD, ids=[str(b[0]) for b in BAD])
+def test_invalid_problems_rejected_on_host(lib, override, code):
+    prob = spec_problem(W.CONFIGS[1], 4096, **override)
+    rc, *_ = pa.pa_plan_ex(prob, 256, raise_on_error=False)
+    assert rc == code
+    assert "verify" in pa.paged_attn_last_error() or len(pa.paged_attn_last_error()) > 10
+    # the same problem is rejected by the launch entry point before any HIP call
+    rc = pa.paged_attn_decode(prob, 16, 16, 16, 16, 16, 16, 16, 0.1, 16, None, 0, None,
+                              raise_on_error=False)
+    assert rc == code
+
+
+def test_null_and_misaligned_pointers(lib):
+    prob = spec_problem(W.CONFIGS[1], 4096)
+    good = [4096] * 7
+    for i in range(7):
+        args = list(good)
+        args[i] = None
+        rc = pa.paged_attn_decode(prob, *args, 0.1, 4096, None, 0, None, raise_on_error=False)
+        assert rc == pa.PA_ERR_INVALID_ARG, i
+    args = list(good)
+    args[0] = 4096 + 8  # q misaligned
+    rc = pa.paged_attn_decode(prob, *args, 0.1, 4096, None, 0, None, raise_on_error=False)
+    assert rc == pa.PA_ERR_INVALID_ARG and "aligned" in pa.paged_attn_last_error()
+    rc = pa.paged_attn_decode(prob, *good, 0.1, 4096 + 2, None, 0, None, raise_on_error=False)
+    assert rc == pa.PA_ERR_INVALID_ARG
+
+
+def test_empty_batch_is_a_no_op(lib):
+    prob = spec_problem(W.CONFIGS[1], 4096, batch=0)
+    assert pa.paged_attn_decode(prob, None, None, None, None, None, None, None, 0.1, None,
+                                None, 0, None, raise_on_error=False) == pa.PA_OK
+
+
+def test_valid_call_without_a_gfx950_device_reports_device_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    prob = spec_problem(W.CONFIGS[1], 4096)
+    rc = pa.paged_attn_decode(prob, *([4096] * 7), 0.1, 4096, None, 0, None,
+                              raise_on_error=False)
+    assert rc == pa.PA_ERR_DEVICE

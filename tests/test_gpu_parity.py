@@ -1,0 +1,233 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerances (max-abs against the fp64 oracle): 1e-5 for fp32 I/O, 4e-3 for
+fp16/bf16 I/O. Block-table indexing must be bit-exact: outputs for the same
+logical cache stored in another physical block order are compared with
+torch.equal, and poisoned (NaN) unused pool space must not change a bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_gqa_decode_amd as pa
+from paged_kv_gqa_decode_amd import workloads as W
+from tests import problems as P
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 4e-3, "bf16": 4e-3}
+DEV = "cuda:0"
+
+
+def to_device(w: W.Workload) -> W.Workload:
+    return W.Workload(w.spec, w.context_lens, w.block_table, w.num_blocks, w.q.to(DEV),
+                      w.k_pool.to(DEV), w.v_pool.to(DEV), w.new_k.to(DEV), w.new_v.to(DEV),
+                      w.scale)
+
+
+def gpu_decode(w: W.Workload, num_partitions=0, kernel=0, max_context_len=None):
+    assert w.q.is_cuda
+    table = torch.from_numpy(np.ascontiguousarray(w.block_table)).to(DEV)
+    lens = torch.from_numpy(np.ascontiguousarray(w.context_lens)).to(DEV)
+    mcl = w.max_context_len if max_context_len is None else max_context_len
+    print(f"[gpu] {w.spec.name} B={w.spec.B} dtype={w.spec.dtype} parts={num_partitions} "
+          f"kernel={kernel} max_ctx={mcl}", flush=True)
+    out = pa.decode(w.q, w.k_pool, w.v_pool, table, lens, w.new_k, w.new_v, w.scale,
+                    max_context_len=mcl, causal=w.spec.causal,
+                    num_partitions=num_partitions, kernel=kernel)
+    torch.cuda.synchronize()
+    return out
+
+
+def ref(w: W.Workload) -> np.ndarray:
+    return oracle.paged_decode(*P.args(w), causal=w.spec.causal)
+
+
+def max_err(out: torch.Tensor, expect: np.ndarray) -> float:
+    return float(np.abs(out.detach().cpu().double().numpy() - expect).max()) if expect.size else 0.0
+
+
+def check(w, out, expect=None):
+    expect = ref(w) if expect is None else expect
+    err = max_err(out, expect)
+    assert np.isfinite(out.detach().cpu().double().numpy()).all()
+    assert err <= TOL[w.spec.dtype], f"max-abs error {err} > {TOL[w.spec.dtype]}"
+    return err
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at full size (every output compared)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", range(len(W.CONFIGS)), ids=[c.name for c in W.CONFIGS])
+def test_config_full_size(cfg):
+    w = W.make_workload(W.CONFIGS[cfg], device=DEV)
+    out = gpu_decode(w)
+    err = check(w, out)
+    print(f"[gpu] {W.CONFIGS[cfg].name}: max-abs error {err:.3e}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Shrunken variants: several pages per wave, ragged tails, several partitions
+# ---------------------------------------------------------------------------
+SMALL = [
+    W.shrink(W.CONFIGS[1], B=5, lengths=("list", (0, 1, 17, 700, 1999)), max_blocks=125),
+    W.shrink(W.CONFIGS[2], B=2, lengths=("list", (5000, 9001)), max_blocks=600),
+    W.shrink(W.CONFIGS[3], B=3, lengths=("list", (0, 35, 300)), max_blocks=20),
+    W.shrink(W.CONFIGS[4], B=9, lengths=("lognormal", 200, 1.0, 16, 3000), max_blocks=100),
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[s.name for s in SMALL])
+@pytest.mark.parametrize("parts", [0, 1, 2, 3, 7])
+def test_small_variants_all_partitions(spec, parts):
+    w = W.make_workload(spec, device=DEV)
+    check(w, gpu_decode(w, num_partitions=parts))
+
+
+GEOMETRIES = [
+    # B, H, KV, D, BS, NQ, causal, dtype, lens
+    (2, 4, 4, 64, 16, 1, True, "f32", (0, 77)),        # MHA
+    (3, 8, 1, 64, 32, 3, True, "f16", (15, 16, 33)),   # MQA, multi-row
+    (2, 8, 2, 128, 32, 3, False, "bf16", (31, 64)),    # non-causal multi-row
+    (2, 16, 2, 128, 16, 8, True, "f16", (0, 333)),     # 64 rows per KV head
+    (1, 32, 2, 128, 16, 8, True, "bf16", (500,)),      # 128 rows per KV head
+    (2, 4, 2, 64, 16, 2, True, "f32", (129, 1)),
+    (2, 4, 2, 128, 32, 1, True, "f32", (700, 64)),
+]
+
+
+@pytest.mark.parametrize("case", GEOMETRIES, ids=lambda c: "-".join(map(str, c[:8])))
+def test_geometries(case):
+    B, H, KV, D, BS, NQ, causal, dtype, lens = case
+    w = to_device(P.small(B=B, H=H, KV=KV, D=D, BS=BS, NQ=NQ, causal=causal, dtype=dtype,
+                          lens=lens, seed=31))
+    expect = ref(w)
+    for parts in (0, 1, 3):
+        check(w, gpu_decode(w, num_partitions=parts), expect)
+
+
+# ---------------------------------------------------------------------------
+# Block-table indexing: bit-exact invariants
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_block_order_is_bit_exact(dtype):
+    w = P.small(B=3, H=8, KV=2, D=128, BS=16, NQ=2, causal=True, dtype=dtype,
+                lens=(70, 16, 333), seed=3)
+    base = gpu_decode(to_device(w), num_partitions=2)
+    for seed in (1, 2):
+        w2 = to_device(P.relayout(w, shuffle_seed=seed, extra_blocks=7))
+        assert torch.equal(gpu_decode(w2, num_partitions=2), base)
+    check(to_device(w), base)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_unused_pool_space_and_table_entries_are_never_read(dtype):
+    w = P.small(B=3, H=8, KV=2, D=128, BS=16, NQ=1, dtype=dtype, lens=(45, 3, 160), seed=4)
+    clean = to_device(P.relayout(w, shuffle_seed=5, extra_blocks=6))
+    base = gpu_decode(clean, num_partitions=3)
+    poisoned = P.relayout(w, shuffle_seed=5, extra_blocks=6, fill=float("nan"))
+    # table entries past each sequence's last page point at poisoned blocks
+    spare = sorted(set(range(poisoned.num_blocks)) - set(
+        int(poisoned.block_table[b, n]) for b in range(3)
+        for n in range((int(poisoned.context_lens[b]) + 15) // 16)))
+    wide = np.zeros((3, poisoned.block_table.shape[1] + 4), dtype=np.int32)
+    wide[:, :poisoned.block_table.shape[1]] = poisoned.block_table
+    for b in range(3):
+        used = (int(poisoned.context_lens[b]) + 15) // 16
+        wide[b, used:] = spare[b % len(spare)]
+    poisoned.block_table = wide
+    poisoned.spec = poisoned.spec.replace(max_blocks=wide.shape[1])
+    out = gpu_decode(to_device(poisoned), num_partitions=3)
+    assert torch.isfinite(out.float()).all()
+    assert torch.equal(out, base)
+
+
+def test_argmax_probe_maps_every_position():
+    # Sequence b makes logical position t_b dominate for head 0: out must be v_t.
+    ts = [0, 1, 15, 16, 17, 31, 63, 100, 255]
+    lens = [256] * len(ts)
+    w = P.small(B=len(ts), H=2, KV=1, D=128, BS=16, NQ=1, dtype="f16", lens=lens, seed=8)
+    w = P.relayout(w, shuffle_seed=12, extra_blocks=3)
+    expect = []
+    for b, t in enumerate(ts):
+        phys = int(w.block_table[b, t // 16])
+        w.k_pool[phys, t % 16, 0] = (w.q[b, 0, 0].float() * 8.0).to(torch.float16)
+        expect.append(w.v_pool[phys, t % 16, 0].float())
+    out = gpu_decode(to_device(w), num_partitions=1).cpu().float()
+    for b in range(len(ts)):
+        assert (out[b, 0, 0] - expect[b]).abs().max() < 2e-3, ts[b]
+
+
+# ---------------------------------------------------------------------------
+# Closed forms and special cases
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_single_key_returns_new_v_exactly(dtype):
+    w = to_device(P.small(B=3, H=8, KV=2, D=128, BS=16, NQ=1, dtype=dtype, lens=(0, 0, 0)))
+    out = gpu_decode(w)
+    G = 4
+    for h in range(8):
+        assert torch.equal(out[:, h, 0], w.new_v[:, h // G, 0])
+
+
+def test_equal_scores_give_the_mean():
+    w = P.small(B=2, H=4, KV=2, D=64, NQ=3, causal=True, lens=(21, 300), dtype="f32", seed=9)
+    w.q.zero_()
+    wd = to_device(w)
+    expect = ref(w)
+    for parts in (1, 4):
+        check(wd, gpu_decode(wd, num_partitions=parts), expect)
+
+
+def test_causality_is_bit_exact():
+    w = P.small(B=2, H=4, KV=2, D=128, NQ=4, causal=True, lens=(10, 90), dtype="bf16", seed=10)
+    base = gpu_decode(to_device(w))
+    for j in range(1, 4):
+        w2 = P.small(B=2, H=4, KV=2, D=128, NQ=4, causal=True, lens=(10, 90), dtype="bf16", seed=10)
+        w2.new_k[:, :, j] += 3.0
+        w2.new_v[:, :, j] -= 2.0
+        out = gpu_decode(to_device(w2))
+        assert torch.equal(out[:, :, :j], base[:, :, :j])
+
+
+def test_combine_remerges_the_workspace():
+    w = to_device(W.make_workload(SMALL[0], device="cpu"))
+    table = torch.from_numpy(w.block_table).to(DEV)
+    lens = torch.from_numpy(w.context_lens).to(DEV)
+    dec = pa.Decoder(w.q, w.k_pool, table, max_context_len=w.max_context_len, num_partitions=4)
+    assert dec.partitions > 1
+    out = dec(w.q, w.k_pool, w.v_pool, table, lens, w.new_k, w.new_v, w.scale).clone()
+    torch.cuda.synchronize()
+    # rows of multi-partition sequences are rebuilt from the workspace alone
+    again = out.clone()
+    multi = [b for b in range(w.spec.B) if int(w.context_lens[b]) > dec.chunk_tokens]
+    assert multi
+    again[multi] = 0
+    pa.paged_attn_combine(dec.problem, lens, dec.workspace, dec.workspace_bytes, again,
+                          stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert torch.equal(again, out)
+
+
+def test_workspace_too_small_is_rejected():
+    w = to_device(W.make_workload(SMALL[1], device="cpu"))
+    table = torch.from_numpy(w.block_table).to(DEV)
+    lens = torch.from_numpy(w.context_lens).to(DEV)
+    prob = pa.make_problem(w.q, w.k_pool, table, max_context_len=w.max_context_len,
+                           num_partitions=4)
+    _, need = pa.pa_workspace_size(prob)
+    assert need > 0
+    ws = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(w.q)
+    rc = pa.paged_attn_decode(prob, w.q, w.k_pool, w.v_pool, table, lens, w.new_k, w.new_v,
+                              w.scale, out, ws, need - 16, raise_on_error=False)
+    assert rc == pa.PA_ERR_WORKSPACE
+
+
+def test_plan_on_device_matches_pure_host_plan():
+    w = W.make_workload(SMALL[0], device="cpu")
+    prob = pa.make_problem(w.q, w.k_pool, torch.from_numpy(w.block_table),
+                           max_context_len=w.max_context_len)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert pa.pa_plan(prob)[1:] == pa.pa_plan_ex(prob, cus)[1:]
