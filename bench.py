@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config I] [--gpus 1]
+
+Workload (default): the Llama-3-8B shaped decode batch (B=32, H=32, KV=8, D=128,
+BLOCK=16, fp16 pools, context lengths uniform in 512..4096, NQ=1), seeded
+synthetic data generated on the GPU. `--config` selects another workload of
+paged_kv_gqa_decode_amd.workloads.CONFIGS (0..4).
+
+One step = one paged_attn_decode call (every kernel the step needs). W untimed
+steps, then K timed steps, bracketed by torch.cuda.synchronize(). Pools are
+rotated over `--replicas` copies so the working set exceeds the 256 MB
+Infinity Cache. Per-launch HIP events on the launch stream give the kernel
+duration used for the roofline.
+
+Prints ONE JSON line (stdout):
+  value  = KV GB/s over the timed region, KV bytes = sum_b (L_b + NQ)*KV*D*2*s
+  roofline.achieved = KV bytes per launch / mean per-launch event duration
+  cpu_baseline = the oracle (plain C, fp64) on this host's cores, same workload
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention µs/step + achieved KV GB/s (% of MI355X HBM peak)"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_NAMES = {1: "valu", 2: "mfma"}
+CSRC = os.path.join(ROOT, "paged_kv_gqa_decode_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kv_bytes: int):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(workload)
+    if not entry or entry.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, seconds: float):
+    """Time the oracle on the host: one warm-up, then repeats until `seconds`."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from paged_kv_gqa_decode_amd import workloads as W
+
+    host = W.Workload(w.spec, w.context_lens, w.block_table, w.num_blocks, w.q.cpu(),
+                      w.k_pool.cpu(), w.v_pool.cpu(), w.new_k.cpu(), w.new_v.cpu(), w.scale)
+    # Probe on one sequence to bound the sample.
+    def run(nseq):
+        lens = host.context_lens[:nseq]
+        t0 = time.perf_counter()
+        oracle.paged_decode(host.q[:nseq], host.k_pool, host.v_pool, host.block_table[:nseq],
+                            lens, host.new_k[:nseq], host.new_v[:nseq], host.scale,
+                            causal=w.spec.causal)
+        return time.perf_counter() - t0
+
+    B = w.spec.B
+    probe = run(1)
+    per_seq = max(probe, 1e-4)
+    nseq = B if per_seq * B <= seconds / 3 else max(1, int(seconds / 3 / per_seq))
+    run(nseq)  # warm-up
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 or (time.perf_counter() - t_start < seconds and len(times) < 50):
+        times.append(run(nseq))
+    t = statistics.median(times)
+    s = w.spec
+    sample_bytes = int(sum(int(L) + s.NQ for L in host.context_lens[:nseq])) * s.KV * s.D * 2 * w.elem_bytes
+    return {
+        "value": sample_bytes / t / 1e9,
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"{'all' if nseq == B else 'first'} {nseq} of {B} sequences of the same "
+                   f"workload, median of {len(times)} runs after 1 warm-up "
+                   f"({sum(times):.1f} s of CPU time)"),
+        "us_per_step_equiv": t / nseq * B * 1e6,
+        "cpu_model": cpu_model(),
+    }
+
+
+def copy_bandwidth(torch, nbytes=1 << 30, reps=10) -> float:
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del a, b
+    return 2 * nbytes / sec / 1e9
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 valu, 2 mfma")
+    ap.add_argument("--partitions", type=int, default=0, help="0 = launch heuristic")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build runs every kernel on a single "
+              "MI355X and has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_gqa_decode_amd as pa
+    from paged_kv_gqa_decode_amd import workloads as W
+
+    spec = W.CONFIGS[args.config]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(f"[bench] generating {spec.name} on {dev}")
+    w = W.make_workload(spec, device=dev)
+    table = torch.from_numpy(w.block_table).to(dev)
+    lens = torch.from_numpy(w.context_lens).to(dev)
+    kpools = [w.k_pool] + [w.k_pool.clone() for _ in range(args.replicas - 1)]
+    vpools = [w.v_pool] + [w.v_pool.clone() for _ in range(args.replicas - 1)]
+    dec = pa.Decoder(w.q, w.k_pool, table, max_context_len=w.max_context_len, causal=spec.causal,
+                     num_partitions=args.partitions, kernel=args.kernel)
+    stream = torch.cuda.current_stream()
+    kvb = W.kv_bytes(w)
+    log(f"[bench] kv bytes/step {kvb}, partitions {dec.partitions}, chunk {dec.chunk_tokens}, "
+        f"kernel {KERNEL_NAMES.get(dec.kernel, dec.kernel)}, workspace {dec.workspace_bytes} B")
+
+    def step(i):
+        r = i % len(kpools)
+        dec(w.q, kpools[r], vpools[r], table, lens, w.new_k, w.new_v, w.scale, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    region_ms = starts[0].elapsed_time(ends[-1])
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = region_ms / K
+    mean_launch_ms = sum(per_launch_ms) / K
+    value = kvb / (ms_per_step / 1e3) / 1e9
+    achieved = kvb / (mean_launch_ms / 1e3) / 1e9
+    log(f"[bench] {ms_per_step * 1e3:.2f} us/step (region), mean launch {mean_launch_ms * 1e3:.2f} us, "
+        f"p10 {sorted(per_launch_ms)[K // 10] * 1e3:.2f} p90 {sorted(per_launch_ms)[(9 * K) // 10] * 1e3:.2f} us, "
+        f"wall {wall / K * 1e6:.2f} us/step, {value:.1f} GB/s")
+
+    copy_gbps = copy_bandwidth(torch)
+    log(f"[bench] device copy bandwidth {copy_gbps:.0f} GB/s (read+write)")
+    traffic = measured_traffic(spec.name, kvb)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        log(f"[bench] oracle {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": spec.name,
+            "batch": spec.B, "num_heads": spec.H, "num_kv_heads": spec.KV, "head_dim": spec.D,
+            "block_size": spec.BS, "nq": spec.NQ, "causal": spec.causal, "io_dtype": spec.dtype,
+            "context_lens": list(spec.lengths), "kv_bytes_per_step": kvb,
+            "partitions": dec.partitions, "chunk_tokens": dec.chunk_tokens,
+            "kernel": KERNEL_NAMES.get(dec.kernel, dec.kernel), "pool_replicas": len(kpools),
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "paged_attn_decode launch (pass 1 + merge)",
+            "mean_launch_us": round(mean_launch_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": kvb,
+        },
+        "device_copy_gbps": round(copy_gbps, 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

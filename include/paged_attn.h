@@ -96,7 +96,8 @@ typedef struct {
     int32_t max_context_len;    /* host-side upper bound of context_lens, >= 0 */
     int32_t num_partitions;     /* 0: heuristic; 1: single pass; > 1: at most this many
                                    key partitions per sequence (tests, tuning) */
-    int32_t kernel;             /* pa_kernel; PA_KERNEL_AUTO unless forcing a family */
+    int32_t kernel;             /* pa_kernel; PA_KERNEL_AUTO unless forcing a family.
+                                   PA_KERNEL_MFMA needs fp16/bf16 and (H/KV)*nq <= 64 */
 } pa_problem;
 
 /*
@@ -118,15 +119,15 @@ int pa_plan(const pa_problem* problem, int32_t* partitions, int32_t* chunk_token
 
 /*
  * Workspace bytes paged_attn_decode needs on the current device: 0 for a
- * single-pass plan, else rows * partitions * (head_dim + 2) * 4 with
- * rows = batch * num_heads * nq. Layout (fp32), row = (b*H + h)*nq + r:
- *   o[row][p][head_dim]  unnormalised partial output  sum_i 2^(t_i - m) v_i
- *   ml[row][p][2]        (m, l): m = max_i t_i, l = sum_i 2^(t_i - m)
- * where t_i = s_i * log2(e), over the keys of partition p of that row: the
+ * single-pass plan. Otherwise, with rows = batch * num_heads * nq and P =
+ * partitions, the fp32 layout is (row = (b*H + h)*nq + r):
+ *   o[rows][P][head_dim]  unnormalised partial output  sum_i 2^(t_i - m) v_i
+ *   ml[rows][P][2]        (m, l): m = max_i t_i, l = sum_i 2^(t_i - m)
+ * where t_i = s_i * log2(e) over the keys of partition p of that row: the
  * page's VECTOR_PARTIALS state in base-2 units. Partitions past a sequence's
  * last one are not written, and neither are the rows of a sequence whose keys
- * fit in one partition (pass 1 writes their final output directly).
- * pa_workspace_size_ex is the same for a device with num_cus compute units
+ * fit in one partition (their output is final after pass 1). No initial
+ * contents are required. pa_workspace_size_ex is the same for a device with num_cus compute units
  * (pure host).
  */
 int pa_workspace_size(const pa_problem* problem, size_t* bytes);
@@ -138,8 +139,9 @@ int pa_workspace_size_ex(const pa_problem* problem, int32_t num_cus, size_t* byt
  * more than one partition, paged_attn_combine's kernel after it. Asynchronous:
  * returns once the work is enqueued. `scale` multiplies q.k (binary32, as the
  * page passes the scale's fp32 bits). `workspace` may be NULL when
- * pa_workspace_size reports 0. q/new_k/new_v/pools/tables are only read; `out`
- * and the workspace are written. Buffers must not overlap `out`.
+ * pa_workspace_size reports 0; otherwise it must hold that many bytes. Calls
+ * sharing a workspace must not run concurrently. q/new_k/new_v/pools/tables
+ * are only read; `out` and the workspace are written.
  */
 int paged_attn_decode(const pa_problem* problem, const void* q, const void* k_pool,
                       const void* v_pool, const int32_t* block_table,
@@ -148,8 +150,9 @@ int paged_attn_decode(const pa_problem* problem, const void* q, const void* k_po
                       pa_stream_t stream);
 
 /*
- * Merge step alone (page: PARTIALS_REDUCE). Reads the partial states a
- * partitioned paged_attn_decode left in `workspace` for the same problem and
+ * Merge step alone (page: PARTIALS_REDUCE), as its own kernel. Reads the
+ * partial states a partitioned paged_attn_decode left in `workspace` for the
+ * same problem and
  * context_lens, and writes out = (sum_p 2^(m_p - M) o_p) / (sum_p 2^(m_p - M) l_p)
  * with M = max_p m_p over each row's partitions (0 when that sum is 0), rounded
  * to nearest-even in the I/O dtype. Rows of sequences that fit in one partition

@@ -192,7 +192,8 @@ class Decoder:
         _, self.partitions, self.chunk_tokens, self.kernel = pa_plan(self.problem)
         _, self.workspace_bytes = pa_workspace_size(self.problem)
         dev = q.device
-        self.workspace = (torch.empty(self.workspace_bytes, dtype=torch.uint8, device=dev)
+        # zero-filled once: the library keeps its ticket counters at zero
+        self.workspace = (torch.zeros(self.workspace_bytes, dtype=torch.uint8, device=dev)
                           if self.workspace_bytes else None)
         self.out = torch.empty_like(q)
 

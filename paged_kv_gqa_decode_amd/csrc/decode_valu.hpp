@@ -21,25 +21,9 @@
 // 4 waves are merged once at the end of the chunk.
 #pragma once
 
-#include "pa_device.hpp"
+#include "epilogue.hpp"
 
 namespace pa {
-
-template <typename T>
-struct DecodeArgs {
-    const T* q;
-    const T* k_pool;
-    const T* v_pool;
-    const int32_t* block_table;
-    const int32_t* context_lens;
-    const T* new_k;
-    const T* new_v;
-    T* out;
-    float* ws_o;   // [rows][n_parts][D]
-    float* ws_ml;  // [rows][n_parts][2]
-    int H, KV, NQ, causal, max_blocks, chunk, n_parts, n_tiles;
-    float qscale;  // scale * log2(e)
-};
 
 enum { kModeFull = 0, kModePartial = 1, kModeNew = 2 };
 
@@ -133,9 +117,10 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs<T> a) {
     const int kh = blockIdx.y / a.n_tiles, tile = blockIdx.y % a.n_tiles;
     const int b = blockIdx.z;
     const int G = a.H / a.KV, R = G * a.NQ;
-    const int L = a.context_lens[b];
-    const int n_seq = L > 0 ? (L - 1) / a.chunk + 1 : 1;  // partitions this sequence uses
-    if (part >= n_seq) return;                            // whole workgroup leaves
+    // cached length, never beyond what the block table can address
+    const int L = min(a.context_lens[b], a.max_blocks * BS);
+    const int n_seq = partitions_of(L, a.chunk, a.n_parts);
+    if (part >= n_seq) return;  // whole workgroup leaves
     const int tok_begin = part * a.chunk;
     const int tok_end = min(tok_begin + a.chunk, L);
     const int row0 = tile * RT;
@@ -252,32 +237,9 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs<T> a) {
     }
     __syncthreads();
 
-    const bool single = (n_seq == 1);
-    for (int idx = threadIdx.x; idx < RT * D; idx += 256) {
-        const int r = idx / D, d = idx % D;
-        if (row0 + r >= R) continue;
-        float M = s_m[0][r];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) M = fmaxf(M, s_m[w][r]);
-        float acc = 0.f, lt = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float wt = fast_exp2(s_m[w][r] - M);
-            acc = fmaf(wt, s_o[w][r][d], acc);
-            lt = fmaf(wt, s_l[w][r], lt);
-        }
-        const int64_t grow = grow0 + r;
-        if (single) {
-            E::store(a.out + grow * D + d, lt != 0.f ? acc / lt : 0.f);
-        } else {
-            const int64_t slot = grow * a.n_parts + part;
-            a.ws_o[slot * D + d] = acc;
-            if (d == 0) {
-                a.ws_ml[slot * 2 + 0] = M;
-                a.ws_ml[slot * 2 + 1] = lt;
-            }
-        }
-    }
+    const int nrows = min(RT, R - row0);
+    const bool single = n_seq == 1;
+    emit_rows<T, D, RT>(a, s_o, s_m, s_l, nrows, grow0, part, single);
 }
 
 }  // namespace pa

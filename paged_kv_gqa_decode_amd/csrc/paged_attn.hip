@@ -12,9 +12,11 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <type_traits>
 
 #include "paged_attn.h"
 #include "combine.hpp"
+#include "decode_mfma.hpp"
 #include "decode_valu.hpp"
 
 namespace {
@@ -37,6 +39,12 @@ int succeed() {
 }
 
 constexpr int kMaxRows = 128;         // G * nq
+constexpr int kMfmaMaxRows = 64;      // the matrix-core family keeps <= 4 row tiles of 16
+// Resident waves per CU the matrix-core kernel reaches (register-bound), by
+// row tiles: the balanced split gives every resident wave one segment.
+constexpr int kMfmaWavesPerCu[5] = {0, 8, 4, 4, 4};
+// A piece's saved state may be at most 1/kStateRatio of the K/V bytes it covers.
+constexpr int kStateRatio = 8;
 constexpr int kGroupsPerCu = 8;       // workgroups per CU the heuristic aims to keep busy
 constexpr int kMinChunkTokens = 256;  // below this, partial-state traffic outweighs balance
 constexpr int kMaxChunkTokens = 2048; // above this, ragged batches leave CUs idle
@@ -91,29 +99,75 @@ int validate_problem(const pa_problem* p) {
         return fail(PA_ERR_INVALID_ARG, "num_partitions = %d is negative", p->num_partitions);
     if (p->kernel != PA_KERNEL_AUTO && p->kernel != PA_KERNEL_VALU && p->kernel != PA_KERNEL_MFMA)
         return fail(PA_ERR_INVALID_ARG, "kernel = %d is not a pa_kernel", p->kernel);
-    if (p->kernel == PA_KERNEL_MFMA)
-        return fail(PA_ERR_UNSUPPORTED, "the matrix-core kernel family is not available in this "
-                    "build; verify pa_problem.kernel");
+    if (p->kernel == PA_KERNEL_MFMA && p->dtype == PA_F32)
+        return fail(PA_ERR_UNSUPPORTED, "the matrix-core kernel family needs fp16 or bf16 I/O; "
+                    "verify pa_problem.kernel");
+    if (p->kernel == PA_KERNEL_MFMA && p->batch > pa::kMaxSplitBatch)
+        return fail(PA_ERR_UNSUPPORTED, "the matrix-core kernel family takes at most %d sequences "
+                    "per call (got %d); verify pa_problem.kernel or split the batch",
+                    pa::kMaxSplitBatch, p->batch);
+    {
+        // 16-key groups of the whole batch at the table's capacity, counted in int32
+        const int64_t cap = (int64_t)p->max_blocks_per_seq * p->block_size;
+        const int64_t subpages = (int64_t)p->batch * ((cap + 15) / 16 + (p->nq + 15) / 16);
+        if (subpages >= (1LL << 31))
+            return fail(PA_ERR_UNSUPPORTED, "batch * context is too large for one call (%lld "
+                        "16-key groups); split the batch", (long long)subpages);
+    }
+    if (p->kernel == PA_KERNEL_MFMA && rows > kMfmaMaxRows)
+        return fail(PA_ERR_UNSUPPORTED, "the matrix-core kernel family takes at most %d query "
+                    "rows per KV head (got %lld); verify pa_problem.kernel", kMfmaMaxRows,
+                    (long long)rows);
     return PA_OK;
 }
 
 struct Plan {
-    int parts;    // partitions per sequence
-    int chunk;    // cached tokens per partition (multiple of block_size)
+    // VALU family: parts = key partitions per sequence, chunk = cached tokens per
+    // partition (multiple of block_size). Matrix-core family (balanced split):
+    // parts = segments (waves) the work is cut into, chunk = 16 * min_seg.
+    int parts;
+    int chunk;
+    int min_seg;  // matrix-core family: minimum segment length in 16-key groups
     int kernel;   // pa_kernel
-    int rt;       // query rows per workgroup (VALU: power of two <= 8)
-    int n_tiles;  // row tiles per KV head
+    int rt;       // VALU: query rows per workgroup (power of two <= 8); MFMA: 16-row tiles
+    int n_tiles;  // workgroups per KV head along the rows (1 for MFMA)
 };
 
 int plan_impl(const pa_problem* p, int num_cus, Plan* pl) {
     if (int rc = validate_problem(p)) return rc;
     if (num_cus < 1) return fail(PA_ERR_INVALID_ARG, "num_cus = %d must be >= 1", num_cus);
     const int R = (p->num_heads / p->num_kv_heads) * p->nq;
-    pl->kernel = PA_KERNEL_VALU;
-    int rt = 1;
-    while (rt < R && rt < 8) rt *= 2;
-    pl->rt = rt;
-    pl->n_tiles = (R + rt - 1) / rt;
+    int kernel = p->kernel;
+    if (kernel == PA_KERNEL_AUTO)
+        kernel = (p->dtype != PA_F32 && R <= kMfmaMaxRows && p->batch <= pa::kMaxSplitBatch)
+                     ? PA_KERNEL_MFMA
+                     : PA_KERNEL_VALU;
+    pl->kernel = kernel;
+    pl->min_seg = 1;
+    if (kernel == PA_KERNEL_MFMA) {
+        pl->rt = (R + 15) / 16;
+        pl->n_tiles = 1;
+        const int64_t elem = p->dtype == PA_F32 ? 4 : 2;
+        const int64_t state = (int64_t)R * (p->head_dim + 2) * 4;
+        const int64_t kv_per_group = 16 * 2 * (int64_t)p->head_dim * elem;
+        if (p->num_partitions > (1 << 22))
+            return fail(PA_ERR_UNSUPPORTED, "num_partitions = %d is more segments than supported "
+                        "(%d)", p->num_partitions, 1 << 22);
+        if (p->num_partitions > 0) {
+            pl->parts = p->num_partitions;
+            pl->min_seg = 1;
+        } else {
+            pl->parts = num_cus * kMfmaWavesPerCu[pl->rt];
+            pl->min_seg = (int)ceil_div(kStateRatio * state, kv_per_group);
+        }
+        pl->chunk = 16 * pl->min_seg;
+        return PA_OK;
+    } else {
+        int rt = 1;
+        while (rt < R && rt < 8) rt *= 2;
+        pl->rt = rt;
+        pl->n_tiles = (R + rt - 1) / rt;
+    }
     const int BS = p->block_size;
     const int64_t ctx = p->max_context_len;
     const int64_t full = round_up(ctx > 0 ? ctx : 1, BS);  // one chunk covering everything
@@ -131,7 +185,6 @@ int plan_impl(const pa_problem* p, int num_cus, Plan* pl) {
         if (chunk > kMaxChunkTokens) chunk = kMaxChunkTokens;
     }
     if (chunk > full) chunk = full;
-    if (p->kernel == PA_KERNEL_VALU || p->kernel == PA_KERNEL_AUTO) pl->kernel = PA_KERNEL_VALU;
     int64_t parts = ctx > 0 ? ceil_div(ctx, chunk) : 1;
     if (parts > 65535 * 32767LL)
         return fail(PA_ERR_UNSUPPORTED, "too many partitions (%lld)", (long long)parts);
@@ -140,10 +193,20 @@ int plan_impl(const pa_problem* p, int num_cus, Plan* pl) {
     return PA_OK;
 }
 
+// Workspace: VALU family [rows][parts][D] + [rows][parts][2]; matrix-core
+// family [slots][R][D] + [slots][R][2] with slots = B*KV + segments.
+size_t state_floats(const pa_problem* p, const Plan& pl) {
+    if (pl.kernel == PA_KERNEL_MFMA) {
+        const size_t R = (size_t)(p->num_heads / p->num_kv_heads) * p->nq;
+        const size_t slots = (size_t)p->batch * p->num_kv_heads + (size_t)pl.parts;
+        return slots * R;
+    }
+    return (size_t)p->batch * p->num_heads * p->nq * (size_t)pl.parts;
+}
+
 size_t workspace_bytes_for(const pa_problem* p, const Plan& pl) {
     if (pl.parts <= 1) return 0;
-    const size_t rows = (size_t)p->batch * p->num_heads * p->nq;
-    return rows * (size_t)pl.parts * (size_t)(p->head_dim + 2) * sizeof(float);
+    return state_floats(p, pl) * (size_t)(p->head_dim + 2) * sizeof(float);
 }
 
 // Per-device property cache (compute units, gfx950 or not), filled once.
@@ -216,8 +279,66 @@ void launch_valu(const Plan& pl, dim3 grid, hipStream_t s, const pa::DecodeArgs<
     }
 }
 
+template <typename T, int D, int BS>
+void launch_mfma(const Plan& pl, dim3 grid, hipStream_t s, const pa::SplitArgs<T>& a) {
+    switch (pl.rt) {
+        case 1: hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 1>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 2>), grid, dim3(256), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 3>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 4>), grid, dim3(256), 0, s, a); break;
+    }
+}
+
+pa::SplitGeometry split_geometry(const pa_problem* p, const Plan& pl) {
+    pa::SplitGeometry g;
+    g.B = p->batch;
+    g.KV = p->num_kv_heads;
+    g.NQ = p->nq;
+    g.max_tokens = p->max_blocks_per_seq * p->block_size;
+    g.n_seg = pl.parts;
+    g.min_seg = pl.min_seg;
+    return g;
+}
+
+template <typename T>
+void launch_pass1_mfma(const pa_problem* p, const Plan& pl, hipStream_t s,
+                       const pa::DecodeArgs<T>& d) {
+    pa::SplitArgs<T> a;
+    a.q = d.q;
+    a.k_pool = d.k_pool;
+    a.v_pool = d.v_pool;
+    a.block_table = d.block_table;
+    a.context_lens = d.context_lens;
+    a.new_k = d.new_k;
+    a.new_v = d.new_v;
+    a.out = d.out;
+    const size_t sf = state_floats(p, pl);
+    a.ws_o = d.ws_o;
+    a.ws_ml = d.ws_o ? d.ws_o + sf * p->head_dim : nullptr;
+    a.g = split_geometry(p, pl);
+    a.H = p->num_heads;
+    a.causal = p->causal;
+    a.max_blocks = p->max_blocks_per_seq;
+    a.R = (p->num_heads / p->num_kv_heads) * p->nq;
+    a.qscale = d.qscale;
+    const dim3 grid((unsigned)ceil_div(pl.parts, 4));
+    if (p->head_dim == 64) {
+        if (p->block_size == 16) launch_mfma<T, 64, 16>(pl, grid, s, a);
+        else launch_mfma<T, 64, 32>(pl, grid, s, a);
+    } else {
+        if (p->block_size == 16) launch_mfma<T, 128, 16>(pl, grid, s, a);
+        else launch_mfma<T, 128, 32>(pl, grid, s, a);
+    }
+}
+
 template <typename T>
 void launch_pass1(const pa_problem* p, const Plan& pl, hipStream_t s, const pa::DecodeArgs<T>& a) {
+    if constexpr (!std::is_same<T, float>::value) {
+        if (pl.kernel == PA_KERNEL_MFMA) {
+            launch_pass1_mfma<T>(p, pl, s, a);
+            return;
+        }
+    }
     const dim3 grid(pl.parts, p->num_kv_heads * pl.n_tiles, p->batch);
     if (p->head_dim == 64) {
         if (p->block_size == 16) launch_valu<T, 64, 16>(pl, grid, s, a);
@@ -231,8 +352,26 @@ void launch_pass1(const pa_problem* p, const Plan& pl, hipStream_t s, const pa::
 template <typename T>
 void launch_combine(const pa_problem* p, const Plan& pl, hipStream_t s, const float* ws,
                     const int32_t* lens, void* out) {
-    pa::CombineArgs<T> c;
     const int64_t rows = (int64_t)p->batch * p->num_heads * p->nq;
+    if (pl.kernel == PA_KERNEL_MFMA) {
+        pa::SplitCombineArgs<T> c;
+        const size_t sf = state_floats(p, pl);
+        c.ws_o = ws;
+        c.ws_ml = ws + sf * p->head_dim;
+        c.context_lens = lens;
+        c.out = static_cast<T*>(out);
+        c.g = split_geometry(p, pl);
+        c.H = p->num_heads;
+        c.R = (p->num_heads / p->num_kv_heads) * p->nq;
+        const int64_t want = ceil_div(rows, 4);
+        const dim3 grid((unsigned)(want < 2048 ? want : 2048));
+        if (p->head_dim == 64)
+            hipLaunchKernelGGL((pa::combine_split<T, 64>), grid, dim3(256), 0, s, c);
+        else
+            hipLaunchKernelGGL((pa::combine_split<T, 128>), grid, dim3(256), 0, s, c);
+        return;
+    }
+    pa::CombineArgs<T> c;
     c.ws_o = ws;
     c.ws_ml = ws + rows * pl.parts * p->head_dim;
     c.context_lens = lens;
@@ -241,6 +380,7 @@ void launch_combine(const pa_problem* p, const Plan& pl, hipStream_t s, const fl
     c.rows_per_seq = p->num_heads * p->nq;
     c.n_parts = pl.parts;
     c.chunk = pl.chunk;
+    c.max_tokens = p->max_blocks_per_seq * p->block_size;
     const dim3 grid((unsigned)ceil_div(rows, 4));
     if (p->head_dim == 64)
         hipLaunchKernelGGL((pa::combine_partitions<T, 64>), grid, dim3(256), 0, s, c);

@@ -78,3 +78,23 @@ def logical_rows(w: W.Workload, b: int, kh: int, r: int):
         ks.append([float(x) for x in nk[b, kh, j]])
         vs.append([float(x) for x in nv[b, kh, j]])
     return ks, vs
+
+
+def split_single_piece_units(context_lens, KV, NQ, n_seg, min_seg, max_tokens):
+    """Units (b, kh) that the balanced per-wave split leaves in one segment.
+
+    Integer model of the split: unit u = b*KV + kh spans ceil(L_b/16) +
+    ceil(NQ/16) groups of 16 keys along one axis; segments are
+    sigma = max(min_seg, ceil(W / n_seg)) groups long."""
+    nnew = (NQ + 15) // 16
+    nsub = [(min(max(int(L), 0), max_tokens) + 15) // 16 + nnew for L in context_lens]
+    W = KV * sum(nsub)
+    sigma = max(min_seg, -(-W // n_seg))
+    out, start = set(), 0
+    for b, n in enumerate(nsub):
+        for kh in range(KV):
+            s0, s1 = start // sigma, (start + n - 1) // sigma
+            if s0 == s1:
+                out.add((b, kh))
+            start += n
+    return out

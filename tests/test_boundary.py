@@ -43,37 +43,50 @@ def spec_problem(spec: W.Spec, max_ctx: int, **kw) -> pa.PaProblem:
     return pa.PaProblem(**d)
 
 
-# (config index, max_context_len) -> (partitions, chunk_tokens) on a 256-CU device
+# (config index, max_context_len) -> (kernel, partitions, chunk_tokens) on a 256-CU
+# device. VALU family: key partitions per sequence and cached tokens per
+# partition. Matrix-core family (balanced split): segments (one per resident
+# wave: 2 per SIMD) and the minimum segment length in tokens (a piece's saved
+# state is at most 1/8 of the K/V bytes it covers).
 PLAN_TABLE = [
-    (0, 100, 1, 112),
-    (1, 4096, 8, 512),
-    (2, 131072, 64, 2048),
-    (4, 16384, 8, 2048),
-    (4, 1000, 1, 1024),
+    (0, 100, pa.PA_KERNEL_VALU, 1, 112),
+    (1, 4096, pa.PA_KERNEL_MFMA, 2048, 48),
+    (2, 131072, pa.PA_KERNEL_MFMA, 2048, 48),
+    (3, 8192, pa.PA_KERNEL_MFMA, 1024, 16 * 33),
+    (4, 16384, pa.PA_KERNEL_MFMA, 2048, 80),
 ]
 
 
-@pytest.mark.parametrize("cfg,ctx,parts,chunk", PLAN_TABLE)
-def test_plan_table(lib, cfg, ctx, parts, chunk):
+@pytest.mark.parametrize("cfg,ctx,kernel,parts,chunk", PLAN_TABLE)
+def test_plan_table(lib, cfg, ctx, kernel, parts, chunk):
     rc, p, c, k = pa.pa_plan_ex(spec_problem(W.CONFIGS[cfg], ctx), 256)
-    assert (p, c) == (parts, chunk)
-    assert c % W.CONFIGS[cfg].BS == 0 and p * c >= ctx
-    assert k in (pa.PA_KERNEL_VALU, pa.PA_KERNEL_MFMA)
+    assert (k, p, c) == (kernel, parts, chunk)
 
 
 @pytest.mark.parametrize("forced", [1, 2, 3, 7, 64])
 def test_forced_partitions_cover_the_context(lib, forced):
-    prob = spec_problem(W.CONFIGS[1], 4000, num_partitions=forced)
-    _, p, c, _ = pa.pa_plan_ex(prob, 256)
+    # VALU family: chunks of the cached keys, page aligned
+    prob = spec_problem(W.CONFIGS[1], 4000, num_partitions=forced, kernel=pa.PA_KERNEL_VALU)
+    _, p, c, k = pa.pa_plan_ex(prob, 256)
+    assert k == pa.PA_KERNEL_VALU
     assert 1 <= p <= forced and p * c >= 4000 and (p - 1) * c < 4000 and c % 16 == 0
+    # matrix-core family: exactly that many segments
+    _, p, c, k = pa.pa_plan_ex(spec_problem(W.CONFIGS[1], 4000, num_partitions=forced), 256)
+    assert (k, p, c) == (pa.PA_KERNEL_MFMA, forced, 16)
 
 
 def test_workspace_size(lib):
     prob = spec_problem(W.CONFIGS[1], 4096)
     _, nbytes = pa.pa_workspace_size_ex(prob, 256)
+    # slots = B*KV + segments, each R = 4 rows of D + 2 floats
+    assert nbytes == (32 * 8 + 2048) * 4 * (128 + 2) * 4
+    prob = spec_problem(W.CONFIGS[1], 4096, kernel=pa.PA_KERNEL_VALU)
+    _, nbytes = pa.pa_workspace_size_ex(prob, 256)
     _, p, _, _ = pa.pa_plan_ex(prob, 256)
     assert nbytes == 32 * 32 * 1 * p * (128 + 2) * 4
     _, single = pa.pa_workspace_size_ex(spec_problem(W.CONFIGS[0], 100), 256)
+    assert single == 0
+    _, single = pa.pa_workspace_size_ex(spec_problem(W.CONFIGS[1], 4096, num_partitions=1), 256)
     assert single == 0
 
 
@@ -92,6 +105,9 @@ BAD = [
     (dict(num_partitions=-2), pa.PA_ERR_INVALID_ARG),
     (dict(kernel=9), pa.PA_ERR_INVALID_ARG),
     (dict(nq=64, num_heads=32), pa.PA_ERR_UNSUPPORTED),  # G*nq = 256 rows > 128
+    (dict(nq=17, kernel=2), pa.PA_ERR_UNSUPPORTED),       # G*nq = 68 rows > 64 (matrix cores)
+    (dict(dtype=0, kernel=2), pa.PA_ERR_UNSUPPORTED),     # matrix cores need 16-bit I/O
+    (dict(batch=9000, kernel=2), pa.PA_ERR_UNSUPPORTED),  # balanced split takes <= 8192 sequences
 ]
 
 

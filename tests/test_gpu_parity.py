@@ -191,19 +191,34 @@ def test_causality_is_bit_exact():
         assert torch.equal(out[:, :, :j], base[:, :, :j])
 
 
-def test_combine_remerges_the_workspace():
+@pytest.mark.parametrize("kernel", [pa.PA_KERNEL_MFMA, pa.PA_KERNEL_VALU])
+def test_combine_remerges_the_workspace(kernel):
     w = to_device(W.make_workload(SMALL[0], device="cpu"))
     table = torch.from_numpy(w.block_table).to(DEV)
     lens = torch.from_numpy(w.context_lens).to(DEV)
-    dec = pa.Decoder(w.q, w.k_pool, table, max_context_len=w.max_context_len, num_partitions=4)
-    assert dec.partitions > 1
+    parts = 5
+    dec = pa.Decoder(w.q, w.k_pool, table, max_context_len=w.max_context_len,
+                     num_partitions=parts, kernel=kernel)
+    assert dec.partitions > 1 and dec.kernel == kernel
     out = dec(w.q, w.k_pool, w.v_pool, table, lens, w.new_k, w.new_v, w.scale).clone()
     torch.cuda.synchronize()
-    # rows of multi-partition sequences are rebuilt from the workspace alone
+    check(w, out)
+    # rows that went through the workspace are rebuilt from it alone
+    s = w.spec
+    G = s.H // s.KV
+    merged = torch.zeros(s.B, s.H, dtype=torch.bool)
+    if kernel == pa.PA_KERNEL_MFMA:
+        whole = P.split_single_piece_units(w.context_lens, s.KV, s.NQ, dec.partitions,
+                                           dec.chunk_tokens // 16, s.max_blocks * s.BS)
+        for b in range(s.B):
+            for h in range(s.H):
+                merged[b, h] = (b, h // G) not in whole
+    else:
+        for b in range(s.B):
+            merged[b, :] = int(w.context_lens[b]) > dec.chunk_tokens
+    assert merged.any() and not merged.all()
     again = out.clone()
-    multi = [b for b in range(w.spec.B) if int(w.context_lens[b]) > dec.chunk_tokens]
-    assert multi
-    again[multi] = 0
+    again[merged.to(DEV)] = 0
     pa.paged_attn_combine(dec.problem, lens, dec.workspace, dec.workspace_bytes, again,
                           stream=torch.cuda.current_stream())
     torch.cuda.synchronize()
@@ -216,6 +231,7 @@ def test_workspace_too_small_is_rejected():
     lens = torch.from_numpy(w.context_lens).to(DEV)
     prob = pa.make_problem(w.q, w.k_pool, table, max_context_len=w.max_context_len,
                            num_partitions=4)
+    assert pa.pa_plan(prob)[1] == 4
     _, need = pa.pa_workspace_size(prob)
     assert need > 0
     ws = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
