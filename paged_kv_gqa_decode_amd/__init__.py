@@ -48,6 +48,12 @@ def library(path: Optional[str] = None):
     if _lib is not None and path is None:
         return _lib
     p = path or LIB_PATH
+    # torch ships its own libamdhip64.so.7; whichever copy is loaded first serves
+    # the whole process, so let torch load it before this library binds to it.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is not built: run `python -m paged_kv_gqa_decode_amd.build` "
                            "(or __graft_entry__.build()) first")

@@ -21,8 +21,13 @@
 // when a score exceeds it by more than 2^kSlack (probabilities stay <= 256),
 // so the accumulators are rescaled almost never.
 // Block-table entries of a piece are read 64 pages at a time into one VGPR
-// (lane i = page i) and taken with readlane; the next two sub-pages' K/V are
-// in flight in registers while the current one is computed.
+// (lane i = page i) and taken with readlane. K/V sub-pages are staged through
+// LDS: each wave owns one sub-page slot; buffer loads write it directly
+// (no VGPRs held by loads in flight), the wave copies it to registers in the
+// MFMA operand layout and immediately issues the next sub-page into the slot,
+// so one sub-page per wave is always in flight while the previous is computed.
+// Small register footprint -> 4 waves per SIMD; many waves, each with one
+// sub-page in flight, is what keeps HBM busy on this part.
 #pragma once
 
 #include "split.hpp"
@@ -80,6 +85,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int b
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
 }
 
+// s_waitcnt immediates (GFX9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8]
+// | vmcnt[5:4] << 14): wait for all vector-memory operations, or for all LDS ops.
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;
+
 // Slack of the lazy reference max, in log2 units (probabilities stay <= 256).
 constexpr float kSlack = 8.0f;
 
@@ -95,6 +105,7 @@ struct SplitArgs {
     T* out;
     float* ws_o;   // [slots][R][D]  unnormalised partial outputs
     float* ws_ml;  // [slots][R][2]  (max, sum) in base-2 units
+    int32_t* meta; // [B*KV][2]      first and last segment overlapping each unit
     SplitGeometry g;
     int H, causal, max_blocks, R;
     float qscale;  // scale * log2(e)
@@ -106,9 +117,17 @@ struct SubPage {
     unsigned v[NP][4];  // keys 4*g16 + j, d = 32*np + 2*c16 .. +1
 };
 
-// Two waves per SIMD: enough registers for three sub-pages in flight per wave.
+// LDS layout of one sub-page slot (16 keys): K operands first, one 16-byte
+// chunk per lane per score step (kk*1024 + lane*16); then V, one 16-byte chunk
+// per lane per output tile pair holding the dwords of keys 4*g16 + 0..3.
+template <typename T, int D>
+struct SlotLayout {
+    static constexpr int kKBytes = 16 * D * (int)sizeof(T);
+    static constexpr int kBytes = 2 * kKBytes;
+};
+
 template <typename T, int D, int BS, int NRT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NRT == 1 ? 2 : 1, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NRT == 1 ? 4 : 1, 4)))
 void decode_mfma(SplitArgs<T> a) {
     using M = Mfma<T>;
     constexpr int KS = D / 32;    // score MFMA steps over d
@@ -117,12 +136,18 @@ void decode_mfma(SplitArgs<T> a) {
     constexpr int SUB = BS / 16;  // 16-key sub-pages per page
     static_assert(D % 32 == 0 && BS % 16 == 0, "shape");
 
-    __shared__ int s_pref[kMaxSplitBatch + 1];
+    using Slot = SlotLayout<T, D>;
+    extern __shared__ __attribute__((aligned(16))) char smem[];  // 4 slots, then the prefix
+    int* s_pref = reinterpret_cast<int*>(smem + 4 * Slot::kBytes);
     build_prefix(a.context_lens, a.g, s_pref);
     const int64_t W = split_total(a.g, s_pref);
     const int64_t sigma = split_sigma(a.g, W);
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // The wave index is uniform within a wave; saying so keeps every per-piece
+    // quantity (sequence, head, page, descriptors, LDS slot) in scalar registers.
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    char* slot_lds = smem + wave * Slot::kBytes;
     const int c16 = lane & 15, g16 = lane >> 4;
     const int gw = blockIdx.x * 4 + wave;  // this wave's segment
     int64_t x = (int64_t)gw * sigma;
@@ -145,6 +170,11 @@ void decode_mfma(SplitArgs<T> a) {
         const int L = min(max(a.context_lens[b], 0), a.g.max_tokens);
         const int nc = nsub - nnew;  // cached sub-pages = ceil(L / 16)
         const int64_t grow0 = ((int64_t)b * a.H + (int64_t)kh * G) * NQ;
+        if (j0 == 0 && lane == 0 && a.meta) {  // the unit's first piece records its segments
+            int32_t* mt = a.meta + 2 * ((int64_t)b * KV + kh);
+            mt[0] = (int32_t)(ustart / sigma);
+            mt[1] = (int32_t)((ustart + nsub - 1) / sigma);
+        }
 
         // Q operand (B of S^T = K Q^T): row 16*rt + c16, d = 32*kk + 8*g16 .. +8
         u32x4_t qop[NRT][KS];
@@ -169,13 +199,16 @@ void decode_mfma(SplitArgs<T> a) {
 
         // Attend one 16-key sub-page: keys [0, valid) exist. For new rows
         // (is_new) key tau is new row t0 + tau, visible to query rows by causality.
-        auto attend = [&](const SubPage<KS, NP>& sp, int valid, bool is_new, int t0) {
+        // kop(kk): K operand of score step kk; vquad(np): this lane's dwords of
+        // keys 4*g16 + 0..3 at d = 32*np + 2*c16. Both read just before use.
+        auto attend = [&](auto&& kop, auto&& vquad, int valid, bool is_new, int t0) {
             // V operands of output tiles 2*np and 2*np+1, built right before use
             auto vops = [&](int np, u32x2_t& lo, u32x2_t& hi) {
+                const u32x4_t q4 = vquad(np);
                 unsigned v[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    v[j] = (4 * g16 + j < valid) ? sp.v[np][j] : 0u;  // unused slots may be NaN
+                    v[j] = (4 * g16 + j < valid) ? q4[j] : 0u;  // unused slots may be NaN
                 lo = u32x2_t{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u),
                              __builtin_amdgcn_perm(v[3], v[2], 0x05040100u)};
                 hi = u32x2_t{__builtin_amdgcn_perm(v[1], v[0], 0x07060302u),
@@ -185,7 +218,7 @@ void decode_mfma(SplitArgs<T> a) {
             for (int rt = 0; rt < NRT; ++rt) {
                 f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < KS; ++kk) s = M::qk(sp.k[kk], qop[rt][kk], s);
+                for (int kk = 0; kk < KS; ++kk) s = M::qk(kop(kk), qop[rt][kk], s);
                 float sv[4];
                 const int row = 16 * rt + c16;
 #pragma unroll
@@ -255,14 +288,18 @@ void decode_mfma(SplitArgs<T> a) {
             const int32_t* trow = a.block_table + (int64_t)b * a.max_blocks;
             const int npages = (L + BS - 1) / BS;
             int pbase = -1000000, phys_lane = 0;  // lane i: block of page pbase + i
-            // One buffer descriptor per sub-page (wave-uniform, scalar registers);
-            // each lane adds a fixed 32-bit byte offset: key c16 for K, keys
-            // 4*g16 + jj for V (the jj step goes in the scalar offset).
+            // One buffer descriptor per sub-page (wave-uniform, scalar registers).
+            // K: lane l fetches key c16, d = 32*kk + 8*g16 (16 bytes) into
+            // kk*1024 + l*16. V: for output tile pair np and key quad i, lane l
+            // fetches the dword of key 4*i + (l&3) at d = 32*np + 2*(l>>2) into
+            // K_bytes + np*1024 + i*256 + l*4, which puts lane L's dwords of keys
+            // 4*(L/16)+0..3 at K_bytes + np*1024 + L*16.
             const uint32_t koff = (uint32_t)((c16 * tstride + 8 * g16) * sizeof(T));
-            const uint32_t voff = (uint32_t)((4 * g16 * tstride + 2 * c16) * sizeof(T));
-            const uint32_t vstep = (uint32_t)(tstride * sizeof(T));
+            const uint32_t voff = (uint32_t)(((lane & 3) * tstride + 2 * (lane >> 2)) * sizeof(T));
+            const uint32_t quad = (uint32_t)(4 * tstride * sizeof(T));
             const int span = (int)(16 * tstride * sizeof(T));  // bytes a sub-page spans
-            auto load_unit = [&](int j, SubPage<KS, NP>& sp) -> int {
+            typedef __attribute__((address_space(3))) void lds_void;
+            auto issue = [&](int j) {
                 const int page = j / SUB, sub = j % SUB;
                 if (page >= pbase + 64) {
                     pbase = page;
@@ -274,29 +311,29 @@ void decode_mfma(SplitArgs<T> a) {
                 const __amdgpu_buffer_rsrc_t vr = make_rsrc(vpool + row0 * tstride, span);
 #pragma unroll
                 for (int kk = 0; kk < KS; ++kk)
-                    sp.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * kk, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        kr, (lds_void*)(slot_lds + kk * 1024), 16, koff, 64 * kk, 0, 0);
 #pragma unroll
                 for (int np = 0; np < NP; ++np)
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        sp.v[np][jj] =
-                            __builtin_amdgcn_raw_buffer_load_b32(vr, voff + 64 * np, jj * vstep, 0);
-                return min(16, L - 16 * j);
+                    for (int i = 0; i < 4; ++i)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            vr, (lds_void*)(slot_lds + Slot::kKBytes + np * 1024 + i * 256), 4,
+                            voff, i * quad + 64 * np, 0, 0);
             };
-            // three register buffers: sub-pages j+1 and j+2 in flight while j is computed
-            const int n = jc - j0;
-            SubPage<KS, NP> b0, b1, b2;
-            int v0 = load_unit(j0, b0), v1 = 0, v2 = 0;
-            if (1 < n) v1 = load_unit(j0 + 1, b1);
-            for (int u = 0; u < n; u += 3) {
-                if (u + 2 < n) v2 = load_unit(j0 + u + 2, b2);
-                attend(b0, v0, false, 0);
-                if (u + 1 >= n) break;
-                if (u + 3 < n) v0 = load_unit(j0 + u + 3, b0);
-                attend(b1, v1, false, 0);
-                if (u + 2 >= n) break;
-                if (u + 4 < n) v1 = load_unit(j0 + u + 4, b1);
-                attend(b2, v2, false, 0);
+            auto kop_lds = [&](int kk) {
+                return *reinterpret_cast<const u32x4_t*>(slot_lds + kk * 1024 + lane * 16);
+            };
+            auto vquad_lds = [&](int np) {
+                return *reinterpret_cast<const u32x4_t*>(slot_lds + Slot::kKBytes + np * 1024 +
+                                                         lane * 16);
+            };
+            issue(j0);
+            for (int j = j0; j < jc; ++j) {
+                __builtin_amdgcn_s_waitcnt(kWaitVm0);    // sub-page j has landed in the slot
+                attend(kop_lds, vquad_lds, min(16, L - 16 * j), false, 0);
+                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // slot read out: free for j + 1
+                if (j + 1 < jc) issue(j + 1);
             }
         }
 
@@ -320,7 +357,11 @@ void decode_mfma(SplitArgs<T> a) {
                                                  a.new_v + (nbase + tv) * D + 32 * np + 2 * c16)
                                            : 0u;
                 }
-            attend(sp, min(16, NQ - t0), true, t0);
+            attend([&](int kk) { return sp.k[kk]; },
+                   [&](int np) {
+                       return u32x4_t{sp.v[np][0], sp.v[np][1], sp.v[np][2], sp.v[np][3]};
+                   },
+                   min(16, NQ - t0), true, t0);
         }
 
         // ---- emit: the finished output, or this piece's state for the combine ----

@@ -40,9 +40,11 @@ int succeed() {
 
 constexpr int kMaxRows = 128;         // G * nq
 constexpr int kMfmaMaxRows = 64;      // the matrix-core family keeps <= 4 row tiles of 16
-// Resident waves per CU the matrix-core kernel reaches (register-bound), by
-// row tiles: the balanced split gives every resident wave one segment.
-constexpr int kMfmaWavesPerCu[5] = {0, 8, 4, 4, 4};
+// Resident waves per CU the matrix-core kernel reaches on register use, by row
+// tiles (its occupancy attribute): the balanced split gives every resident wave
+// one segment. LDS can lower it further (mfma_waves_per_cu).
+constexpr int kMfmaWavesPerCu[5] = {0, 16, 4, 4, 4};
+constexpr int kLdsPerCu = 160 * 1024;
 // A piece's saved state may be at most 1/kStateRatio of the K/V bytes it covers.
 constexpr int kStateRatio = 8;
 constexpr int kGroupsPerCu = 8;       // workgroups per CU the heuristic aims to keep busy
@@ -133,6 +135,20 @@ struct Plan {
     int n_tiles;  // workgroups per KV head along the rows (1 for MFMA)
 };
 
+// Dynamic LDS of the matrix-core kernel: 4 sub-page slots (16 keys of K and V)
+// plus the per-sequence prefix of the split.
+size_t mfma_lds_bytes(const pa_problem* p) {
+    const size_t elem = p->dtype == PA_F32 ? 4 : 2;
+    const size_t slots = 4 * (2 * 16 * (size_t)p->head_dim * elem);
+    return slots + ((size_t)p->batch + 1) * sizeof(int);
+}
+
+int mfma_waves_per_cu(const pa_problem* p, int row_tiles) {
+    const int by_lds = (int)(kLdsPerCu / mfma_lds_bytes(p)) * 4;
+    const int by_regs = kMfmaWavesPerCu[row_tiles];
+    return by_lds < by_regs ? by_lds : by_regs;
+}
+
 int plan_impl(const pa_problem* p, int num_cus, Plan* pl) {
     if (int rc = validate_problem(p)) return rc;
     if (num_cus < 1) return fail(PA_ERR_INVALID_ARG, "num_cus = %d must be >= 1", num_cus);
@@ -157,7 +173,7 @@ int plan_impl(const pa_problem* p, int num_cus, Plan* pl) {
             pl->parts = p->num_partitions;
             pl->min_seg = 1;
         } else {
-            pl->parts = num_cus * kMfmaWavesPerCu[pl->rt];
+            pl->parts = num_cus * mfma_waves_per_cu(p, pl->rt);
             pl->min_seg = (int)ceil_div(kStateRatio * state, kv_per_group);
         }
         pl->chunk = 16 * pl->min_seg;
@@ -204,9 +220,17 @@ size_t state_floats(const pa_problem* p, const Plan& pl) {
     return (size_t)p->batch * p->num_heads * p->nq * (size_t)pl.parts;
 }
 
+// Matrix-core family: after the states, two int32 per (sequence, KV head): the
+// first and last segment that overlap the unit (written by pass 1).
+size_t meta_offset(const pa_problem* p, const Plan& pl) {
+    return state_floats(p, pl) * (size_t)(p->head_dim + 2) * sizeof(float);
+}
+
 size_t workspace_bytes_for(const pa_problem* p, const Plan& pl) {
     if (pl.parts <= 1) return 0;
-    return state_floats(p, pl) * (size_t)(p->head_dim + 2) * sizeof(float);
+    size_t bytes = meta_offset(p, pl);
+    if (pl.kernel == PA_KERNEL_MFMA) bytes += (size_t)p->batch * p->num_kv_heads * 2 * sizeof(int32_t);
+    return bytes;
 }
 
 // Per-device property cache (compute units, gfx950 or not), filled once.
@@ -280,12 +304,12 @@ void launch_valu(const Plan& pl, dim3 grid, hipStream_t s, const pa::DecodeArgs<
 }
 
 template <typename T, int D, int BS>
-void launch_mfma(const Plan& pl, dim3 grid, hipStream_t s, const pa::SplitArgs<T>& a) {
+void launch_mfma(const Plan& pl, dim3 grid, size_t lds, hipStream_t s, const pa::SplitArgs<T>& a) {
     switch (pl.rt) {
-        case 1: hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 1>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 2>), grid, dim3(256), 0, s, a); break;
-        case 3: hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 3>), grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 4>), grid, dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 1>), grid, dim3(256), lds, s, a); break;
+        case 2: hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 2>), grid, dim3(256), lds, s, a); break;
+        case 3: hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 3>), grid, dim3(256), lds, s, a); break;
+        default: hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 4>), grid, dim3(256), lds, s, a); break;
     }
 }
 
@@ -315,6 +339,9 @@ void launch_pass1_mfma(const pa_problem* p, const Plan& pl, hipStream_t s,
     const size_t sf = state_floats(p, pl);
     a.ws_o = d.ws_o;
     a.ws_ml = d.ws_o ? d.ws_o + sf * p->head_dim : nullptr;
+    a.meta = d.ws_o ? reinterpret_cast<int32_t*>(reinterpret_cast<char*>(d.ws_o) +
+                                                 meta_offset(p, pl))
+                    : nullptr;
     a.g = split_geometry(p, pl);
     a.H = p->num_heads;
     a.causal = p->causal;
@@ -322,12 +349,13 @@ void launch_pass1_mfma(const pa_problem* p, const Plan& pl, hipStream_t s,
     a.R = (p->num_heads / p->num_kv_heads) * p->nq;
     a.qscale = d.qscale;
     const dim3 grid((unsigned)ceil_div(pl.parts, 4));
+    const size_t lds = mfma_lds_bytes(p);
     if (p->head_dim == 64) {
-        if (p->block_size == 16) launch_mfma<T, 64, 16>(pl, grid, s, a);
-        else launch_mfma<T, 64, 32>(pl, grid, s, a);
+        if (p->block_size == 16) launch_mfma<T, 64, 16>(pl, grid, lds, s, a);
+        else launch_mfma<T, 64, 32>(pl, grid, lds, s, a);
     } else {
-        if (p->block_size == 16) launch_mfma<T, 128, 16>(pl, grid, s, a);
-        else launch_mfma<T, 128, 32>(pl, grid, s, a);
+        if (p->block_size == 16) launch_mfma<T, 128, 16>(pl, grid, lds, s, a);
+        else launch_mfma<T, 128, 32>(pl, grid, lds, s, a);
     }
 }
 
@@ -358,17 +386,29 @@ void launch_combine(const pa_problem* p, const Plan& pl, hipStream_t s, const fl
         const size_t sf = state_floats(p, pl);
         c.ws_o = ws;
         c.ws_ml = ws + sf * p->head_dim;
-        c.context_lens = lens;
+        c.meta = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(ws) +
+                                                  meta_offset(p, pl));
         c.out = static_cast<T*>(out);
-        c.g = split_geometry(p, pl);
+        c.KV = p->num_kv_heads;
         c.H = p->num_heads;
+        c.NQ = p->nq;
         c.R = (p->num_heads / p->num_kv_heads) * p->nq;
-        const int64_t want = ceil_div(rows, 4);
-        const dim3 grid((unsigned)(want < 2048 ? want : 2048));
-        if (p->head_dim == 64)
-            hipLaunchKernelGGL((pa::combine_split<T, 64>), grid, dim3(256), 0, s, c);
-        else
-            hipLaunchKernelGGL((pa::combine_split<T, 128>), grid, dim3(256), 0, s, c);
+        // pieces per unit is data dependent; segments / units + 1 estimates it
+        const int64_t units = (int64_t)p->batch * p->num_kv_heads;
+        const int64_t pieces = pl.parts / units + 1;
+        if (pieces >= 32) {
+            const dim3 grid((unsigned)(units * c.R));
+            if (p->head_dim == 64)
+                hipLaunchKernelGGL((pa::combine_split<T, 64, 1>), grid, dim3(256), 0, s, c);
+            else
+                hipLaunchKernelGGL((pa::combine_split<T, 128, 1>), grid, dim3(256), 0, s, c);
+        } else {
+            const dim3 grid((unsigned)(units * ((c.R + 3) / 4)));
+            if (p->head_dim == 64)
+                hipLaunchKernelGGL((pa::combine_split<T, 64, 4>), grid, dim3(256), 0, s, c);
+            else
+                hipLaunchKernelGGL((pa::combine_split<T, 128, 4>), grid, dim3(256), 0, s, c);
+        }
         return;
     }
     pa::CombineArgs<T> c;
