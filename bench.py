@@ -145,6 +145,9 @@ def main():
     ap.add_argument("--partitions", type=int, default=0, help="0 = launch heuristic")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run device-to-device copies of a known size (for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters of a profiler run)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -154,6 +157,17 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        nbytes, reps = 256 << 20, 10
+        a = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(reps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": nbytes,
+                          "bytes_written_per_copy": nbytes, "copies": reps}), flush=True)
+        return
 
     import paged_kv_gqa_decode_amd as pa
     from paged_kv_gqa_decode_amd import workloads as W
@@ -167,40 +181,53 @@ def main():
     lens = torch.from_numpy(w.context_lens).to(dev)
     kpools = [w.k_pool] + [w.k_pool.clone() for _ in range(args.replicas - 1)]
     vpools = [w.v_pool] + [w.v_pool.clone() for _ in range(args.replicas - 1)]
+    # The combine is enqueued by the bench itself (PA_FLAG_DEFER_COMBINE) so that
+    # HIP events can bracket pass 1 and the combine separately; the step is the same.
     dec = pa.Decoder(w.q, w.k_pool, table, max_context_len=w.max_context_len, causal=spec.causal,
-                     num_partitions=args.partitions, kernel=args.kernel)
+                     num_partitions=args.partitions, kernel=args.kernel,
+                     flags=pa.PA_FLAG_DEFER_COMBINE)
     stream = torch.cuda.current_stream()
     kvb = W.kv_bytes(w)
+    two = dec.partitions > 1
     log(f"[bench] kv bytes/step {kvb}, partitions {dec.partitions}, chunk {dec.chunk_tokens}, "
         f"kernel {KERNEL_NAMES.get(dec.kernel, dec.kernel)}, workspace {dec.workspace_bytes} B")
 
-    def step(i):
+    def step(i, ev=None):
         r = i % len(kpools)
+        if ev is not None:
+            ev[0].record(stream)
         dec(w.q, kpools[r], vpools[r], table, lens, w.new_k, w.new_v, w.scale, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        if two:
+            pa.paged_attn_combine(dec.problem, lens, dec.workspace, dec.workspace_bytes, dec.out,
+                                  stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     K = args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        starts[i].record(stream)
-        step(i)
-        ends[i].record(stream)
+        step(i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    region_ms = starts[0].elapsed_time(ends[-1])
-    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    region_ms = evs[0][0].elapsed_time(evs[-1][2])
+    pass1_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    comb_ms = [e[1].elapsed_time(e[2]) for e in evs]
     ms_per_step = region_ms / K
-    mean_launch_ms = sum(per_launch_ms) / K
+    mean_pass1 = sum(pass1_ms) / K
+    mean_comb = sum(comb_ms) / K
     value = kvb / (ms_per_step / 1e3) / 1e9
-    achieved = kvb / (mean_launch_ms / 1e3) / 1e9
-    log(f"[bench] {ms_per_step * 1e3:.2f} us/step (region), mean launch {mean_launch_ms * 1e3:.2f} us, "
-        f"p10 {sorted(per_launch_ms)[K // 10] * 1e3:.2f} p90 {sorted(per_launch_ms)[(9 * K) // 10] * 1e3:.2f} us, "
-        f"wall {wall / K * 1e6:.2f} us/step, {value:.1f} GB/s")
+    achieved = kvb / (mean_pass1 / 1e3) / 1e9
+    srt = sorted(pass1_ms)
+    log(f"[bench] {ms_per_step * 1e3:.2f} us/step (region), pass 1 {mean_pass1 * 1e3:.2f} us "
+        f"(p10 {srt[K // 10] * 1e3:.2f} p90 {srt[(9 * K) // 10] * 1e3:.2f}), combine "
+        f"{mean_comb * 1e3:.2f} us, wall {wall / K * 1e6:.2f} us/step, {value:.1f} GB/s")
 
     copy_gbps = copy_bandwidth(torch)
     log(f"[bench] device copy bandwidth {copy_gbps:.0f} GB/s (read+write)")
@@ -243,9 +270,10 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "paged_attn_decode launch (pass 1 + merge)",
-            "mean_launch_us": round(mean_launch_ms * 1e3, 3),
+            "kernel": f"pass 1 ({KERNEL_NAMES.get(dec.kernel, dec.kernel)} decode kernel)",
+            "mean_launch_us": round(mean_pass1 * 1e3, 3),
             "algorithmic_bytes_per_launch": kvb,
+            "combine_mean_us": round(mean_comb * 1e3, 3) if two else 0.0,
         },
         "device_copy_gbps": round(copy_gbps, 1),
         "cpu_baseline": cpu,

@@ -98,7 +98,15 @@ typedef struct {
                                    key partitions per sequence (tests, tuning) */
     int32_t kernel;             /* pa_kernel; PA_KERNEL_AUTO unless forcing a family.
                                    PA_KERNEL_MFMA needs fp16/bf16 and (H/KV)*nq <= 64 */
+    int32_t flags;              /* bitwise OR of pa_flag values, 0 by default */
 } pa_problem;
+
+typedef enum {
+    /* paged_attn_decode enqueues pass 1 only; the caller enqueues paged_attn_combine
+       (same problem, context_lens and workspace) on the same stream afterwards, e.g.
+       to time the two kernels separately. Without this flag decode does both. */
+    PA_FLAG_DEFER_COMBINE = 1
+} pa_flag;
 
 /*
  * Launch plan, a pure host function of the problem and the number of compute
@@ -168,7 +176,7 @@ int paged_attn_combine(const pa_problem* problem, const int32_t* context_lens,
 const char* paged_attn_last_error(void);
 
 /* ABI version of this header (major * 100 + minor). */
-int paged_attn_version(void);
+int paged_attn_version(void);  /* 101: pa_problem.flags */
 
 #ifdef __cplusplus
 }

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "libpaged_attn.so")
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_DEVICE, PA_ERR_LAUNCH = range(6)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
+PA_FLAG_DEFER_COMBINE = 1
 
 EXPORTED = ("pa_plan_ex", "pa_plan", "pa_workspace_size", "pa_workspace_size_ex",
             "paged_attn_decode", "paged_attn_combine", "paged_attn_last_error",
@@ -30,7 +31,7 @@ class PaProblem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "num_heads", "num_kv_heads", "head_dim", "block_size", "num_blocks",
         "max_blocks_per_seq", "nq", "causal", "dtype", "max_context_len", "num_partitions",
-        "kernel")]
+        "kernel", "flags")]
 
 
 class PagedAttnError(RuntimeError):
@@ -176,7 +177,8 @@ def _dtype_code(t) -> int:
 
 
 def make_problem(q, k_pool, block_table, *, max_context_len: int, causal: bool = True,
-                 num_partitions: int = 0, kernel: int = PA_KERNEL_AUTO) -> PaProblem:
+                 num_partitions: int = 0, kernel: int = PA_KERNEL_AUTO,
+                 flags: int = 0) -> PaProblem:
     B, H, NQ, D = q.shape
     NB, BS, KV, D2 = k_pool.shape
     assert D == D2, "head_dim of q and the pools differ"
@@ -184,17 +186,18 @@ def make_problem(q, k_pool, block_table, *, max_context_len: int, causal: bool =
                      num_blocks=NB, max_blocks_per_seq=block_table.shape[1] if block_table.dim() == 2 else 0,
                      nq=NQ, causal=int(causal), dtype=_dtype_code(q),
                      max_context_len=int(max_context_len), num_partitions=int(num_partitions),
-                     kernel=int(kernel))
+                     kernel=int(kernel), flags=int(flags))
 
 
 class Decoder:
     """Holds the problem, workspace and output of one decode shape for repeated calls."""
 
     def __init__(self, q, k_pool, block_table, *, max_context_len: int, causal: bool = True,
-                 num_partitions: int = 0, kernel: int = PA_KERNEL_AUTO):
+                 num_partitions: int = 0, kernel: int = PA_KERNEL_AUTO, flags: int = 0):
         import torch
         self.problem = make_problem(q, k_pool, block_table, max_context_len=max_context_len,
-                                    causal=causal, num_partitions=num_partitions, kernel=kernel)
+                                    causal=causal, num_partitions=num_partitions, kernel=kernel,
+                                    flags=flags)
         _, self.partitions, self.chunk_tokens, self.kernel = pa_plan(self.problem)
         _, self.workspace_bytes = pa_workspace_size(self.problem)
         dev = q.device

@@ -99,6 +99,8 @@ int validate_problem(const pa_problem* p) {
                     p->max_context_len, (long long)p->max_blocks_per_seq * p->block_size);
     if (p->num_partitions < 0)
         return fail(PA_ERR_INVALID_ARG, "num_partitions = %d is negative", p->num_partitions);
+    if (p->flags & ~PA_FLAG_DEFER_COMBINE)
+        return fail(PA_ERR_INVALID_ARG, "flags = 0x%x has unknown bits", p->flags);
     if (p->kernel != PA_KERNEL_AUTO && p->kernel != PA_KERNEL_VALU && p->kernel != PA_KERNEL_MFMA)
         return fail(PA_ERR_INVALID_ARG, "kernel = %d is not a pa_kernel", p->kernel);
     if (p->kernel == PA_KERNEL_MFMA && p->dtype == PA_F32)
@@ -458,7 +460,7 @@ int run_decode(const pa_problem* p, const Plan& pl, const void* q, const void* k
     if (hipError_t e = hipGetLastError(); e != hipSuccess)
         return fail(PA_ERR_LAUNCH, "pass-1 launch failed: %s; verify the device state",
                     hipGetErrorString(e));
-    if (pl.parts > 1) {
+    if (pl.parts > 1 && !(p->flags & PA_FLAG_DEFER_COMBINE)) {
         launch_combine<T>(p, pl, s, static_cast<const float*>(workspace), context_lens, out);
         if (hipError_t e = hipGetLastError(); e != hipSuccess)
             return fail(PA_ERR_LAUNCH, "combine launch failed: %s; verify the device state",
@@ -574,6 +576,6 @@ int paged_attn_combine(const pa_problem* problem, const int32_t* context_lens,
 
 const char* paged_attn_last_error(void) { return t_error.c_str(); }
 
-int paged_attn_version(void) { return 100; }
+int paged_attn_version(void) { return 101; }
 
 }  // extern "C"

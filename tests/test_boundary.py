@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(names) == set(pa.EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert pa.paged_attn_version() == 100
+    assert pa.paged_attn_version() == 101
 
 
 def spec_problem(spec: W.Spec, max_ctx: int, **kw) -> pa.PaProblem:
@@ -105,6 +105,7 @@ BAD = [
     (dict(num_blocks=0), pa.PA_ERR_INVALID_ARG),
     (dict(num_partitions=-2), pa.PA_ERR_INVALID_ARG),
     (dict(kernel=9), pa.PA_ERR_INVALID_ARG),
+    (dict(flags=6), pa.PA_ERR_INVALID_ARG),
     (dict(nq=64, num_heads=32), pa.PA_ERR_UNSUPPORTED),  # G*nq = 256 rows > 128
     (dict(nq=17, kernel=2), pa.PA_ERR_UNSUPPORTED),       # G*nq = 68 rows > 64 (matrix cores)
     (dict(dtype=0, kernel=2), pa.PA_ERR_UNSUPPORTED),     # matrix cores need 16-bit I/O

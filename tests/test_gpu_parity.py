@@ -247,3 +247,22 @@ def test_plan_on_device_matches_pure_host_plan():
                            max_context_len=w.max_context_len)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert pa.pa_plan(prob)[1:] == pa.pa_plan_ex(prob, cus)[1:]
+
+
+@pytest.mark.parametrize("kernel", [pa.PA_KERNEL_MFMA, pa.PA_KERNEL_VALU])
+def test_deferred_combine_matches_one_call(kernel):
+    w = to_device(W.make_workload(SMALL[1], device="cpu"))
+    table = torch.from_numpy(w.block_table).to(DEV)
+    lens = torch.from_numpy(w.context_lens).to(DEV)
+    args = (w.q, w.k_pool, w.v_pool, table, lens, w.new_k, w.new_v, w.scale)
+    one = pa.Decoder(w.q, w.k_pool, table, max_context_len=w.max_context_len, num_partitions=6,
+                     kernel=kernel)
+    two = pa.Decoder(w.q, w.k_pool, table, max_context_len=w.max_context_len, num_partitions=6,
+                     kernel=kernel, flags=pa.PA_FLAG_DEFER_COMBINE)
+    a = one(*args).clone()
+    two(*args)
+    pa.paged_attn_combine(two.problem, lens, two.workspace, two.workspace_bytes, two.out,
+                          stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert torch.equal(a, two.out)
+    check(w, a)
