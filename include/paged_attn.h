@@ -112,9 +112,12 @@ typedef enum {
  * Launch plan, a pure host function of the problem and the number of compute
  * units of the device (the page's partitions() plays this role: it picks the
  * partition count from the context length and the number of query rows).
- * Outputs: partitions = key partitions per sequence (1 = single pass, no
- * workspace, no combine), chunk_tokens = cached tokens per partition (a
- * multiple of block_size), kernel = pa_kernel family used for pass 1.
+ * Outputs: kernel = pa_kernel family used for pass 1; for PA_KERNEL_MFMA,
+ * partitions = segments the whole batch's keys are cut into (one per resident
+ * wave; 1 = no merge) and chunk_tokens = 16 * the minimum segment length in
+ * 16-key groups; for PA_KERNEL_VALU, partitions = key partitions per sequence
+ * (1 = single pass) and chunk_tokens = cached tokens per partition (a multiple
+ * of block_size). num_partitions > 0 in the problem fixes `partitions`.
  * Any output pointer may be NULL. No HIP call is made.
  */
 int pa_plan_ex(const pa_problem* problem, int32_t num_cus, int32_t* partitions,
@@ -126,17 +129,22 @@ int pa_plan(const pa_problem* problem, int32_t* partitions, int32_t* chunk_token
             int32_t* kernel);
 
 /*
- * Workspace bytes paged_attn_decode needs on the current device: 0 for a
- * single-pass plan. Otherwise, with rows = batch * num_heads * nq and P =
- * partitions, the fp32 layout is (row = (b*H + h)*nq + r):
- *   o[rows][P][head_dim]  unnormalised partial output  sum_i 2^(t_i - m) v_i
- *   ml[rows][P][2]        (m, l): m = max_i t_i, l = sum_i 2^(t_i - m)
- * where t_i = s_i * log2(e) over the keys of partition p of that row: the
- * page's VECTOR_PARTIALS state in base-2 units. Partitions past a sequence's
- * last one are not written, and neither are the rows of a sequence whose keys
- * fit in one partition (their output is final after pass 1). No initial
- * contents are required. pa_workspace_size_ex is the same for a device with num_cus compute units
- * (pure host).
+ * Workspace bytes paged_attn_decode needs on the current device: 0 for a plan
+ * that needs no merge. No initial contents are required. The workspace holds
+ * fp32 online-softmax states (the page's VECTOR_PARTIALS state, in base-2
+ * units): o = sum_i 2^(t_i - m) v_i (unnormalised), m = max_i t_i and
+ * l = sum_i 2^(t_i - m), with t_i = s_i * log2(e) over some keys of a row.
+ *   PA_KERNEL_MFMA (balanced split): all (sequence, KV head) key lists laid end
+ *   to end in groups of 16 keys are cut into `partitions` equal segments; a
+ *   segment's piece of unit u = b*KV + kh is slot u + segment. Layout:
+ *   o[slots][R][head_dim], ml[slots][R][2], then int32 [B*KV][2] = first and
+ *   last segment of each unit (written by pass 1); slots = B*KV + partitions,
+ *   R = (H/KV)*nq (rows of one unit, r_local = (h % G)*nq + r).
+ *   PA_KERNEL_VALU (chunks of chunk_tokens cached keys per sequence):
+ *   o[rows][P][head_dim], ml[rows][P][2] with rows = B*H*nq, row = (b*H + h)*nq + r.
+ * States that are not needed (a unit or sequence done in one piece) are not
+ * written; those outputs are final after pass 1. pa_workspace_size_ex is the
+ * same for a device with num_cus compute units (pure host).
  */
 int pa_workspace_size(const pa_problem* problem, size_t* bytes);
 int pa_workspace_size_ex(const pa_problem* problem, int32_t num_cus, size_t* bytes);
