@@ -90,10 +90,14 @@ namespace pa {
 // Merge for the balanced per-wave split (split.hpp): unit u = b*KV + h/G has one
 // state per segment s in [s0, s1] that overlaps it, stored in slot u + s; pass 1
 // recorded (s0, s1) per unit. Units inside one segment were finished by pass 1.
-// RPW = 4: a workgroup takes 4 rows of one unit, one wave per row, each wave
-// summing every piece with 8 pieces' loads in flight (few pieces per unit).
-// RPW = 1: a workgroup takes one row; its 4 waves take every 4th piece and are
-// merged through LDS (many pieces per unit, e.g. a few very long sequences).
+// The merge is PARTIALS_REDUCE of the docs.rs page "onnxruntime-ep-mlx 0.31.1:
+// src/ops/paged_attention.rs" in base 2: out = sum_s 2^(m_s - M) o_s /
+// sum_s 2^(m_s - M) l_s with M = max_s m_s.
+// WPR waves share one output row (WPR = 1: a workgroup takes 4 rows of a unit;
+// WPR = 4: one row, its pieces dealt to 4 waves in contiguous runs and the four
+// partial merges combined through LDS). Each wave loads the (m, l) of up to 64
+// pieces lane-parallel and the partial outputs of up to kBatch pieces at once,
+// so a row costs two dependent memory latencies after the metadata.
 template <typename T>
 struct SplitCombineArgs {
     const float* ws_o;     // [slots][R][D]
@@ -103,83 +107,106 @@ struct SplitCombineArgs {
     int KV, H, NQ, R;
 };
 
-template <typename T, int D, int RPW>
+template <typename T, int D, int WPR>
 __global__ __launch_bounds__(256) void combine_split(SplitCombineArgs<T> a) {
     using E = Elem<T>;
-    constexpr int PER = D / 64;
-    constexpr int BATCH = 8;
-    constexpr int WAVES_PER_ROW = 4 / RPW;
-    static_assert(D % 64 == 0 && (RPW == 1 || RPW == 4), "shape");
+    constexpr int PER = D / 64;      // output elements per lane
+    constexpr int kBatch = 16;       // partial outputs in flight per wave
+    constexpr int RPB = 4 / WPR;     // rows per workgroup
+    static_assert(D % 64 == 0 && (WPR == 1 || WPR == 4), "shape");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int tiles = (a.R + RPW - 1) / RPW;
+    const int R = a.R;
+    const int tiles = (R + RPB - 1) / RPB;
     const int64_t u = blockIdx.x / tiles;
-    const int rho = (int)(blockIdx.x % tiles) * RPW + (RPW == 4 ? wave : 0);
+    const int rho = (int)(blockIdx.x % tiles) * RPB + (WPR == 1 ? wave : 0);
     const int s0 = a.meta[2 * u], s1 = a.meta[2 * u + 1];
     if (s0 == s1) return;  // finished by pass 1 (whole workgroup)
-    const int n = s1 - s0 + 1, R = a.R;
+    const int n = s1 - s0 + 1;
+    const bool active = rho < R;  // WPR = 1: the unit's last tile may be short
+    // this wave's pieces [p0, p1) of the row
+    const int per_w = (n + WPR - 1) / WPR;
+    const int p0 = WPR == 1 ? 0 : min(n, wave * per_w), p1 = WPR == 1 ? n : min(n, p0 + per_w);
     const int64_t first = u + s0;
-    const int b = (int)(u / a.KV), kh = (int)(u % a.KV);
-    const int64_t grow = ((int64_t)b * a.H + (int64_t)kh * (a.H / a.KV)) * a.NQ + rho;
-    const bool active = rho < R;  // RPW = 4: the unit's last tile may be short
     const float* ml = a.ws_ml + (first * R + rho) * 2;
-    const int64_t mstride = (int64_t)R * 2;
     const float* po = a.ws_o + (first * R + rho) * D + lane * PER;
-    const int64_t ostride = (int64_t)R * D;
-    const int pw = RPW == 4 ? 0 : wave;  // first piece of this wave
+    const int64_t mstride = (int64_t)R * 2, ostride = (int64_t)R * D;
 
-    float M = kNegMax;
-    if (active)
-        for (int p = pw * 64 + lane; p < n; p += 64 * WAVES_PER_ROW)
-            M = fmaxf(M, ml[p * mstride]);
-    M = wave_max(M);
-    __shared__ float s_max[4], s_l[4];
-    __shared__ float s_o[4][D];
-    if constexpr (RPW == 1) {
-        if (lane == 0) s_max[wave] = M;
-        __syncthreads();
-        M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
-    }
+    float M = kNegMax, Lw = 0.f;
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    float lsum = 0.f;
     if (active) {
-        for (int p0 = pw; p0 < n; p0 += WAVES_PER_ROW * BATCH) {
-            float ov[BATCH][PER], mv[BATCH], lv[BATCH];
+        for (int c0 = p0; c0 < p1; c0 += 64) {  // runs of up to 64 pieces
+            const int cn = min(64, p1 - c0);
+            // partial outputs of the first batch, issued before the (m, l) are used
+            float ov[kBatch][PER];
 #pragma unroll
-            for (int j = 0; j < BATCH; ++j) {
-                const int p = p0 + WAVES_PER_ROW * j;
-                const bool ok = p < n;
+            for (int j = 0; j < kBatch; ++j)
 #pragma unroll
-                for (int e = 0; e < PER; ++e) ov[j][e] = ok ? po[p * ostride + e] : 0.f;
-                mv[j] = ok ? ml[p * mstride] : kNegMax;
-                lv[j] = ok ? ml[p * mstride + 1] : 0.f;
-            }
+                for (int e = 0; e < PER; ++e)
+                    ov[j][e] = j < cn ? po[(c0 + j) * ostride + e] : 0.f;
+            const bool mine = lane < cn;
+            const float mp = mine ? ml[(c0 + lane) * mstride] : kNegMax;
+            const float lp = mine ? ml[(c0 + lane) * mstride + 1] : 0.f;
+            const float Mr = wave_max(mp);
+            const float Mn = fmaxf(M, Mr);
+            const float sc = fast_exp2(M - Mn);  // rescale what earlier runs gathered
+            Lw *= sc;
 #pragma unroll
-            for (int j = 0; j < BATCH; ++j) {
-                const float w = fast_exp2(mv[j] - M);
-                lsum = fmaf(w, lv[j], lsum);
+            for (int e = 0; e < PER; ++e) acc[e] *= sc;
+            M = Mn;
+            const float wp = mine ? fast_exp2(mp - M) : 0.f;
+            Lw += wave_sum(wp * lp);
+            for (int j0 = 0; j0 < cn; j0 += kBatch) {
+                if (j0 > 0) {
 #pragma unroll
-                for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, ov[j][e], acc[e]);
+                    for (int j = 0; j < kBatch; ++j)
+#pragma unroll
+                        for (int e = 0; e < PER; ++e)
+                            ov[j][e] = j0 + j < cn ? po[(c0 + j0 + j) * ostride + e] : 0.f;
+                }
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    // weight of piece j0 + j (lane j0 + j; 0 past the run's end)
+                    const float w = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wp), (j0 + j) & 63));
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, ov[j][e], acc[e]);
+                }
             }
         }
     }
-    if constexpr (RPW == 1) {
+    if constexpr (WPR == 4) {
+        __shared__ float s_m[4], s_l[4];
+        __shared__ float s_o[4][D];
+        if (lane == 0) {
+            s_m[wave] = M;
+            s_l[wave] = Lw;
+        }
 #pragma unroll
         for (int e = 0; e < PER; ++e) s_o[wave][lane * PER + e] = acc[e];
-        if (lane == 0) s_l[wave] = lsum;
         __syncthreads();
-        if (threadIdx.x < D) {
+        if (active && threadIdx.x < D) {
             const int d = threadIdx.x;
-            const float lt = (s_l[0] + s_l[1]) + (s_l[2] + s_l[3]);
-            const float o = (s_o[0][d] + s_o[1][d]) + (s_o[2][d] + s_o[3][d]);
+            const float Mt = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+            float o = 0.f, lt = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float f = fast_exp2(s_m[w] - Mt);
+                o = fmaf(f, s_o[w][d], o);
+                lt = fmaf(f, s_l[w], lt);
+            }
+            const int b = (int)(u / a.KV), kh = (int)(u % a.KV);
+            const int64_t grow = ((int64_t)b * a.H + (int64_t)kh * (a.H / a.KV)) * a.NQ + rho;
             E::store(a.out + grow * D + d, lt != 0.f ? o / lt : 0.f);
         }
     } else if (active) {
+        const int b = (int)(u / a.KV), kh = (int)(u % a.KV);
+        const int64_t grow = ((int64_t)b * a.H + (int64_t)kh * (a.H / a.KV)) * a.NQ + rho;
         T* dst = a.out + grow * D + lane * PER;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) E::store(dst + e, lsum != 0.f ? acc[e] / lsum : 0.f);
+        for (int e = 0; e < PER; ++e) E::store(dst + e, Lw != 0.f ? acc[e] / Lw : 0.f);
     }
 }
 

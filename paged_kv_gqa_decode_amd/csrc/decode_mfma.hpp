@@ -1,34 +1,38 @@
 // Pass 1 of paged GQA decode attention on the matrix cores (gfx950, fp16/bf16),
-// with the work cut into equal per-wave segments (split.hpp).
+// with the work cut into equal segments along the key axis (split.hpp).
 //
 // Operation: docs.rs page "onnxruntime-ep-mlx 0.31.1: src/ops/paged_attention.rs",
 // VECTOR_BODY (scores, online softmax, accumulation) and VECTOR_PARTIALS.
 //
-// A wave attends one piece (a run of 16-key sub-pages of one (sequence, KV
-// head) unit) at a time, for all R = G*NQ query rows of the KV head in row
-// tiles of 16, so each K/V page is fetched from HBM once per GQA group:
+// A segment is a run of 16-key sub-pages along the axis of all (sequence, KV
+// head) units; it is attended for all R = G*NQ query rows of each KV head in
+// row tiles of 16, so each K/V page is fetched from HBM once per GQA group:
 //   scores  S^T[16 keys x 16 rows] = K Q^T  : v_mfma_f32_16x16x32 (D/32 steps);
 //           A = K: lane l holds key l%16, 8 elements of d; B = Q: row l%16
 //   softmax fp32 on the VALU; the D-layout of S^T (key 4*(l/16)+i, row l%16)
 //           is exactly the A layout of the next product, so P stays in lane
-//   output  O[16 rows x 16 d] += P V        : v_mfma_f32_16x16x16 per 16 d;
-//           B = V: lane l needs keys 4*(l/16)..+3 at one d. Each lane loads the
+//   output  O[16 rows x 16 d] += P V per 16 d (Mfma<T>::pv);
+//           B = V: lane l needs keys 4*(l/16)..+3 at one d. Each lane reads the
 //           dword (d, d+1) of its 4 keys and v_perm splits it into the
 //           operands of two d-columns, so output tile 2j holds d = 32j + 2c and
 //           tile 2j+1 holds d = 32j + 2c + 1 for column c.
-// bf16 probabilities are split into hi + lo bf16 parts (two products), so P
-// keeps ~16 significant bits; fp16 P keeps 11. The reference max moves only
-// when a score exceeds it by more than 2^kSlack (probabilities stay <= 256),
-// so the accumulators are rescaled almost never.
-// Block-table entries of a piece are read 64 pages at a time into one VGPR
-// (lane i = page i) and taken with readlane. K/V sub-pages are staged through
-// LDS: each wave owns one sub-page slot; buffer loads write it directly
-// (no VGPRs held by loads in flight), the wave copies it to registers in the
-// MFMA operand layout and immediately issues the next sub-page into the slot,
-// so one sub-page per wave is always in flight while the previous is computed.
-// Small register footprint -> 4 waves per SIMD; many waves, each with one
-// sub-page in flight, is what keeps HBM busy on this part.
+// The reference max moves only when a score exceeds it by more than 2^kSlack
+// (probabilities stay <= 256), so the accumulators are rescaled almost never.
+// Sub-pages are staged through LDS by buffer-to-LDS loads (no VGPRs held by
+// loads in flight); block-table entries are read 64 pages at a time into one
+// VGPR (lane i = page i), one sub-page ahead of their use, and taken with
+// readlane.
+//   decode_mfma (R <= 16): one wave per segment with one LDS slot; the wave
+//     reads the slot into registers and refills it with the next sub-page
+//     before computing, so one sub-page per wave is in flight at all times.
+//     Four waves per SIMD.
+//   decode_mfma_coop (16 < R <= 64): NW waves per segment (one per row tile)
+//     share a ring of kRing slots; each wave loads its share of every
+//     sub-page, one barrier per sub-page publishes it, and kRing - 1
+//     sub-pages per workgroup are in flight.
 #pragma once
+
+#include <type_traits>
 
 #include "split.hpp"
 
@@ -45,40 +49,59 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 template <typename T> struct Mfma;
 
+// Mfma<T>: the two products of one 16-key sub-page and the P operand.
+//   qk: S^T += K Q^T over 32 d (v_mfma_f32_16x16x32).
+//   make_p: P operand(s) of 4 probabilities of a lane. fp16: one operand
+//     (round to nearest). bf16: p = hi + lo with hi = p truncated to bf16 and
+//     lo = the exact fp32 remainder truncated again, so P keeps ~16 bits.
+//   pv: O += P V for one 16-column output tile. fp16: v_mfma_f32_16x16x16f16.
+//     bf16: one v_mfma_f32_16x16x32_bf16 whose 32-long contraction holds the
+//     hi parts against V and the lo parts against the same V again (lane k
+//     index 8*g + j: j < 4 -> hi of key 4*g + j, j >= 4 -> lo of key 4*g + j - 4).
 template <> struct Mfma<_Float16> {
-    static constexpr bool kSplitP = false;
     __device__ static __forceinline__ f32x4_t qk(u32x4_t k, u32x4_t q, f32x4_t acc) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, k),
                                                       __builtin_bit_cast(f16x8_t, q), acc, 0, 0, 0);
-    }
-    __device__ static __forceinline__ f32x4_t pv(u32x2_t p, u32x2_t v, f32x4_t acc) {
-        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, p),
-                                                     __builtin_bit_cast(f16x4_t, v), acc, 0, 0, 0);
     }
     __device__ static __forceinline__ unsigned pack2(float lo, float hi) {
         return (unsigned)__builtin_bit_cast(uint16_t, (_Float16)lo) |
                ((unsigned)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
     }
+    __device__ static __forceinline__ void make_p(const float (&p)[4], u32x2_t& phi, u32x2_t&) {
+        phi = u32x2_t{pack2(p[0], p[1]), pack2(p[2], p[3])};
+    }
+    __device__ static __forceinline__ f32x4_t pv(u32x2_t phi, u32x2_t, u32x2_t v, f32x4_t acc) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, phi),
+                                                     __builtin_bit_cast(f16x4_t, v), acc, 0, 0, 0);
+    }
 };
 
 template <> struct Mfma<bf16_t> {
-    static constexpr bool kSplitP = true;
     __device__ static __forceinline__ f32x4_t qk(u32x4_t k, u32x4_t q, f32x4_t acc) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k),
                                                        __builtin_bit_cast(bf16x8_t, q), acc, 0, 0, 0);
     }
-    __device__ static __forceinline__ f32x4_t pv(u32x2_t p, u32x2_t v, f32x4_t acc) {
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, p),
-                                                         __builtin_bit_cast(i16x4_t, v), acc, 0, 0, 0);
-    }
     __device__ static __forceinline__ unsigned pack2(float lo, float hi) {
         return (unsigned)f32_to_bf16_rne(lo) | ((unsigned)f32_to_bf16_rne(hi) << 16);
     }
+    // high halves of two fp32 values, packed (element 0 in the low half)
+    __device__ static __forceinline__ unsigned high2(float a, float b) {
+        return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+    }
+    __device__ static __forceinline__ void make_p(const float (&p)[4], u32x2_t& phi, u32x2_t& plo) {
+        float lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo[i] = p[i] - __uint_as_float(__float_as_uint(p[i]) & 0xffff0000u);
+        phi = u32x2_t{high2(p[0], p[1]), high2(p[2], p[3])};
+        plo = u32x2_t{high2(lo[0], lo[1]), high2(lo[2], lo[3])};
+    }
+    __device__ static __forceinline__ f32x4_t pv(u32x2_t phi, u32x2_t plo, u32x2_t v, f32x4_t acc) {
+        const u32x4_t a = u32x4_t{phi[0], phi[1], plo[0], plo[1]};
+        const u32x4_t b = u32x4_t{v[0], v[1], v[0], v[1]};
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+    }
 };
-
-__device__ __forceinline__ float bf16_round(float x) {
-    return __uint_as_float((unsigned)f32_to_bf16_rne(x) << 16);
-}
 
 // Raw buffer descriptor over `bytes` bytes at p (GFX9-family format word).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
@@ -89,6 +112,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int b
 // | vmcnt[5:4] << 14): wait for all vector-memory operations, or for all LDS ops.
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitLgkm0 = 0xC07F;
+// wait until at most n vector-memory operations of this wave are outstanding
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 // Slack of the lazy reference max, in log2 units (probabilities stay <= 256).
 constexpr float kSlack = 8.0f;
@@ -111,84 +136,239 @@ struct SplitArgs {
     float qscale;  // scale * log2(e)
 };
 
-template <int KS, int NP>
-struct SubPage {
-    u32x4_t k[KS];      // key c16, d = 32*kk + 8*g16 .. +8
-    unsigned v[NP][4];  // keys 4*g16 + j, d = 32*np + 2*c16 .. +1
-};
-
-// LDS layout of one sub-page slot (16 keys): K operands first, one 16-byte
-// chunk per lane per score step (kk*1024 + lane*16); then V, one 16-byte chunk
-// per lane per output tile pair holding the dwords of keys 4*g16 + 0..3.
+// LDS layout of one sub-page slot (16 keys), filled by row-coalesced 16-byte
+// buffer-to-LDS loads; each load instruction fills 1 KB (kKeysPerOp whole
+// rows of 2*D bytes).
+//  K: rows back to back; chunk c (16 bytes) of key k sits at position
+//     c ^ swz(k), so a K-operand read (keys 0..15, one chunk) spreads over all
+//     banks. Offsets depend on the key: one fetch offset per instruction.
+//  V: plain rows, with kVPad bytes after each instruction's 1 KB, so a
+//     V-operand read (keys 4*g + j, g = 0..3, one dword column) lands on
+//     distinct banks for the four g; addresses are one base plus constants.
 template <typename T, int D>
 struct SlotLayout {
-    static constexpr int kKBytes = 16 * D * (int)sizeof(T);
-    static constexpr int kBytes = 2 * kKBytes;
+    static constexpr int kRowBytes = D * (int)sizeof(T);
+    static constexpr int kChunks = kRowBytes / 16;       // 16-byte chunks per row
+    static constexpr int kKeysPerOp = 1024 / kRowBytes;  // rows per load instruction
+    static constexpr int kOps = 16 / kKeysPerOp;         // load instructions per half
+    static constexpr int kRowsPerBank = 256 / kRowBytes; // rows sharing one 256-byte bank line
+    static constexpr int kVPad = 64;
+    static constexpr int kKBytes = 16 * kRowBytes;
+    static constexpr int kVBytes = kOps * (1024 + kVPad);
+    static constexpr int kBytes = kKBytes + kVBytes;
+    __device__ static __forceinline__ int swz(int k) { return (k / kRowsPerBank) % kChunks; }
+    // K: byte offset of logical chunk c of key k
+    __device__ static __forceinline__ int k_addr(int k, int c) {
+        return k * kRowBytes + ((c ^ swz(k)) << 4);
+    }
+    // K: the offset lane l fetches in instruction i is k_fetch_base ^ (64*i).
+    // For both row sizes the instruction-i row of lane l has swz = 4*i + l/16,
+    // so its chunk is ((l % kChunks) ^ (l/16)) ^ (4*i): only offset bits 6..7
+    // depend on i, and the row part is a multiple of the 256- or 128-byte row.
+    __device__ static __forceinline__ int k_fetch_base(int lane, int tbytes) {
+        return (lane / kChunks) * tbytes + (((lane % kChunks) ^ (lane >> 4)) << 4);
+    }
+    // V: offset that lane l fetches in every instruction (plain rows)
+    __device__ static __forceinline__ int v_fetch_off(int lane, int tbytes) {
+        return (lane / kChunks) * tbytes + ((lane % kChunks) << 4);
+    }
+    // V: byte offset (from the V half) of element d of key k
+    __device__ static __forceinline__ int v_addr(int k, int d) {
+        return (k / kKeysPerOp) * (1024 + kVPad) + (k % kKeysPerOp) * kRowBytes + d * (int)sizeof(T);
+    }
 };
 
-template <typename T, int D, int BS, int NRT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NRT == 1 ? 4 : 1, 4)))
-void decode_mfma(SplitArgs<T> a) {
-    using M = Mfma<T>;
-    constexpr int KS = D / 32;    // score MFMA steps over d
-    constexpr int NT = D / 16;    // output tiles over d
-    constexpr int NP = D / 32;    // output tile pairs
-    constexpr int SUB = BS / 16;  // 16-key sub-pages per page
-    static_assert(D % 32 == 0 && BS % 16 == 0, "shape");
+typedef __attribute__((address_space(3))) void lds_void;
 
-    using Slot = SlotLayout<T, D>;
-    extern __shared__ __attribute__((aligned(16))) char smem[];  // 4 slots, then the prefix
-    int* s_pref = reinterpret_cast<int*>(smem + 4 * Slot::kBytes);
-    build_prefix(a.context_lens, a.g, s_pref);
-    const int64_t W = split_total(a.g, s_pref);
-    const int64_t sigma = split_sigma(a.g, W);
+// ---- the stream of one segment's sub-pages: cursor, table windows, fetches ----
+template <typename T, int D, int BS>
+struct SubPageStream {
+    using Lay = SlotLayout<T, D>;
+    static constexpr int KS = D / 32;    // load instructions per half (K or V)
+    static constexpr int SUB = BS / 16;  // 16-key sub-pages per page
+    static constexpr int kNewStride = D * (int)sizeof(T);  // row stride of new_k/new_v
 
-    // The wave index is uniform within a wave; saying so keeps every per-piece
-    // quantity (sequence, head, page, descriptors, LDS slot) in scalar registers.
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    char* slot_lds = smem + wave * Slot::kBytes;
-    const int c16 = lane & 15, g16 = lane >> 4;
-    const int gw = blockIdx.x * 4 + wave;  // this wave's segment
-    int64_t x = (int64_t)gw * sigma;
-    const int64_t x_end = min(W, x + sigma);
-    if (x >= W) return;  // no barrier follows
-    const int KV = a.g.KV, NQ = a.g.NQ, R = a.R;
-    const int G = a.H / KV;
-    const int nnew = (NQ + 15) / 16;
-    const int64_t tstride = (int64_t)KV * D;
+    struct Cur {
+        int b, kh, j;   // unit (b, kh), sub-page j of it
+        int nsub, nc;   // sub-pages of the unit; the first nc hold cached keys
+        int L;          // cached keys of sequence b
+    };
+    struct Src {
+        const T* k;  // first row of the 16-key span (head kh)
+        const T* v;
+        int rmax;    // last row that exists (15 for cached keys)
+    };
 
-    int b = split_find_seq(a.g, s_pref, x);
-    while (x < x_end) {
-        while ((int64_t)KV * s_pref[b + 1] <= x) ++b;
-        const int nsub = s_pref[b + 1] - s_pref[b];
-        const int64_t seq_start = (int64_t)KV * s_pref[b];
-        const int kh = (int)((x - seq_start) / nsub);
-        const int64_t ustart = seq_start + (int64_t)kh * nsub;
-        const int64_t pend = min(x_end, ustart + nsub);
-        const int j0 = (int)(x - ustart), j1 = (int)(pend - ustart);
-        const int L = min(max(a.context_lens[b], 0), a.g.max_tokens);
-        const int nc = nsub - nnew;  // cached sub-pages = ceil(L / 16)
-        const int64_t grow0 = ((int64_t)b * a.H + (int64_t)kh * G) * NQ;
-        if (j0 == 0 && lane == 0 && a.meta) {  // the unit's first piece records its segments
-            int32_t* mt = a.meta + 2 * ((int64_t)b * KV + kh);
-            mt[0] = (int32_t)(ustart / sigma);
-            mt[1] = (int32_t)((ustart + nsub - 1) / sigma);
+    const SplitArgs<T>& a;
+    const int* s_pref;
+    const int* s_len;
+    int KV, NQ, nnew, tbytes, lane;
+    int kfb, vfb;  // per-lane fetch offsets of a cached sub-page
+    int win_b = -1, win_base = 0, win_phys = 0;  // table window in use
+    int pre_b = -1, pre_base = 0, pre_phys = 0;  // table window loaded ahead
+
+    __device__ __forceinline__ SubPageStream(const SplitArgs<T>& args, const int* pref,
+                                             const int* lens, int ln)
+        : a(args), s_pref(pref), s_len(lens), KV(args.g.KV), NQ(args.g.NQ),
+          nnew((args.g.NQ + 15) / 16), tbytes(args.g.KV * D * (int)sizeof(T)), lane(ln) {
+        kfb = Lay::k_fetch_base(lane, tbytes);
+        vfb = Lay::v_fetch_off(lane, tbytes);
+    }
+    __device__ __forceinline__ void enter_seq(Cur& c) const {
+        c.nsub = s_pref[c.b + 1] - s_pref[c.b];
+        c.nc = c.nsub - nnew;
+        c.L = s_len[c.b];
+    }
+    __device__ __forceinline__ Cur seek(int64_t x) const {  // the sub-page at axis position x
+        Cur c;
+        c.b = split_find_seq(a.g, s_pref, x);
+        enter_seq(c);
+        const int64_t off = x - (int64_t)KV * s_pref[c.b];
+        c.kh = (int)(off / c.nsub);
+        c.j = (int)(off - (int64_t)c.kh * c.nsub);
+        return c;
+    }
+    __device__ __forceinline__ void step(Cur& c) const {  // next sub-page along the axis
+        if (++c.j < c.nsub) return;
+        c.j = 0;
+        if (++c.kh < KV) return;
+        c.kh = 0;
+        ++c.b;
+        enter_seq(c);
+    }
+    // Loads the table window of c ahead of locate(c), unless it is loaded.
+    // COMPLETE: wait for the load right here (a window change is rare), so no
+    // register stays pending across the caller's loop, whose other loads are
+    // counted precisely.
+    template <bool COMPLETE = false>
+    __device__ __forceinline__ void prefetch_table(const Cur& c) {
+        if (c.j >= c.nc) return;  // new rows: no table
+        const int base = (c.j / SUB) & ~63;
+        if ((c.b == win_b && base == win_base) || (c.b == pre_b && base == pre_base)) return;
+        pre_b = c.b;
+        pre_base = base;
+        const int npages = (c.L + BS - 1) / BS;
+        pre_phys = base + lane < npages
+                       ? a.block_table[(int64_t)c.b * a.max_blocks + base + lane] : 0;
+        if constexpr (COMPLETE) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
+    __device__ __forceinline__ Src locate(const Cur& c) {
+        Src s;
+        if (c.j < c.nc) {
+            const int page = c.j / SUB;
+            if (c.b != win_b || (page & ~63) != win_base) {  // loaded ahead by prefetch_table
+                win_b = pre_b;
+                win_base = pre_base;
+                win_phys = pre_phys;
+            }
+            const int64_t phys = __builtin_amdgcn_readlane(win_phys, page - win_base);
+            const int64_t row0 = phys * BS + 16 * (c.j % SUB);
+            s.k = a.k_pool + (row0 * KV + c.kh) * D;
+            s.v = a.v_pool + (row0 * KV + c.kh) * D;
+            s.rmax = 15;
+        } else {
+            const int t0 = 16 * (c.j - c.nc);
+            const int64_t r0 = ((int64_t)c.b * KV + c.kh) * NQ + t0;
+            s.k = a.new_k + r0 * D;
+            s.v = a.new_v + r0 * D;
+            s.rmax = min(15, NQ - t0 - 1);
         }
+        return s;
+    }
+    // Issues load instructions i = i0, i0 + istep, ... (< KS) of the K and the
+    // V half of sub-page `s` into the slot at `slot` (row-coalesced, 16 bytes
+    // per lane per instruction). Cached keys: pool row stride, no range check
+    // needed. New rows: all offsets in voffset and rows past nq clamped to the
+    // last one (they are masked later). (Offsets go in as plain int values: an
+    // array element or a dependent expression passed as is makes the host
+    // compilation pass drop the kernel's launch stub.)
+    template <int COUNT>
+    __device__ __forceinline__ void fetch(const Src& s, char* slot, int i0, int istep,
+                                          bool cached) const {
+        char* const k_lds = slot;
+        char* const v_lds = slot + Lay::kKBytes;
+        if (cached) {
+            const __amdgpu_buffer_rsrc_t kr = make_rsrc(s.k, 16 * tbytes);
+            const __amdgpu_buffer_rsrc_t vr = make_rsrc(s.v, 16 * tbytes);
+#pragma unroll
+            for (int t = 0; t < COUNT; ++t) {
+                const int i = i0 + istep * t;
+                const int koff = kfb ^ (64 * i);
+                const int soff = i * Lay::kKeysPerOp * tbytes;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(k_lds + i * 1024), 16,
+                                                         koff, soff, 0, 0);
+            }
+#pragma unroll
+            for (int t = 0; t < COUNT; ++t) {
+                const int i = i0 + istep * t;
+                const int soff = i * Lay::kKeysPerOp * tbytes;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    vr, (lds_void*)(v_lds + i * (1024 + Lay::kVPad)), 16, vfb, soff, 0, 0);
+            }
+        } else {
+            const __amdgpu_buffer_rsrc_t kr = make_rsrc(s.k, (s.rmax + 1) * kNewStride);
+            const __amdgpu_buffer_rsrc_t vr = make_rsrc(s.v, (s.rmax + 1) * kNewStride);
+            int ln = lane;
+            asm volatile("" : "+v"(ln));  // computed here, not kept live across the loop
+#pragma unroll
+            for (int t = 0; t < COUNT; ++t) {
+                const int i = i0 + istep * t;
+                const int row = Lay::kKeysPerOp * i + ln / Lay::kChunks;
+                const int rc = min(row, s.rmax);
+                const int koff = rc * kNewStride + (((ln % Lay::kChunks) ^ Lay::swz(row)) << 4);
+                const int voff = rc * kNewStride + ((ln % Lay::kChunks) << 4);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(k_lds + i * 1024), 16,
+                                                         koff, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    vr, (lds_void*)(v_lds + i * (1024 + Lay::kVPad)), 16, voff, 0, 0, 0);
+            }
+        }
+    }
+    // axis position of the first sub-page of unit (c.b, c.kh)
+    __device__ __forceinline__ int64_t unit_start(const Cur& c) const {
+        return (int64_t)KV * s_pref[c.b] + (int64_t)c.kh * c.nsub;
+    }
+};
 
-        // Q operand (B of S^T = K Q^T): row 16*rt + c16, d = 32*kk + 8*g16 .. +8
-        u32x4_t qop[NRT][KS];
+// ---- online-softmax state of NRT row tiles (rows 16*(rt0 + rt) + c16) ----
+template <typename T, int D, int NRT>
+struct RowTiles {
+    using M = Mfma<T>;
+    using Lay = SlotLayout<T, D>;
+    static constexpr int KS = D / 32;  // score MFMA steps over d
+    static constexpr int NT = D / 16;  // output tiles over d
+    static constexpr int NP = D / 32;  // output tile pairs
+
+    const SplitArgs<T>& a;
+    int lane, c16, g16, rt0;
+    u32x4_t qop[NRT][KS];  // B of S^T = K Q^T: row 16*(rt0+rt) + c16, d = 32*kk + 8*g16 .. +8
+    float m[NRT], lsum[NRT];
+    f32x4_t acc[NRT][NT];
+    u32x2_t phi[NRT], plo[NRT];
+    int rmod[NRT];  // query row modulo nq: its position among the new rows
+
+    __device__ __forceinline__ RowTiles(const SplitArgs<T>& args, int ln, int first_tile)
+        : a(args), lane(ln), c16(ln & 15), g16(ln >> 4), rt0(first_tile) {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) rmod[rt] = (16 * (rt0 + rt) + c16) % args.g.NQ;
+    }
+    __device__ __forceinline__ int64_t grow0(int b, int kh) const {  // first output row of the unit
+        const int G = a.H / a.g.KV;
+        return ((int64_t)b * a.H + (int64_t)kh * G) * a.g.NQ;
+    }
+    __device__ __forceinline__ void load_q(int b, int kh) {
+        const int64_t g0 = grow0(b, kh);
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
-            const int row = 16 * rt + c16;
+            const int row = 16 * (rt0 + rt) + c16;
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk)
-                qop[rt][kk] = row < R ? *reinterpret_cast<const u32x4_t*>(
-                                            a.q + (grow0 + row) * D + 32 * kk + 8 * g16)
-                                      : u32x4_t{0, 0, 0, 0};
+                qop[rt][kk] = row < a.R ? *reinterpret_cast<const u32x4_t*>(
+                                              a.q + (g0 + row) * D + 32 * kk + 8 * g16)
+                                        : u32x4_t{0, 0, 0, 0};
         }
-        float m[NRT], lsum[NRT];
-        f32x4_t acc[NRT][NT];
+    }
+    __device__ __forceinline__ void reset() {
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
             m[rt] = kNegMax;
@@ -196,190 +376,107 @@ void decode_mfma(SplitArgs<T> a) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-
-        // Attend one 16-key sub-page: keys [0, valid) exist. For new rows
-        // (is_new) key tau is new row t0 + tau, visible to query rows by causality.
-        // kop(kk): K operand of score step kk; vquad(np): this lane's dwords of
-        // keys 4*g16 + 0..3 at d = 32*np + 2*c16. Both read just before use.
-        auto attend = [&](auto&& kop, auto&& vquad, int valid, bool is_new, int t0) {
-            // V operands of output tiles 2*np and 2*np+1, built right before use
-            auto vops = [&](int np, u32x2_t& lo, u32x2_t& hi) {
-                const u32x4_t q4 = vquad(np);
-                unsigned v[4];
+    }
+    // K operands and V dwords of one sub-page, read from a slot.
+    __device__ __forceinline__ void read_k(const char* slot, u32x4_t (&kop)[KS]) const {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    v[j] = (4 * g16 + j < valid) ? q4[j] : 0u;  // unused slots may be NaN
-                lo = u32x2_t{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u),
-                             __builtin_amdgcn_perm(v[3], v[2], 0x05040100u)};
-                hi = u32x2_t{__builtin_amdgcn_perm(v[1], v[0], 0x07060302u),
-                             __builtin_amdgcn_perm(v[3], v[2], 0x07060302u)};
-            };
+        for (int kk = 0; kk < KS; ++kk)
+            kop[kk] = *reinterpret_cast<const u32x4_t*>(slot + Lay::k_addr(c16, 4 * kk + g16));
+    }
+    __device__ __forceinline__ void read_v(const char* slot, unsigned (&vq)[NP][4]) const {
+        // this lane's dwords of keys 4*g16 + 0..3 at d = 32*np + 2*c16
+        const char* const v_rd = slot + Lay::kKBytes + Lay::v_addr(4 * g16, 2 * c16);
 #pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) {
-                f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int np = 0; np < NP; ++np)
 #pragma unroll
-                for (int kk = 0; kk < KS; ++kk) s = M::qk(kop(kk), qop[rt][kk], s);
-                float sv[4];
-                const int row = 16 * rt + c16;
+            for (int jj = 0; jj < 4; ++jj)
+                vq[np][jj] = *reinterpret_cast<const unsigned*>(v_rd + Lay::v_addr(jj, 32 * np));
+    }
+    // Visible-key limits of one sub-page: keys [0, valid) exist; for new rows
+    // (is_new) key tau is new row t0 + tau, visible to a query row by causality.
+    __device__ __forceinline__ void limits(int valid, bool is_new, int t0, int (&lim)[NRT]) const {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tau = 4 * g16 + i;
-                    bool vis = tau < valid;
-                    if (is_new) vis = vis && (!a.causal || t0 + tau <= row % NQ);
-                    sv[i] = vis ? s[i] * a.qscale : -__builtin_inff();
-                }
-                // m[rt] is the same in the 4 lanes of a row (lanes c16 + 16*g).
-                float tm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-                if (__any(tm > m[rt] + kSlack)) {
-                    tm = fmaxf(tm, __shfl_xor(tm, 16));
-                    tm = fmaxf(tm, __shfl_xor(tm, 32));  // exact max of the row's 16 keys
-                    const float mn = tm > m[rt] + kSlack ? tm : m[rt];
-                    const float alpha = fast_exp2(m[rt] - mn);
-                    m[rt] = mn;
-                    lsum[rt] *= alpha;
-                    float ai[4];  // output rows 4*g16 + i take the factor of that row
+        for (int rt = 0; rt < NRT; ++rt)
+            lim[rt] = is_new && a.causal ? min(valid, rmod[rt] - t0 + 1) : valid;
+    }
+    // S^T and the online softmax for one sub-page; leaves the P operands in
+    // phi/plo. Keys 4*g16 + i >= lim[rt] are not visible to this lane's row.
+    __device__ __forceinline__ void scores(const u32x4_t (&kop)[KS], const int (&lim)[NRT]) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g16 + i);
+        for (int rt = 0; rt < NRT; ++rt) {
+            f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
+            for (int kk = 0; kk < KS; ++kk) s = M::qk(kop[kk], qop[rt][kk], s);
+            float sv[4];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[rt][nt][i] *= ai[i];
-                }
-                float p[4];
+            for (int i = 0; i < 4; ++i) sv[i] = 4 * g16 + i < lim[rt] ? s[i] * a.qscale : -__builtin_inff();
+            // m[rt] is the same in the 4 lanes of a row (lanes c16 + 16*g).
+            float tm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+            if (__any(tm > m[rt] + kSlack)) {
+                tm = fmaxf(tm, __shfl_xor(tm, 16));
+                tm = fmaxf(tm, __shfl_xor(tm, 32));  // exact max of the row's 16 keys
+                const float mn = tm > m[rt] + kSlack ? tm : m[rt];
+                const float alpha = fast_exp2(m[rt] - mn);
+                m[rt] = mn;
+                lsum[rt] *= alpha;
+                float ai[4];  // output rows 4*g16 + i take the factor of that row
 #pragma unroll
-                for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - m[rt]);
-                lsum[rt] += (p[0] + p[1]) + (p[2] + p[3]);
-                if constexpr (!M::kSplitP) {
-                    const u32x2_t pop = u32x2_t{M::pack2(p[0], p[1]), M::pack2(p[2], p[3])};
+                for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g16 + i);
 #pragma unroll
-                    for (int np = 0; np < NP; ++np) {
-                        u32x2_t vlo, vhi;
-                        vops(np, vlo, vhi);
-                        acc[rt][2 * np] = M::pv(pop, vlo, acc[rt][2 * np]);
-                        acc[rt][2 * np + 1] = M::pv(pop, vhi, acc[rt][2 * np + 1]);
-                    }
-                } else {
-                    float hi[4], lo[4];
+                for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        hi[i] = bf16_round(p[i]);
-                        lo[i] = p[i] - hi[i];
-                    }
-                    const u32x2_t phi = u32x2_t{M::pack2(hi[0], hi[1]), M::pack2(hi[2], hi[3])};
-                    const u32x2_t plo = u32x2_t{M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3])};
-#pragma unroll
-                    for (int np = 0; np < NP; ++np) {
-                        u32x2_t vlo, vhi;
-                        vops(np, vlo, vhi);
-                        acc[rt][2 * np] = M::pv(phi, vlo, acc[rt][2 * np]);
-                        acc[rt][2 * np] = M::pv(plo, vlo, acc[rt][2 * np]);
-                        acc[rt][2 * np + 1] = M::pv(phi, vhi, acc[rt][2 * np + 1]);
-                        acc[rt][2 * np + 1] = M::pv(plo, vhi, acc[rt][2 * np + 1]);
-                    }
-                }
+                    for (int i = 0; i < 4; ++i) acc[rt][nt][i] *= ai[i];
             }
-        };
-
-        // ---- cached sub-pages [j0, jc) of this unit ----
-        const int jc = min(j1, nc);
-        if (j0 < jc) {
-            const T* kpool = a.k_pool + (int64_t)kh * D;
-            const T* vpool = a.v_pool + (int64_t)kh * D;
-            const int32_t* trow = a.block_table + (int64_t)b * a.max_blocks;
-            const int npages = (L + BS - 1) / BS;
-            int pbase = -1000000, phys_lane = 0;  // lane i: block of page pbase + i
-            // One buffer descriptor per sub-page (wave-uniform, scalar registers).
-            // K: lane l fetches key c16, d = 32*kk + 8*g16 (16 bytes) into
-            // kk*1024 + l*16. V: for output tile pair np and key quad i, lane l
-            // fetches the dword of key 4*i + (l&3) at d = 32*np + 2*(l>>2) into
-            // K_bytes + np*1024 + i*256 + l*4, which puts lane L's dwords of keys
-            // 4*(L/16)+0..3 at K_bytes + np*1024 + L*16.
-            const uint32_t koff = (uint32_t)((c16 * tstride + 8 * g16) * sizeof(T));
-            const uint32_t voff = (uint32_t)(((lane & 3) * tstride + 2 * (lane >> 2)) * sizeof(T));
-            const uint32_t quad = (uint32_t)(4 * tstride * sizeof(T));
-            const int span = (int)(16 * tstride * sizeof(T));  // bytes a sub-page spans
-            typedef __attribute__((address_space(3))) void lds_void;
-            auto issue = [&](int j) {
-                const int page = j / SUB, sub = j % SUB;
-                if (page >= pbase + 64) {
-                    pbase = page;
-                    phys_lane = page + lane < npages ? trow[page + lane] : 0;
-                }
-                const int64_t phys = __builtin_amdgcn_readlane(phys_lane, page - pbase);
-                const int64_t row0 = phys * BS + 16 * sub;
-                const __amdgpu_buffer_rsrc_t kr = make_rsrc(kpool + row0 * tstride, span);
-                const __amdgpu_buffer_rsrc_t vr = make_rsrc(vpool + row0 * tstride, span);
+            float p[4];
 #pragma unroll
-                for (int kk = 0; kk < KS; ++kk)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        kr, (lds_void*)(slot_lds + kk * 1024), 16, koff, 64 * kk, 0, 0);
-#pragma unroll
-                for (int np = 0; np < NP; ++np)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                            vr, (lds_void*)(slot_lds + Slot::kKBytes + np * 1024 + i * 256), 4,
-                            voff, i * quad + 64 * np, 0, 0);
-            };
-            auto kop_lds = [&](int kk) {
-                return *reinterpret_cast<const u32x4_t*>(slot_lds + kk * 1024 + lane * 16);
-            };
-            auto vquad_lds = [&](int np) {
-                return *reinterpret_cast<const u32x4_t*>(slot_lds + Slot::kKBytes + np * 1024 +
-                                                         lane * 16);
-            };
-            issue(j0);
-            for (int j = j0; j < jc; ++j) {
-                __builtin_amdgcn_s_waitcnt(kWaitVm0);    // sub-page j has landed in the slot
-                attend(kop_lds, vquad_lds, min(16, L - 16 * j), false, 0);
-                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // slot read out: free for j + 1
-                if (j + 1 < jc) issue(j + 1);
-            }
+            for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - m[rt]);
+            lsum[rt] += (p[0] + p[1]) + (p[2] + p[3]);
+            M::make_p(p, phi[rt], plo[rt]);
         }
-
-        // ---- new-row tiles [max(j0, nc), j1) of this unit ----
-        const int64_t nbase = ((int64_t)b * KV + kh) * NQ;
-        for (int j = max(j0, nc); j < j1; ++j) {
-            const int t0 = 16 * (j - nc);
-            SubPage<KS, NP> sp;
-            const int tk = t0 + c16;
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk)
-                sp.k[kk] = tk < NQ ? *reinterpret_cast<const u32x4_t*>(
-                                         a.new_k + (nbase + tk) * D + 32 * kk + 8 * g16)
-                                   : u32x4_t{0, 0, 0, 0};
+    }
+    // O += P V; keys [valid, 16) are zeroed first (their slot rows may hold NaN).
+    __device__ __forceinline__ void accumulate(unsigned (&vq)[NP][4], int valid) {
+        if (valid < 16) {
 #pragma unroll
             for (int np = 0; np < NP; ++np)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int tv = t0 + 4 * g16 + jj;
-                    sp.v[np][jj] = tv < NQ ? *reinterpret_cast<const unsigned*>(
-                                                 a.new_v + (nbase + tv) * D + 32 * np + 2 * c16)
-                                           : 0u;
-                }
-            attend([&](int kk) { return sp.k[kk]; },
-                   [&](int np) {
-                       return u32x4_t{sp.v[np][0], sp.v[np][1], sp.v[np][2], sp.v[np][3]};
-                   },
-                   min(16, NQ - t0), true, t0);
+                for (int jj = 0; jj < 4; ++jj)
+                    if (4 * g16 + jj >= valid) vq[np][jj] = 0u;
         }
-
-        // ---- emit: the finished output, or this piece's state for the combine ----
-        const bool whole = (j0 == 0 && j1 == nsub);
-        const int64_t slot = (int64_t)b * KV + kh + gw;
+#pragma unroll
+        for (int np = 0; np < NP; ++np) {
+            const unsigned* v = vq[np];
+            // operands of output tiles 2*np (even d) and 2*np+1 (odd d)
+            const u32x2_t vlo = u32x2_t{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u),
+                                        __builtin_amdgcn_perm(v[3], v[2], 0x05040100u)};
+            const u32x2_t vhi = u32x2_t{__builtin_amdgcn_perm(v[1], v[0], 0x07060302u),
+                                        __builtin_amdgcn_perm(v[3], v[2], 0x07060302u)};
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+                acc[rt][2 * np] = M::pv(phi[rt], plo[rt], vlo, acc[rt][2 * np]);
+                acc[rt][2 * np + 1] = M::pv(phi[rt], plo[rt], vhi, acc[rt][2 * np + 1]);
+            }
+        }
+    }
+    // The unit's finished output (whole unit attended here), or this piece's
+    // state for the combine (workspace slot u + segment).
+    __device__ __forceinline__ void emit(int b, int kh, int64_t segment, bool whole) const {
+        const int64_t g0 = grow0(b, kh);
+        const int R = a.R;
+        const int64_t slot = (int64_t)b * a.g.KV + kh + segment;
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
             float lrow = lsum[rt];
             lrow += __shfl_xor(lrow, 16);
-            lrow += __shfl_xor(lrow, 32);  // l of row 16*rt + c16
+            lrow += __shfl_xor(lrow, 32);  // l of row 16*(rt0+rt) + c16
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 16 * rt + 4 * g16 + i;  // output row held in acc[rt][*][i]
+                const int r = 16 * (rt0 + rt) + 4 * g16 + i;  // output row held in acc[rt][*][i]
                 const float l_r = __shfl(lrow, 4 * g16 + i);
                 if (r >= R) continue;
                 if (whole) {
                     const float inv = l_r != 0.f ? 1.f / l_r : 0.f;
-                    unsigned* dst = reinterpret_cast<unsigned*>(a.out + (grow0 + r) * D + 2 * c16);
+                    unsigned* dst = reinterpret_cast<unsigned*>(a.out + (g0 + r) * D + 2 * c16);
 #pragma unroll
                     for (int np = 0; np < NP; ++np)
                         dst[16 * np] = M::pack2(acc[rt][2 * np][i] * inv, acc[rt][2 * np + 1][i] * inv);
@@ -390,13 +487,209 @@ void decode_mfma(SplitArgs<T> a) {
                         dst[16 * np] = f32x2_t{acc[rt][2 * np][i], acc[rt][2 * np + 1][i]};
                 }
             }
-            if (!whole && g16 == 0 && 16 * rt + c16 < R) {
-                float* ml = a.ws_ml + (slot * R + 16 * rt + c16) * 2;
+            const int row = 16 * (rt0 + rt) + c16;
+            if (!whole && g16 == 0 && row < R) {
+                float* ml = a.ws_ml + (slot * R + row) * 2;
                 ml[0] = m[rt];
                 ml[1] = lrow;
             }
         }
-        x = pend;
+    }
+};
+
+// The first piece of a unit records the segments [s0, s1] that overlap it.
+template <typename T, typename Stream>
+__device__ __forceinline__ void record_segments(const SplitArgs<T>& a, const Stream& st,
+                                                const typename Stream::Cur& c, int64_t sigma) {
+    const int64_t ustart = st.unit_start(c);
+    int32_t* mt = a.meta + 2 * ((int64_t)c.b * a.g.KV + c.kh);
+    mt[0] = (int32_t)(ustart / sigma);
+    mt[1] = (int32_t)((ustart + c.nsub - 1) / sigma);
+}
+
+// ---- one wave per segment (R <= 16) ----
+template <typename T, int D, int BS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void decode_mfma(SplitArgs<T> a) {
+    using Lay = SlotLayout<T, D>;
+    using Stream = SubPageStream<T, D, BS>;
+    using Cur = typename Stream::Cur;
+    constexpr int KS = D / 32, NP = D / 32;
+    static_assert(D % 32 == 0 && BS % 16 == 0 && Lay::kOps == KS, "shape");
+
+    // LDS: 4 sub-page slots, then the per-sequence prefix and lengths.
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    int* s_pref = reinterpret_cast<int*>(smem + 4 * Lay::kBytes);
+    int* s_len = s_pref + a.g.B + 1;
+    build_prefix(a.context_lens, a.g, s_pref, s_len);
+    const int64_t W = split_total(a.g, s_pref);
+    const int64_t sigma = split_sigma(a.g, W);
+
+    // The wave index is uniform within a wave; saying so keeps every per-unit
+    // quantity (sequence, head, page, descriptors, LDS slot) in scalar registers.
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    char* const slot = smem + wave * Lay::kBytes;
+    const int gw = blockIdx.x * 4 + wave;  // this wave's segment
+    const int64_t x0 = (int64_t)gw * sigma;
+    if (x0 >= W) return;  // no barrier follows
+    const int n_total = (int)(min(W, x0 + sigma) - x0);  // sub-pages this wave attends
+
+    Stream st(a, s_pref, s_len, lane);
+    RowTiles<T, D, 1> rows(a, lane, 0);
+    Cur cc = st.seek(x0);  // the sub-page being attended
+    Cur pc = cc;           // the next sub-page to fetch
+    st.prefetch_table(cc);
+    st.template fetch<KS>(st.locate(cc), slot, 0, 1, cc.j < cc.nc);
+    if (n_total > 1) {
+        st.step(pc);
+        st.prefetch_table(pc);
+    }
+    rows.load_q(cc.b, cc.kh);
+    rows.reset();
+    bool piece_from_start = cc.j == 0;
+    for (int i = 0; i < n_total; ++i) {
+        const bool more = i + 1 < n_total;  // pc is the next sub-page of this wave
+        if (cc.j == 0 && lane == 0 && a.meta) record_segments(a, st, cc, sigma);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);  // sub-page i, table window, Q have landed
+        // Read the whole slot out, then refill it with the next sub-page at once:
+        // the fetch is in flight during all of this sub-page's arithmetic.
+        u32x4_t kop[KS];
+        unsigned vq[NP][4];
+        rows.read_k(slot, kop);
+        rows.read_v(slot, vq);
+        if (more) {
+            const typename Stream::Src sn = st.locate(pc);
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // slot read out
+            st.template fetch<KS>(sn, slot, 0, 1, pc.j < pc.nc);
+        }
+        const bool is_new = cc.j >= cc.nc;
+        const int t0 = 16 * (cc.j - cc.nc);
+        const int valid = is_new ? min(16, st.NQ - t0) : min(16, cc.L - 16 * cc.j);
+        int lim[1];
+        rows.limits(valid, is_new, t0, lim);
+        rows.scores(kop, lim);
+        if (more && pc.j == 0) rows.load_q(pc.b, pc.kh);  // Q of the next unit
+        rows.accumulate(vq, valid);
+        if (cc.j + 1 == cc.nsub || !more) {
+            rows.emit(cc.b, cc.kh, gw, piece_from_start && cc.j + 1 == cc.nsub);
+            rows.reset();
+            piece_from_start = true;
+        }
+        if (more) {
+            cc = pc;
+            if (i + 2 < n_total) {
+                st.step(pc);
+                st.prefetch_table(pc);
+            }
+        }
+    }
+}
+
+// ---- NW waves per segment, one row tile each, sharing a ring of sub-pages ----
+constexpr int kRing = 4;  // sub-page slots per workgroup
+
+template <typename T, int D, int BS, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void decode_mfma_coop(SplitArgs<T> a) {
+    using Lay = SlotLayout<T, D>;
+    using Stream = SubPageStream<T, D, BS>;
+    using Cur = typename Stream::Cur;
+    constexpr int KS = D / 32, NP = D / 32;
+    constexpr int NWI = NW < KS ? NW : KS;  // waves that issue loads
+    constexpr int IPW = KS / NWI;           // instructions per half per issuing wave
+    static_assert(D % 32 == 0 && BS % 16 == 0 && Lay::kOps == KS && KS % NWI == 0, "shape");
+    static_assert(kRing >= 3, "ring");
+
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    int* s_pref = reinterpret_cast<int*>(smem + kRing * Lay::kBytes);
+    int* s_len = s_pref + a.g.B + 1;
+    build_prefix(a.context_lens, a.g, s_pref, s_len);
+    const int64_t W = split_total(a.g, s_pref);
+    const int64_t sigma = split_sigma(a.g, W);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t seg = blockIdx.x;  // this workgroup's segment
+    const int64_t x0 = seg * sigma;
+    if (x0 >= W) return;  // uniform over the workgroup: no barrier follows
+    const int n_total = (int)(min(W, x0 + sigma) - x0);
+    const bool issues = wave < NWI;  // this wave loads instructions wave, wave + NWI, ...
+    const bool has_rows = 16 * wave < a.R;
+
+    Stream st(a, s_pref, s_len, lane);
+    RowTiles<T, D, 1> rows(a, lane, wave);
+    Cur cc = st.seek(x0);
+    Cur pc = cc;  // next sub-page to fetch: kRing - 1 ahead of cc once primed
+    // prime the ring: sub-pages 0 .. kRing-2 into slots 0 .. kRing-2
+    int primed = 0;
+    for (; primed < kRing - 1 && primed < n_total; ++primed) {
+        st.template prefetch_table<true>(pc);
+        const typename Stream::Src s0 = st.locate(pc);
+        if (issues) st.template fetch<IPW>(s0, smem + primed * Lay::kBytes, wave, NWI, pc.j < pc.nc);
+        if (primed + 1 < n_total) st.step(pc);
+    }
+    st.template prefetch_table<true>(pc);
+    if (has_rows) rows.load_q(cc.b, cc.kh);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the ring is primed; Q and tables are in
+    rows.reset();
+    bool piece_from_start = cc.j == 0;
+    for (int i = 0; i < n_total; ++i) {
+        const int ahead = min(kRing - 2, n_total - 1 - i);  // sub-pages fetched after i
+        if (cc.j == 0 && lane == 0 && wave == 0 && a.meta) record_segments(a, st, cc, sigma);
+        // this wave's loads of sub-page i have landed (later ones may be in flight)
+        if (issues) {
+            if (ahead >= 2) __builtin_amdgcn_s_waitcnt(wait_vm(2 * IPW * 2));
+            else if (ahead == 1) __builtin_amdgcn_s_waitcnt(wait_vm(2 * IPW));
+            else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        } else {
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);  // Q and the table window
+        }
+        // Every wave's part of sub-page i is in; slot i-1 is read out. A bare
+        // barrier: each wave has already waited for its own loads (LDS needs no
+        // flush within the CU), and a fenced barrier would also wait for the
+        // loads still in flight into the other slots.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // refill the slot of sub-page i - 1 with sub-page i + kRing - 1
+        const int nxt = i + kRing - 1;
+        if (nxt < n_total) {
+            const typename Stream::Src sn = st.locate(pc);
+            if (issues)
+                st.template fetch<IPW>(sn, smem + (nxt % kRing) * Lay::kBytes, wave, NWI, pc.j < pc.nc);
+            if (nxt + 1 < n_total) {
+                st.step(pc);
+                st.template prefetch_table<true>(pc);
+            }
+        }
+        const char* slot = smem + (i % kRing) * Lay::kBytes;
+        const bool is_new = cc.j >= cc.nc;
+        const int t0 = 16 * (cc.j - cc.nc);
+        const int valid = is_new ? min(16, st.NQ - t0) : min(16, cc.L - 16 * cc.j);
+        const bool unit_ends = cc.j + 1 == cc.nsub || i + 1 == n_total;
+        if (has_rows) {
+            u32x4_t kop[KS];
+            unsigned vq[NP][4];
+            rows.read_k(slot, kop);
+            rows.read_v(slot, vq);
+            int lim[1];
+            rows.limits(valid, is_new, t0, lim);
+            rows.scores(kop, lim);
+            rows.accumulate(vq, valid);
+            if (unit_ends) {
+                rows.emit(cc.b, cc.kh, seg, piece_from_start && cc.j + 1 == cc.nsub);
+                rows.reset();
+            }
+        }
+        if (unit_ends) piece_from_start = true;
+        if (i + 1 < n_total) {
+            st.step(cc);
+            if (has_rows && cc.j == 0) {  // Q of the next unit (rare: waited for at once)
+                rows.load_q(cc.b, cc.kh);
+                __builtin_amdgcn_s_waitcnt(kWaitVm0);
+            }
+        }
     }
 }
 

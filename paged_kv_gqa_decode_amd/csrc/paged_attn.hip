@@ -40,10 +40,11 @@ int succeed() {
 
 constexpr int kMaxRows = 128;         // G * nq
 constexpr int kMfmaMaxRows = 64;      // the matrix-core family keeps <= 4 row tiles of 16
-// Resident waves per CU the matrix-core kernel reaches on register use, by row
-// tiles (its occupancy attribute): the balanced split gives every resident wave
-// one segment. LDS can lower it further (mfma_waves_per_cu).
-constexpr int kMfmaWavesPerCu[5] = {0, 16, 4, 4, 4};
+// Resident waves per CU the matrix-core kernels reach on register use (their
+// occupancy attribute: 4 per SIMD). The balanced split gives every resident
+// wave (R <= 16) or workgroup (R > 16, one wave per row tile) one segment; LDS
+// can lower it further (mfma_segments_per_cu).
+constexpr int kMfmaWavesPerCu = 16;
 constexpr int kLdsPerCu = 160 * 1024;
 // A piece's saved state may be at most 1/kStateRatio of the K/V bytes it covers.
 constexpr int kStateRatio = 8;
@@ -137,18 +138,26 @@ struct Plan {
     int n_tiles;  // workgroups per KV head along the rows (1 for MFMA)
 };
 
-// Dynamic LDS of the matrix-core kernel: 4 sub-page slots (16 keys of K and V)
-// plus the per-sequence prefix of the split.
-size_t mfma_lds_bytes(const pa_problem* p) {
-    const size_t elem = p->dtype == PA_F32 ? 4 : 2;
-    const size_t slots = 4 * (2 * 16 * (size_t)p->head_dim * elem);
-    return slots + ((size_t)p->batch + 1) * sizeof(int);
+// Waves per workgroup of the matrix-core family: 4 single-wave segments for
+// R <= 16 (decode_mfma), else one wave per row tile, 2 or 4 (decode_mfma_coop).
+int mfma_group_waves(int row_tiles) { return row_tiles <= 2 ? (row_tiles == 1 ? 4 : 2) : 4; }
+
+// Dynamic LDS of a matrix-core workgroup: its sub-page slots (4: one per wave,
+// or the ring of the cooperative kernel) plus the per-sequence prefix of the
+// split and the sequence lengths.
+size_t mfma_lds_bytes(const pa_problem* p, int row_tiles) {
+    const size_t slot = p->head_dim == 64 ? pa::SlotLayout<_Float16, 64>::kBytes
+                                           : pa::SlotLayout<_Float16, 128>::kBytes;
+    const size_t slots = row_tiles == 1 ? 4 : pa::kRing;
+    return slots * slot + (2 * (size_t)p->batch + 1) * sizeof(int);
 }
 
-int mfma_waves_per_cu(const pa_problem* p, int row_tiles) {
-    const int by_lds = (int)(kLdsPerCu / mfma_lds_bytes(p)) * 4;
-    const int by_regs = kMfmaWavesPerCu[row_tiles];
-    return by_lds < by_regs ? by_lds : by_regs;
+// Segments one CU holds at once: waves (R <= 16) or workgroups (R > 16).
+int mfma_segments_per_cu(const pa_problem* p, int row_tiles) {
+    const int nw = mfma_group_waves(row_tiles);
+    int groups = (int)(kLdsPerCu / mfma_lds_bytes(p, row_tiles));
+    if (groups > kMfmaWavesPerCu / nw) groups = kMfmaWavesPerCu / nw;
+    return row_tiles == 1 ? 4 * groups : groups;
 }
 
 int plan_impl(const pa_problem* p, int num_cus, Plan* pl) {
@@ -175,7 +184,7 @@ int plan_impl(const pa_problem* p, int num_cus, Plan* pl) {
             pl->parts = p->num_partitions;
             pl->min_seg = 1;
         } else {
-            pl->parts = num_cus * mfma_waves_per_cu(p, pl->rt);
+            pl->parts = num_cus * mfma_segments_per_cu(p, pl->rt);
             pl->min_seg = (int)ceil_div(kStateRatio * state, kv_per_group);
         }
         pl->chunk = 16 * pl->min_seg;
@@ -306,12 +315,14 @@ void launch_valu(const Plan& pl, dim3 grid, hipStream_t s, const pa::DecodeArgs<
 }
 
 template <typename T, int D, int BS>
-void launch_mfma(const Plan& pl, dim3 grid, size_t lds, hipStream_t s, const pa::SplitArgs<T>& a) {
-    switch (pl.rt) {
-        case 1: hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 1>), grid, dim3(256), lds, s, a); break;
-        case 2: hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 2>), grid, dim3(256), lds, s, a); break;
-        case 3: hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 3>), grid, dim3(256), lds, s, a); break;
-        default: hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 4>), grid, dim3(256), lds, s, a); break;
+void launch_mfma(const Plan& pl, size_t lds, hipStream_t s, const pa::SplitArgs<T>& a) {
+    if (pl.rt == 1) {
+        const dim3 grid((unsigned)ceil_div(pl.parts, 4));
+        hipLaunchKernelGGL((pa::decode_mfma<T, D, BS>), grid, dim3(256), lds, s, a);
+    } else if (mfma_group_waves(pl.rt) == 2) {
+        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2>), dim3(pl.parts), dim3(128), lds, s, a);
+    } else {
+        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 4>), dim3(pl.parts), dim3(256), lds, s, a);
     }
 }
 
@@ -350,14 +361,13 @@ void launch_pass1_mfma(const pa_problem* p, const Plan& pl, hipStream_t s,
     a.max_blocks = p->max_blocks_per_seq;
     a.R = (p->num_heads / p->num_kv_heads) * p->nq;
     a.qscale = d.qscale;
-    const dim3 grid((unsigned)ceil_div(pl.parts, 4));
-    const size_t lds = mfma_lds_bytes(p);
+    const size_t lds = mfma_lds_bytes(p, pl.rt);
     if (p->head_dim == 64) {
-        if (p->block_size == 16) launch_mfma<T, 64, 16>(pl, grid, lds, s, a);
-        else launch_mfma<T, 64, 32>(pl, grid, lds, s, a);
+        if (p->block_size == 16) launch_mfma<T, 64, 16>(pl, lds, s, a);
+        else launch_mfma<T, 64, 32>(pl, lds, s, a);
     } else {
-        if (p->block_size == 16) launch_mfma<T, 128, 16>(pl, grid, lds, s, a);
-        else launch_mfma<T, 128, 32>(pl, grid, lds, s, a);
+        if (p->block_size == 16) launch_mfma<T, 128, 16>(pl, lds, s, a);
+        else launch_mfma<T, 128, 32>(pl, lds, s, a);
     }
 }
 
@@ -395,21 +405,22 @@ void launch_combine(const pa_problem* p, const Plan& pl, hipStream_t s, const fl
         c.H = p->num_heads;
         c.NQ = p->nq;
         c.R = (p->num_heads / p->num_kv_heads) * p->nq;
-        // pieces per unit is data dependent; segments / units + 1 estimates it
+        // pieces per unit is data dependent; segments / units + 1 estimates it.
+        // Many pieces per row: four waves per row; else one wave per row.
         const int64_t units = (int64_t)p->batch * p->num_kv_heads;
         const int64_t pieces = pl.parts / units + 1;
-        if (pieces >= 32) {
+        if (pieces >= 48) {
             const dim3 grid((unsigned)(units * c.R));
-            if (p->head_dim == 64)
-                hipLaunchKernelGGL((pa::combine_split<T, 64, 1>), grid, dim3(256), 0, s, c);
-            else
-                hipLaunchKernelGGL((pa::combine_split<T, 128, 1>), grid, dim3(256), 0, s, c);
-        } else {
-            const dim3 grid((unsigned)(units * ((c.R + 3) / 4)));
             if (p->head_dim == 64)
                 hipLaunchKernelGGL((pa::combine_split<T, 64, 4>), grid, dim3(256), 0, s, c);
             else
                 hipLaunchKernelGGL((pa::combine_split<T, 128, 4>), grid, dim3(256), 0, s, c);
+        } else {
+            const dim3 grid((unsigned)(units * ((c.R + 3) / 4)));
+            if (p->head_dim == 64)
+                hipLaunchKernelGGL((pa::combine_split<T, 64, 1>), grid, dim3(256), 0, s, c);
+            else
+                hipLaunchKernelGGL((pa::combine_split<T, 128, 1>), grid, dim3(256), 0, s, c);
         }
         return;
     }

@@ -27,41 +27,40 @@ struct SplitGeometry {
     int min_seg;                // minimum segment length, in sub-pages
 };
 
-// s_pref[b] = sum_{b' < b} n_sub(b'), b = 0..B (exclusive prefix in LDS).
-// Every thread of the workgroup must call this; ends with __syncthreads.
+// s_pref[b] = sum_{b' < b} n_sub(b'), b = 0..B (exclusive prefix in LDS), and
+// s_len[b] = the cached length of sequence b clamped to [0, max_tokens].
+// Every thread of the workgroup must call this; the first wave scans 64
+// sequences per round (8 rounds' loads in flight at once), one barrier at the end.
 __device__ __forceinline__ void build_prefix(const int32_t* context_lens, const SplitGeometry& g,
-                                             int* s_pref) {
-    __shared__ int s_part[256];
-    const int nnew = (g.NQ + 15) / 16;
-    const int per = (g.B + 255) / 256;
-    const int b0 = threadIdx.x * per;
-    int sum = 0;
-    for (int i = 0; i < per; ++i) {
-        const int b = b0 + i;
-        if (b < g.B) {
-            const int L = min(max(context_lens[b], 0), g.max_tokens);
-            sum += (L + 15) / 16 + nnew;
+                                             int* s_pref, int* s_len) {
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const int nnew = (g.NQ + 15) / 16;
+        int carry = 0;
+        for (int base = 0; base < g.B; base += 512) {
+            int n[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int b = base + 64 * r + lane;
+                const int L = b < g.B ? min(max(context_lens[b], 0), g.max_tokens) : 0;
+                if (b < g.B) s_len[b] = L;
+                n[r] = b < g.B ? (L + 15) / 16 + nnew : 0;
+            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                int incl = n[r];  // inclusive scan over the wave
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int v = __shfl_up(incl, off);
+                    if (lane >= off) incl += v;
+                }
+                const int b = base + 64 * r + lane;
+                if (b < g.B) s_pref[b] = carry + incl - n[r];
+                carry += __shfl(incl, 63);
+            }
         }
+        if (lane == 0) s_pref[g.B] = carry;
     }
-    s_part[threadIdx.x] = sum;
-    __syncthreads();
-    // exclusive scan of the 256 partial sums (Hillis-Steele in LDS)
-    for (int off = 1; off < 256; off <<= 1) {
-        const int v = threadIdx.x >= off ? s_part[threadIdx.x - off] : 0;
-        __syncthreads();
-        s_part[threadIdx.x] += v;
-        __syncthreads();
-    }
-    int run = threadIdx.x > 0 ? s_part[threadIdx.x - 1] : 0;
-    for (int i = 0; i < per; ++i) {
-        const int b = b0 + i;
-        if (b < g.B) {
-            s_pref[b] = run;
-            const int L = min(max(context_lens[b], 0), g.max_tokens);
-            run += (L + 15) / 16 + nnew;
-        }
-    }
-    if (threadIdx.x == 255) s_pref[g.B] = s_part[255];
     __syncthreads();
 }
 

@@ -91,6 +91,8 @@ GEOMETRIES = [
     (3, 8, 1, 64, 32, 3, True, "f16", (15, 16, 33)),   # MQA, multi-row
     (2, 8, 2, 128, 32, 3, False, "bf16", (31, 64)),    # non-causal multi-row
     (2, 16, 2, 128, 16, 8, True, "f16", (0, 333)),     # 64 rows per KV head
+    (2, 16, 2, 64, 16, 5, True, "bf16", (40, 250)),    # 40 rows, D=64: 2 of 4 waves load
+    (2, 16, 1, 128, 32, 3, True, "f16", (100, 1)),     # 48 rows: one wave without rows
     (1, 32, 2, 128, 16, 8, True, "bf16", (500,)),      # 128 rows per KV head
     (2, 4, 2, 64, 16, 2, True, "f32", (129, 1)),
     (2, 4, 2, 128, 32, 1, True, "f32", (700, 64)),
