@@ -19,9 +19,9 @@
 // The reference max moves only when a score exceeds it by more than 2^kSlack
 // (probabilities stay <= 256), so the accumulators are rescaled almost never.
 // Sub-pages are staged through LDS by buffer-to-LDS loads (no VGPRs held by
-// loads in flight); block-table entries are read 64 pages at a time into one
-// VGPR (lane i = page i), one sub-page ahead of their use, and taken with
-// readlane.
+// loads in flight); block-table entries are scalar loads issued one fetch ahead
+// of their use, so they never share the vector-memory counter with the loads
+// whose completion the kernels count.
 //   decode_mfma (R <= 16): one wave per segment with one LDS slot; the wave
 //     reads the slot into registers and refills it with the next sub-page
 //     before computing, so one sub-page per wave is in flight at all times.
@@ -200,16 +200,17 @@ struct SubPageStream {
     };
 
     const SplitArgs<T>& a;
+    const int32_t* __restrict__ table;  // block table; entries are read with scalar loads
     const int* s_pref;
     const int* s_len;
     int KV, NQ, nnew, tbytes, lane;
     int kfb, vfb;  // per-lane fetch offsets of a cached sub-page
-    int win_b = -1, win_base = 0, win_phys = 0;  // table window in use
-    int pre_b = -1, pre_base = 0, pre_phys = 0;  // table window loaded ahead
+    int pre_b = -1, pre_page = 0, pre_phys = 0;  // table entry loaded ahead
 
-    __device__ __forceinline__ SubPageStream(const SplitArgs<T>& args, const int* pref,
+    __device__ __forceinline__ SubPageStream(const SplitArgs<T>& args,
+                                             const int32_t* __restrict__ tab, const int* pref,
                                              const int* lens, int ln)
-        : a(args), s_pref(pref), s_len(lens), KV(args.g.KV), NQ(args.g.NQ),
+        : a(args), table(tab), s_pref(pref), s_len(lens), KV(args.g.KV), NQ(args.g.NQ),
           nnew((args.g.NQ + 15) / 16), tbytes(args.g.KV * D * (int)sizeof(T)), lane(ln) {
         kfb = Lay::k_fetch_base(lane, tbytes);
         vfb = Lay::v_fetch_off(lane, tbytes);
@@ -236,32 +237,23 @@ struct SubPageStream {
         ++c.b;
         enter_seq(c);
     }
-    // Loads the table window of c ahead of locate(c), unless it is loaded.
-    // COMPLETE: wait for the load right here (a window change is rare), so no
-    // register stays pending across the caller's loop, whose other loads are
-    // counted precisely.
-    template <bool COMPLETE = false>
+    // Block-table entry of a cached sub-page: a scalar load (wave-uniform
+    // address, read-only table), counted apart from the vector loads in flight.
+    __device__ __forceinline__ int table_entry(const Cur& c) const {
+        return table[(int64_t)c.b * a.max_blocks + c.j / SUB];
+    }
+    // Starts loading the table entry of c ahead of locate(c).
     __device__ __forceinline__ void prefetch_table(const Cur& c) {
         if (c.j >= c.nc) return;  // new rows: no table
-        const int base = (c.j / SUB) & ~63;
-        if ((c.b == win_b && base == win_base) || (c.b == pre_b && base == pre_base)) return;
         pre_b = c.b;
-        pre_base = base;
-        const int npages = (c.L + BS - 1) / BS;
-        pre_phys = base + lane < npages
-                       ? a.block_table[(int64_t)c.b * a.max_blocks + base + lane] : 0;
-        if constexpr (COMPLETE) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        pre_page = c.j / SUB;
+        pre_phys = table_entry(c);
     }
-    __device__ __forceinline__ Src locate(const Cur& c) {
+    __device__ __forceinline__ Src locate(const Cur& c) const {
         Src s;
         if (c.j < c.nc) {
             const int page = c.j / SUB;
-            if (c.b != win_b || (page & ~63) != win_base) {  // loaded ahead by prefetch_table
-                win_b = pre_b;
-                win_base = pre_base;
-                win_phys = pre_phys;
-            }
-            const int64_t phys = __builtin_amdgcn_readlane(win_phys, page - win_base);
+            const int64_t phys = (c.b == pre_b && page == pre_page) ? pre_phys : table_entry(c);
             const int64_t row0 = phys * BS + 16 * (c.j % SUB);
             s.k = a.k_pool + (row0 * KV + c.kh) * D;
             s.v = a.v_pool + (row0 * KV + c.kh) * D;
@@ -508,16 +500,20 @@ __device__ __forceinline__ void record_segments(const SplitArgs<T>& a, const Str
 }
 
 // ---- one wave per segment (R <= 16) ----
+// The wave streams its segment's sub-pages through one LDS slot: it reads the
+// slot into registers and refills it with the next sub-page before computing,
+// so one sub-page per wave is in flight at all times (four waves per SIMD).
 template <typename T, int D, int BS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void decode_mfma(SplitArgs<T> a) {
+void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table) {
     using Lay = SlotLayout<T, D>;
     using Stream = SubPageStream<T, D, BS>;
+    using Rows = RowTiles<T, D, 1>;
     using Cur = typename Stream::Cur;
     constexpr int KS = D / 32, NP = D / 32;
     static_assert(D % 32 == 0 && BS % 16 == 0 && Lay::kOps == KS, "shape");
 
-    // LDS: 4 sub-page slots, then the per-sequence prefix and lengths.
+    // LDS: per wave one slot, then the prefix and lengths.
     extern __shared__ __attribute__((aligned(16))) char smem[];
     int* s_pref = reinterpret_cast<int*>(smem + 4 * Lay::kBytes);
     int* s_len = s_pref + a.g.B + 1;
@@ -529,21 +525,21 @@ void decode_mfma(SplitArgs<T> a) {
     // quantity (sequence, head, page, descriptors, LDS slot) in scalar registers.
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    char* const slot = smem + wave * Lay::kBytes;
-    const int gw = blockIdx.x * 4 + wave;  // this wave's segment
-    const int64_t x0 = (int64_t)gw * sigma;
+    const int64_t gw = blockIdx.x * 4 + wave;  // this wave's segment
+    const int64_t x0 = gw * sigma;
     if (x0 >= W) return;  // no barrier follows
     const int n_total = (int)(min(W, x0 + sigma) - x0);  // sub-pages this wave attends
+    char* const slot = smem + wave * Lay::kBytes;
 
-    Stream st(a, s_pref, s_len, lane);
-    RowTiles<T, D, 1> rows(a, lane, 0);
+    Stream st(a, table, s_pref, s_len, lane);
+    Rows rows(a, lane, 0);
     Cur cc = st.seek(x0);  // the sub-page being attended
     Cur pc = cc;           // the next sub-page to fetch
     st.prefetch_table(cc);
     st.template fetch<KS>(st.locate(cc), slot, 0, 1, cc.j < cc.nc);
     if (n_total > 1) {
         st.step(pc);
-        st.prefetch_table(pc);
+        st.prefetch_table(pc);  // its table entry, one fetch ahead
     }
     rows.load_q(cc.b, cc.kh);
     rows.reset();
@@ -551,9 +547,9 @@ void decode_mfma(SplitArgs<T> a) {
     for (int i = 0; i < n_total; ++i) {
         const bool more = i + 1 < n_total;  // pc is the next sub-page of this wave
         if (cc.j == 0 && lane == 0 && a.meta) record_segments(a, st, cc, sigma);
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);  // sub-page i, table window, Q have landed
-        // Read the whole slot out, then refill it with the next sub-page at once:
-        // the fetch is in flight during all of this sub-page's arithmetic.
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);  // sub-page i and Q have landed
+        // Read the slot out, then refill it at once: the next fetch is in
+        // flight during this sub-page's arithmetic.
         u32x4_t kop[KS];
         unsigned vq[NP][4];
         rows.read_k(slot, kop);
@@ -591,7 +587,7 @@ constexpr int kRing = 4;  // sub-page slots per workgroup
 
 template <typename T, int D, int BS, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void decode_mfma_coop(SplitArgs<T> a) {
+void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table) {
     using Lay = SlotLayout<T, D>;
     using Stream = SubPageStream<T, D, BS>;
     using Cur = typename Stream::Cur;
@@ -617,19 +613,19 @@ void decode_mfma_coop(SplitArgs<T> a) {
     const bool issues = wave < NWI;  // this wave loads instructions wave, wave + NWI, ...
     const bool has_rows = 16 * wave < a.R;
 
-    Stream st(a, s_pref, s_len, lane);
+    Stream st(a, table, s_pref, s_len, lane);
     RowTiles<T, D, 1> rows(a, lane, wave);
     Cur cc = st.seek(x0);
     Cur pc = cc;  // next sub-page to fetch: kRing - 1 ahead of cc once primed
     // prime the ring: sub-pages 0 .. kRing-2 into slots 0 .. kRing-2
     int primed = 0;
     for (; primed < kRing - 1 && primed < n_total; ++primed) {
-        st.template prefetch_table<true>(pc);
+        st.prefetch_table(pc);
         const typename Stream::Src s0 = st.locate(pc);
         if (issues) st.template fetch<IPW>(s0, smem + primed * Lay::kBytes, wave, NWI, pc.j < pc.nc);
         if (primed + 1 < n_total) st.step(pc);
     }
-    st.template prefetch_table<true>(pc);
+    st.prefetch_table(pc);
     if (has_rows) rows.load_q(cc.b, cc.kh);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the ring is primed; Q and tables are in
     rows.reset();
@@ -660,7 +656,7 @@ void decode_mfma_coop(SplitArgs<T> a) {
                 st.template fetch<IPW>(sn, smem + (nxt % kRing) * Lay::kBytes, wave, NWI, pc.j < pc.nc);
             if (nxt + 1 < n_total) {
                 st.step(pc);
-                st.template prefetch_table<true>(pc);
+                st.prefetch_table(pc);
             }
         }
         const char* slot = smem + (i % kRing) * Lay::kBytes;

@@ -142,21 +142,26 @@ struct Plan {
 // R <= 16 (decode_mfma), else one wave per row tile, 2 or 4 (decode_mfma_coop).
 int mfma_group_waves(int row_tiles) { return row_tiles <= 2 ? (row_tiles == 1 ? 4 : 2) : 4; }
 
-// Dynamic LDS of a matrix-core workgroup: its sub-page slots (4: one per wave,
-// or the ring of the cooperative kernel) plus the per-sequence prefix of the
-// split and the sequence lengths.
+// Dynamic LDS of a matrix-core workgroup: its sub-page slots (one per wave for
+// R <= 16; the ring for the cooperative kernel) and the per-sequence prefix of
+// the split and the sequence lengths.
 size_t mfma_lds_bytes(const pa_problem* p, int row_tiles) {
-    const size_t slot = p->head_dim == 64 ? pa::SlotLayout<_Float16, 64>::kBytes
-                                           : pa::SlotLayout<_Float16, 128>::kBytes;
-    const size_t slots = row_tiles == 1 ? 4 : pa::kRing;
-    return slots * slot + (2 * (size_t)p->batch + 1) * sizeof(int);
+    size_t group;
+    if (row_tiles == 1)
+        group = 4 * (size_t)(p->head_dim == 64 ? pa::SlotLayout<_Float16, 64>::kBytes
+                                               : pa::SlotLayout<_Float16, 128>::kBytes);
+    else
+        group = pa::kRing * (size_t)(p->head_dim == 64 ? pa::SlotLayout<_Float16, 64>::kBytes
+                                                       : pa::SlotLayout<_Float16, 128>::kBytes);
+    return group + (2 * (size_t)p->batch + 1) * sizeof(int);
 }
 
 // Segments one CU holds at once: waves (R <= 16) or workgroups (R > 16).
 int mfma_segments_per_cu(const pa_problem* p, int row_tiles) {
     const int nw = mfma_group_waves(row_tiles);
+    const int waves = kMfmaWavesPerCu;
     int groups = (int)(kLdsPerCu / mfma_lds_bytes(p, row_tiles));
-    if (groups > kMfmaWavesPerCu / nw) groups = kMfmaWavesPerCu / nw;
+    if (groups > waves / nw) groups = waves / nw;
     return row_tiles == 1 ? 4 * groups : groups;
 }
 
@@ -315,14 +320,17 @@ void launch_valu(const Plan& pl, dim3 grid, hipStream_t s, const pa::DecodeArgs<
 }
 
 template <typename T, int D, int BS>
-void launch_mfma(const Plan& pl, size_t lds, hipStream_t s, const pa::SplitArgs<T>& a) {
+void launch_mfma(const Plan& pl, size_t lds, hipStream_t s, const pa::SplitArgs<T>& a,
+                 const int32_t* table) {
     if (pl.rt == 1) {
         const dim3 grid((unsigned)ceil_div(pl.parts, 4));
-        hipLaunchKernelGGL((pa::decode_mfma<T, D, BS>), grid, dim3(256), lds, s, a);
+        hipLaunchKernelGGL((pa::decode_mfma<T, D, BS>), grid, dim3(256), lds, s, a, table);
     } else if (mfma_group_waves(pl.rt) == 2) {
-        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2>), dim3(pl.parts), dim3(128), lds, s, a);
+        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2>), dim3(pl.parts), dim3(128), lds, s, a,
+                           table);
     } else {
-        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 4>), dim3(pl.parts), dim3(256), lds, s, a);
+        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 4>), dim3(pl.parts), dim3(256), lds, s, a,
+                           table);
     }
 }
 
@@ -363,11 +371,11 @@ void launch_pass1_mfma(const pa_problem* p, const Plan& pl, hipStream_t s,
     a.qscale = d.qscale;
     const size_t lds = mfma_lds_bytes(p, pl.rt);
     if (p->head_dim == 64) {
-        if (p->block_size == 16) launch_mfma<T, 64, 16>(pl, lds, s, a);
-        else launch_mfma<T, 64, 32>(pl, lds, s, a);
+        if (p->block_size == 16) launch_mfma<T, 64, 16>(pl, lds, s, a, d.block_table);
+        else launch_mfma<T, 64, 32>(pl, lds, s, a, d.block_table);
     } else {
-        if (p->block_size == 16) launch_mfma<T, 128, 16>(pl, lds, s, a);
-        else launch_mfma<T, 128, 32>(pl, lds, s, a);
+        if (p->block_size == 16) launch_mfma<T, 128, 16>(pl, lds, s, a, d.block_table);
+        else launch_mfma<T, 128, 32>(pl, lds, s, a, d.block_table);
     }
 }
 

@@ -67,6 +67,24 @@ def test_config_full_size(cfg):
     print(f"[gpu] {W.CONFIGS[cfg].name}: max-abs error {err:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("cfg", [1, 4], ids=["llama3_8b_decode", "ragged_serving"])
+def test_repeated_calls_reuse_the_workspace(cfg):
+    # One Decoder (problem, workspace, output) called again and again, as a
+    # serving loop does: every call must match the oracle.
+    w = W.make_workload(W.CONFIGS[cfg], device=DEV)
+    table = torch.from_numpy(w.block_table).to(DEV)
+    lens = torch.from_numpy(w.context_lens).to(DEV)
+    dec = pa.Decoder(w.q, w.k_pool, table, max_context_len=w.max_context_len,
+                     causal=w.spec.causal)
+    assert dec.partitions > 1
+    expect = ref(w)
+    for rep in range(4):
+        print(f"[gpu] {w.spec.name} repeat {rep}", flush=True)
+        out = dec(w.q, w.k_pool, w.v_pool, table, lens, w.new_k, w.new_v, w.scale)
+        torch.cuda.synchronize()
+        check(w, out, expect)
+
+
 # ---------------------------------------------------------------------------
 # Shrunken variants: several pages per wave, ragged tails, several partitions
 # ---------------------------------------------------------------------------
