@@ -12,10 +12,9 @@
 //   softmax fp32 on the VALU; the D-layout of S^T (key 4*(l/16)+i, row l%16)
 //           is exactly the A layout of the next product, so P stays in lane
 //   output  O[16 rows x 16 d] += P V per 16 d (Mfma<T>::pv);
-//           B = V: lane l needs keys 4*(l/16)..+3 at one d. Each lane reads the
-//           dword (d, d+1) of its 4 keys and v_perm splits it into the
-//           operands of two d-columns, so output tile 2j holds d = 32j + 2c and
-//           tile 2j+1 holds d = 32j + 2c + 1 for column c.
+//           B = V: lane l needs keys 4*(l/16)..+3 at d = 16t + l%16; one
+//           transposing LDS read (ds_read_b64_tr_b16) of the row-major V slot
+//           delivers exactly that, so output tile t holds d = 16t + l%16.
 // The reference max moves only when a score exceeds it by more than 2^kSlack
 // (probabilities stay <= 256), so the accumulators are rescaled almost never.
 // Sub-pages are staged through LDS by buffer-to-LDS loads (no VGPRs held by
@@ -138,13 +137,13 @@ struct SplitArgs {
 
 // LDS layout of one sub-page slot (16 keys), filled by row-coalesced 16-byte
 // buffer-to-LDS loads; each load instruction fills 1 KB (kKeysPerOp whole
-// rows of 2*D bytes).
-//  K: rows back to back; chunk c (16 bytes) of key k sits at position
-//     c ^ swz(k), so a K-operand read (keys 0..15, one chunk) spreads over all
-//     banks. Offsets depend on the key: one fetch offset per instruction.
-//  V: plain rows, with kVPad bytes after each instruction's 1 KB, so a
-//     V-operand read (keys 4*g + j, g = 0..3, one dword column) lands on
-//     distinct banks for the four g; addresses are one base plus constants.
+// rows of 2*D bytes). K rows, then V rows, back to back; the 16-byte chunk c of
+// key row k sits at position c ^ swz(k) (K) or c ^ vswz(k) (V), which puts the
+// operand reads on distinct banks (the minimum number of passes):
+//  K: a K-operand read takes one chunk of keys 0..15: swz(k) spreads them.
+//  V: a transposing read (ds_read_b64_tr_b16) takes 8 bytes of 16 rows for
+//     one 16-column tile: vswz(k) = 2 * (row line % (kChunks/2)) moves the
+//     32-byte column pair of consecutive row lines apart.
 template <typename T, int D>
 struct SlotLayout {
     static constexpr int kRowBytes = D * (int)sizeof(T);
@@ -152,14 +151,19 @@ struct SlotLayout {
     static constexpr int kKeysPerOp = 1024 / kRowBytes;  // rows per load instruction
     static constexpr int kOps = 16 / kKeysPerOp;         // load instructions per half
     static constexpr int kRowsPerBank = 256 / kRowBytes; // rows sharing one 256-byte bank line
-    static constexpr int kVPad = 64;
     static constexpr int kKBytes = 16 * kRowBytes;
-    static constexpr int kVBytes = kOps * (1024 + kVPad);
-    static constexpr int kBytes = kKBytes + kVBytes;
+    static constexpr int kBytes = 2 * kKBytes;
     __device__ static __forceinline__ int swz(int k) { return (k / kRowsPerBank) % kChunks; }
+    __device__ static __forceinline__ int vswz(int k) {
+        return 2 * ((k / kRowsPerBank) % (kChunks / 2));
+    }
     // K: byte offset of logical chunk c of key k
     __device__ static __forceinline__ int k_addr(int k, int c) {
         return k * kRowBytes + ((c ^ swz(k)) << 4);
+    }
+    // V (from the V half): byte offset of logical chunk c of key k
+    __device__ static __forceinline__ int v_addr(int k, int c) {
+        return k * kRowBytes + ((c ^ vswz(k)) << 4);
     }
     // K: the offset lane l fetches in instruction i is k_fetch_base ^ (64*i).
     // For both row sizes the instruction-i row of lane l has swz = 4*i + l/16,
@@ -168,13 +172,11 @@ struct SlotLayout {
     __device__ static __forceinline__ int k_fetch_base(int lane, int tbytes) {
         return (lane / kChunks) * tbytes + (((lane % kChunks) ^ (lane >> 4)) << 4);
     }
-    // V: offset that lane l fetches in every instruction (plain rows)
-    __device__ static __forceinline__ int v_fetch_off(int lane, int tbytes) {
-        return (lane / kChunks) * tbytes + ((lane % kChunks) << 4);
-    }
-    // V: byte offset (from the V half) of element d of key k
-    __device__ static __forceinline__ int v_addr(int k, int d) {
-        return (k / kKeysPerOp) * (1024 + kVPad) + (k % kKeysPerOp) * kRowBytes + d * (int)sizeof(T);
+    // V: offset (beyond the instruction's first row) that lane l fetches in
+    // instruction i: chunk (l % kChunks) ^ vswz(k) of key k = i*kKeysPerOp + l/kChunks
+    __device__ static __forceinline__ int v_fetch_off(int i, int lane, int tbytes) {
+        const int k = kKeysPerOp * i + lane / kChunks;
+        return (lane / kChunks) * tbytes + (((lane % kChunks) ^ vswz(k)) << 4);
     }
 };
 
@@ -204,7 +206,7 @@ struct SubPageStream {
     const int* s_pref;
     const int* s_len;
     int KV, NQ, nnew, tbytes, lane;
-    int kfb, vfb;  // per-lane fetch offsets of a cached sub-page
+    int kfb;  // per-lane K fetch offset of a cached sub-page (instruction 0)
     int pre_b = -1, pre_page = 0, pre_phys = 0;  // table entry loaded ahead
 
     __device__ __forceinline__ SubPageStream(const SplitArgs<T>& args,
@@ -213,7 +215,6 @@ struct SubPageStream {
         : a(args), table(tab), s_pref(pref), s_len(lens), KV(args.g.KV), NQ(args.g.NQ),
           nnew((args.g.NQ + 15) / 16), tbytes(args.g.KV * D * (int)sizeof(T)), lane(ln) {
         kfb = Lay::k_fetch_base(lane, tbytes);
-        vfb = Lay::v_fetch_off(lane, tbytes);
     }
     __device__ __forceinline__ void enter_seq(Cur& c) const {
         c.nsub = s_pref[c.b + 1] - s_pref[c.b];
@@ -293,9 +294,10 @@ struct SubPageStream {
 #pragma unroll
             for (int t = 0; t < COUNT; ++t) {
                 const int i = i0 + istep * t;
+                const int voff = Lay::v_fetch_off(i, lane, tbytes);
                 const int soff = i * Lay::kKeysPerOp * tbytes;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    vr, (lds_void*)(v_lds + i * (1024 + Lay::kVPad)), 16, vfb, soff, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(v_lds + i * 1024), 16,
+                                                         voff, soff, 0, 0);
             }
         } else {
             const __amdgpu_buffer_rsrc_t kr = make_rsrc(s.k, (s.rmax + 1) * kNewStride);
@@ -308,11 +310,11 @@ struct SubPageStream {
                 const int row = Lay::kKeysPerOp * i + ln / Lay::kChunks;
                 const int rc = min(row, s.rmax);
                 const int koff = rc * kNewStride + (((ln % Lay::kChunks) ^ Lay::swz(row)) << 4);
-                const int voff = rc * kNewStride + ((ln % Lay::kChunks) << 4);
+                const int voff = rc * kNewStride + (((ln % Lay::kChunks) ^ Lay::vswz(row)) << 4);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(k_lds + i * 1024), 16,
                                                          koff, 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    vr, (lds_void*)(v_lds + i * (1024 + Lay::kVPad)), 16, voff, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(v_lds + i * 1024), 16,
+                                                         voff, 0, 0, 0);
             }
         }
     }
@@ -329,7 +331,7 @@ struct RowTiles {
     using Lay = SlotLayout<T, D>;
     static constexpr int KS = D / 32;  // score MFMA steps over d
     static constexpr int NT = D / 16;  // output tiles over d
-    static constexpr int NP = D / 32;  // output tile pairs
+    static constexpr int NP = D / 32;  // load instructions per half (K or V)
 
     const SplitArgs<T>& a;
     int lane, c16, g16, rt0;
@@ -369,20 +371,37 @@ struct RowTiles {
             for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     }
-    // K operands and V dwords of one sub-page, read from a slot.
+    // K operands of one sub-page, read from a slot (256-byte aligned). Chunk
+    // 4*kk + g16 of key c16 sits at c16*R + (((g16 ^ swz(c16)) ^ 4*kk) << 4), so
+    // the address of step kk is one base XOR (kk << 6); the base is recomputed
+    // per call (opaque to the optimizer) rather than kept as KS live registers.
     __device__ __forceinline__ void read_k(const char* slot, u32x4_t (&kop)[KS]) const {
+        uintptr_t base = reinterpret_cast<uintptr_t>(slot) + Lay::k_addr(c16, g16);
+        asm volatile("" : "+v"(base));
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
-            kop[kk] = *reinterpret_cast<const u32x4_t*>(slot + Lay::k_addr(c16, 4 * kk + g16));
+            kop[kk] = *reinterpret_cast<const u32x4_t*>(base ^ (uintptr_t)(kk << 6));
     }
-    __device__ __forceinline__ void read_v(const char* slot, unsigned (&vq)[NP][4]) const {
-        // this lane's dwords of keys 4*g16 + 0..3 at d = 32*np + 2*c16
-        const char* const v_rd = slot + Lay::kKBytes + Lay::v_addr(4 * g16, 2 * c16);
+    // V operands of the NT output tiles: B of O += P V for tile t is V[key
+    // 4*g16 + j][d = 16*t + c16], j = 0..3, read with one transposing LDS read:
+    // within a 16-lane group, lane s supplies row 4*g16 + s/4, columns
+    // 16*t + 4*(s%4) .. +3, and lane c16 receives column c16 of the 4 rows.
+    // (Chunk 2*t + h of a row sits at ((2*t + h) ^ vswz) << 4 = base ^ (t << 5):
+    // one base per call, recomputed per call like read_k's.)
+    __device__ __forceinline__ void read_v(const char* slot, u32x2_t (&vt)[NT]) const {
+        typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+        const int s = c16;
+        const int row = 4 * g16 + s / 4;
+        uintptr_t base = reinterpret_cast<uintptr_t>(slot) + Lay::kKBytes +
+                         Lay::v_addr(row, (s & 3) >> 1) + 8 * (s & 1);
+        asm volatile("" : "+v"(base));
 #pragma unroll
-        for (int np = 0; np < NP; ++np)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                vq[np][jj] = *reinterpret_cast<const unsigned*>(v_rd + Lay::v_addr(jj, 32 * np));
+        for (int t = 0; t < NT; ++t) {
+            const uintptr_t p = base ^ (uintptr_t)(t << 5);
+            const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(__attribute__((address_space(3))) char*)(uintptr_t)(uint32_t)p);
+            vt[t] = __builtin_bit_cast(u32x2_t, v);
+        }
     }
     // Visible-key limits of one sub-page: keys [0, valid) exist; for new rows
     // (is_new) key tau is new row t0 + tau, visible to a query row by causality.
@@ -427,28 +446,19 @@ struct RowTiles {
         }
     }
     // O += P V; keys [valid, 16) are zeroed first (their slot rows may hold NaN).
-    __device__ __forceinline__ void accumulate(unsigned (&vq)[NP][4], int valid) {
+    // Lane key 4*g16 + j is 16-bit half j of the lane's two dwords.
+    __device__ __forceinline__ void accumulate(u32x2_t (&vt)[NT], int valid) {
         if (valid < 16) {
+            const int k0 = 4 * g16;
+            const unsigned m0 = (k0 < valid ? 0xffffu : 0u) | (k0 + 1 < valid ? 0xffff0000u : 0u);
+            const unsigned m1 = (k0 + 2 < valid ? 0xffffu : 0u) | (k0 + 3 < valid ? 0xffff0000u : 0u);
 #pragma unroll
-            for (int np = 0; np < NP; ++np)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    if (4 * g16 + jj >= valid) vq[np][jj] = 0u;
+            for (int t = 0; t < NT; ++t) vt[t] = u32x2_t{vt[t][0] & m0, vt[t][1] & m1};
         }
 #pragma unroll
-        for (int np = 0; np < NP; ++np) {
-            const unsigned* v = vq[np];
-            // operands of output tiles 2*np (even d) and 2*np+1 (odd d)
-            const u32x2_t vlo = u32x2_t{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u),
-                                        __builtin_amdgcn_perm(v[3], v[2], 0x05040100u)};
-            const u32x2_t vhi = u32x2_t{__builtin_amdgcn_perm(v[1], v[0], 0x07060302u),
-                                        __builtin_amdgcn_perm(v[3], v[2], 0x07060302u)};
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) {
-                acc[rt][2 * np] = M::pv(phi[rt], plo[rt], vlo, acc[rt][2 * np]);
-                acc[rt][2 * np + 1] = M::pv(phi[rt], plo[rt], vhi, acc[rt][2 * np + 1]);
-            }
-        }
+            for (int rt = 0; rt < NRT; ++rt) acc[rt][t] = M::pv(phi[rt], plo[rt], vt[t], acc[rt][t]);
     }
     // The unit's finished output (whole unit attended here), or this piece's
     // state for the combine (workspace slot u + segment).
@@ -466,17 +476,16 @@ struct RowTiles {
                 const int r = 16 * (rt0 + rt) + 4 * g16 + i;  // output row held in acc[rt][*][i]
                 const float l_r = __shfl(lrow, 4 * g16 + i);
                 if (r >= R) continue;
+                // tile t holds d = 16*t + c16
                 if (whole) {
                     const float inv = l_r != 0.f ? 1.f / l_r : 0.f;
-                    unsigned* dst = reinterpret_cast<unsigned*>(a.out + (g0 + r) * D + 2 * c16);
+                    T* dst = a.out + (g0 + r) * D + c16;
 #pragma unroll
-                    for (int np = 0; np < NP; ++np)
-                        dst[16 * np] = M::pack2(acc[rt][2 * np][i] * inv, acc[rt][2 * np + 1][i] * inv);
+                    for (int t = 0; t < NT; ++t) Elem<T>::store(dst + 16 * t, acc[rt][t][i] * inv);
                 } else {
-                    f32x2_t* dst = reinterpret_cast<f32x2_t*>(a.ws_o + (slot * R + r) * D + 2 * c16);
+                    float* dst = a.ws_o + (slot * R + r) * D + c16;
 #pragma unroll
-                    for (int np = 0; np < NP; ++np)
-                        dst[16 * np] = f32x2_t{acc[rt][2 * np][i], acc[rt][2 * np + 1][i]};
+                    for (int t = 0; t < NT; ++t) dst[16 * t] = acc[rt][t][i];
                 }
             }
             const int row = 16 * (rt0 + rt) + c16;
@@ -510,11 +519,11 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table) {
     using Stream = SubPageStream<T, D, BS>;
     using Rows = RowTiles<T, D, 1>;
     using Cur = typename Stream::Cur;
-    constexpr int KS = D / 32, NP = D / 32;
+    constexpr int KS = D / 32;
     static_assert(D % 32 == 0 && BS % 16 == 0 && Lay::kOps == KS, "shape");
 
     // LDS: per wave one slot, then the prefix and lengths.
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    extern __shared__ __attribute__((aligned(1024))) char smem[];  // slots start 1 KiB aligned (XOR addressing)
     int* s_pref = reinterpret_cast<int*>(smem + 4 * Lay::kBytes);
     int* s_len = s_pref + a.g.B + 1;
     build_prefix(a.context_lens, a.g, s_pref, s_len);
@@ -551,9 +560,9 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table) {
         // Read the slot out, then refill it at once: the next fetch is in
         // flight during this sub-page's arithmetic.
         u32x4_t kop[KS];
-        unsigned vq[NP][4];
+        u32x2_t vt[D / 16];
         rows.read_k(slot, kop);
-        rows.read_v(slot, vq);
+        rows.read_v(slot, vt);
         if (more) {
             const typename Stream::Src sn = st.locate(pc);
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // slot read out
@@ -566,7 +575,7 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table) {
         rows.limits(valid, is_new, t0, lim);
         rows.scores(kop, lim);
         if (more && pc.j == 0) rows.load_q(pc.b, pc.kh);  // Q of the next unit
-        rows.accumulate(vq, valid);
+        rows.accumulate(vt, valid);
         if (cc.j + 1 == cc.nsub || !more) {
             rows.emit(cc.b, cc.kh, gw, piece_from_start && cc.j + 1 == cc.nsub);
             rows.reset();
@@ -583,21 +592,33 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table) {
 }
 
 // ---- NW waves per segment, one row tile each, sharing a ring of sub-pages ----
-constexpr int kRing = 4;  // sub-page slots per workgroup
+// Waits until at most `ahead` (<= MAXA) sub-pages' loads of OPS each are outstanding.
+template <int OPS, int MAXA>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+    if constexpr (MAXA > 0) {
+        if (ahead >= MAXA) {
+            __builtin_amdgcn_s_waitcnt(wait_vm(OPS * MAXA));
+            return;
+        }
+        wait_ahead<OPS, MAXA - 1>(ahead);
+    } else {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
+}
 
-template <typename T, int D, int BS, int NW>
+template <typename T, int D, int BS, int NW, int kRing>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table) {
     using Lay = SlotLayout<T, D>;
     using Stream = SubPageStream<T, D, BS>;
     using Cur = typename Stream::Cur;
-    constexpr int KS = D / 32, NP = D / 32;
+    constexpr int KS = D / 32;
     constexpr int NWI = NW < KS ? NW : KS;  // waves that issue loads
     constexpr int IPW = KS / NWI;           // instructions per half per issuing wave
     static_assert(D % 32 == 0 && BS % 16 == 0 && Lay::kOps == KS && KS % NWI == 0, "shape");
     static_assert(kRing >= 3, "ring");
 
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    extern __shared__ __attribute__((aligned(1024))) char smem[];  // slots start 1 KiB aligned (XOR addressing)
     int* s_pref = reinterpret_cast<int*>(smem + kRing * Lay::kBytes);
     int* s_len = s_pref + a.g.B + 1;
     build_prefix(a.context_lens, a.g, s_pref, s_len);
@@ -635,9 +656,7 @@ void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table) {
         if (cc.j == 0 && lane == 0 && wave == 0 && a.meta) record_segments(a, st, cc, sigma);
         // this wave's loads of sub-page i have landed (later ones may be in flight)
         if (issues) {
-            if (ahead >= 2) __builtin_amdgcn_s_waitcnt(wait_vm(2 * IPW * 2));
-            else if (ahead == 1) __builtin_amdgcn_s_waitcnt(wait_vm(2 * IPW));
-            else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+            wait_ahead<2 * IPW, kRing - 2>(ahead);
         } else {
             __builtin_amdgcn_s_waitcnt(kWaitVm0);  // Q and the table window
         }
@@ -666,13 +685,13 @@ void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table) {
         const bool unit_ends = cc.j + 1 == cc.nsub || i + 1 == n_total;
         if (has_rows) {
             u32x4_t kop[KS];
-            unsigned vq[NP][4];
+            u32x2_t vt[D / 16];
             rows.read_k(slot, kop);
-            rows.read_v(slot, vq);
+            rows.read_v(slot, vt);
             int lim[1];
             rows.limits(valid, is_new, t0, lim);
             rows.scores(kop, lim);
-            rows.accumulate(vq, valid);
+            rows.accumulate(vt, valid);
             if (unit_ends) {
                 rows.emit(cc.b, cc.kh, seg, piece_from_start && cc.j + 1 == cc.nsub);
                 rows.reset();

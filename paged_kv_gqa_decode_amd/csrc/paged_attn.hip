@@ -138,6 +138,12 @@ struct Plan {
     int n_tiles;  // workgroups per KV head along the rows (1 for MFMA)
 };
 
+// Ring slots per workgroup of the cooperative kernel (R > 16).
+#ifndef PA_COOP_RING
+#define PA_COOP_RING 4
+#endif
+constexpr int kCoopRing = PA_COOP_RING;
+
 // Waves per workgroup of the matrix-core family: 4 single-wave segments for
 // R <= 16 (decode_mfma), else one wave per row tile, 2 or 4 (decode_mfma_coop).
 int mfma_group_waves(int row_tiles) { return row_tiles <= 2 ? (row_tiles == 1 ? 4 : 2) : 4; }
@@ -151,7 +157,7 @@ size_t mfma_lds_bytes(const pa_problem* p, int row_tiles) {
         group = 4 * (size_t)(p->head_dim == 64 ? pa::SlotLayout<_Float16, 64>::kBytes
                                                : pa::SlotLayout<_Float16, 128>::kBytes);
     else
-        group = pa::kRing * (size_t)(p->head_dim == 64 ? pa::SlotLayout<_Float16, 64>::kBytes
+        group = kCoopRing * (size_t)(p->head_dim == 64 ? pa::SlotLayout<_Float16, 64>::kBytes
                                                        : pa::SlotLayout<_Float16, 128>::kBytes);
     return group + (2 * (size_t)p->batch + 1) * sizeof(int);
 }
@@ -326,10 +332,10 @@ void launch_mfma(const Plan& pl, size_t lds, hipStream_t s, const pa::SplitArgs<
         const dim3 grid((unsigned)ceil_div(pl.parts, 4));
         hipLaunchKernelGGL((pa::decode_mfma<T, D, BS>), grid, dim3(256), lds, s, a, table);
     } else if (mfma_group_waves(pl.rt) == 2) {
-        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2>), dim3(pl.parts), dim3(128), lds, s, a,
+        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2, kCoopRing>), dim3(pl.parts), dim3(128), lds, s, a,
                            table);
     } else {
-        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 4>), dim3(pl.parts), dim3(256), lds, s, a,
+        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 4, kCoopRing>), dim3(pl.parts), dim3(256), lds, s, a,
                            table);
     }
 }
