@@ -87,22 +87,24 @@ __global__ __launch_bounds__(256) void combine_partitions(CombineArgs<T> a) {
 
 namespace pa {
 
-// Merge for the balanced per-wave split (split.hpp): unit u = b*KV + h/G has one
-// state per segment s in [s0, s1] that overlaps it, stored in slot u + s; pass 1
-// recorded (s0, s1) per unit. Units inside one segment were finished by pass 1.
+// Merge for the balanced split (split.hpp): (sequence b, KV head kh) has one
+// state per group g in [g0, g1] that overlaps sequence b, stored in slot
+// (b + g)*KV + kh; pass 1 recorded (g0, g1) per sequence. Sequences inside one
+// group were finished by pass 1.
 // The merge is PARTIALS_REDUCE of the docs.rs page "onnxruntime-ep-mlx 0.31.1:
-// src/ops/paged_attention.rs" in base 2: out = sum_s 2^(m_s - M) o_s /
-// sum_s 2^(m_s - M) l_s with M = max_s m_s.
-// WPR waves share one output row (WPR = 1: a workgroup takes 4 rows of a unit;
-// WPR = 4: one row, its pieces dealt to 4 waves in contiguous runs and the four
-// partial merges combined through LDS). Each wave loads the (m, l) of up to 64
-// pieces lane-parallel and the partial outputs of up to kBatch pieces at once,
-// so a row costs two dependent memory latencies after the metadata.
+// src/ops/paged_attention.rs" in base 2: out = sum_g 2^(m_g - M) o_g /
+// sum_g 2^(m_g - M) l_g with M = max_g m_g.
+// WPR waves share one output row (WPR = 1: a workgroup takes 4 rows of a
+// (sequence, head); WPR = 4: one row, its pieces dealt to 4 waves in contiguous
+// runs and the four partial merges combined through LDS). Each wave loads the
+// (m, l) of up to 64 pieces lane-parallel and the partial outputs of up to
+// kBatch pieces at once, so a row costs two dependent memory latencies after
+// the metadata.
 template <typename T>
 struct SplitCombineArgs {
     const float* ws_o;     // [slots][R][D]
     const float* ws_ml;    // [slots][R][2]
-    const int32_t* meta;   // [B*KV][2]  first and last segment of each unit
+    const int32_t* meta;   // [B][2]     first and last group of each sequence
     T* out;
     int KV, H, NQ, R;
 };
@@ -118,19 +120,21 @@ __global__ __launch_bounds__(256) void combine_split(SplitCombineArgs<T> a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int R = a.R;
     const int tiles = (R + RPB - 1) / RPB;
-    const int64_t u = blockIdx.x / tiles;
+    const int64_t u = blockIdx.x / tiles;  // b * KV + kh
     const int rho = (int)(blockIdx.x % tiles) * RPB + (WPR == 1 ? wave : 0);
-    const int s0 = a.meta[2 * u], s1 = a.meta[2 * u + 1];
+    const int64_t b = u / a.KV;
+    const int s0 = a.meta[2 * b], s1 = a.meta[2 * b + 1];
     if (s0 == s1) return;  // finished by pass 1 (whole workgroup)
     const int n = s1 - s0 + 1;
-    const bool active = rho < R;  // WPR = 1: the unit's last tile may be short
+    const bool active = rho < R;  // WPR = 1: the last tile of rows may be short
     // this wave's pieces [p0, p1) of the row
     const int per_w = (n + WPR - 1) / WPR;
     const int p0 = WPR == 1 ? 0 : min(n, wave * per_w), p1 = WPR == 1 ? n : min(n, p0 + per_w);
-    const int64_t first = u + s0;
+    const int64_t first = (b + s0) * a.KV + (u - b * a.KV);  // slot of piece g0
     const float* ml = a.ws_ml + (first * R + rho) * 2;
     const float* po = a.ws_o + (first * R + rho) * D + lane * PER;
-    const int64_t mstride = (int64_t)R * 2, ostride = (int64_t)R * D;
+    // consecutive groups of one (sequence, head) are KV slots apart
+    const int64_t mstride = (int64_t)a.KV * R * 2, ostride = (int64_t)a.KV * R * D;
 
     float M = kNegMax, Lw = 0.f;
     float acc[PER];

@@ -1,12 +1,12 @@
 // Pass 1 of paged GQA decode attention on the matrix cores (gfx950, fp16/bf16),
-// with the work cut into equal segments along the key axis (split.hpp).
+// with the work cut into equal groups along the sequence axis (split.hpp).
 //
 // Operation: docs.rs page "onnxruntime-ep-mlx 0.31.1: src/ops/paged_attention.rs",
 // VECTOR_BODY (scores, online softmax, accumulation) and VECTOR_PARTIALS.
 //
-// A segment is a run of 16-key sub-pages along the axis of all (sequence, KV
-// head) units; it is attended for all R = G*NQ query rows of each KV head in
-// row tiles of 16, so each K/V page is fetched from HBM once per GQA group:
+// One wave attends one KV head over one group's positions (16-key sub-pages)
+// for all R = G*NQ query rows of that head, in NRT row tiles of 16, so each
+// K/V page is fetched from HBM once per GQA group:
 //   scores  S^T[16 keys x 16 rows] = K Q^T  : v_mfma_f32_16x16x32 (D/32 steps);
 //           A = K: lane l holds key l%16, 8 elements of d; B = Q: row l%16
 //   softmax fp32 on the VALU; the D-layout of S^T (key 4*(l/16)+i, row l%16)
@@ -17,18 +17,16 @@
 //           delivers exactly that, so output tile t holds d = 16t + l%16.
 // The reference max moves only when a score exceeds it by more than 2^kSlack
 // (probabilities stay <= 256), so the accumulators are rescaled almost never.
-// Sub-pages are staged through LDS by buffer-to-LDS loads (no VGPRs held by
-// loads in flight); block-table entries are scalar loads issued one fetch ahead
-// of their use, so they never share the vector-memory counter with the loads
-// whose completion the kernels count.
-//   decode_mfma (R <= 16): one wave per segment with one LDS slot; the wave
-//     reads the slot into registers and refills it with the next sub-page
-//     before computing, so one sub-page per wave is in flight at all times.
-//     Four waves per SIMD.
-//   decode_mfma_coop (16 < R <= 64): NW waves per segment (one per row tile)
-//     share a ring of kRing slots; each wave loads its share of every
-//     sub-page, one barrier per sub-page publishes it, and kRing - 1
-//     sub-pages per workgroup are in flight.
+// Sub-pages are staged through a ring of NS LDS slots per wave by
+// buffer-to-LDS loads (no VGPRs held by loads in flight, non-temporal: the pool
+// is streamed once); block-table entries are scalar loads issued one fetch
+// ahead of their use, so they never share the vector-memory counter with the
+// loads whose completion the wave counts. The KV waves of a group read the
+// heads of the same pages at the same time (the pool keeps a token's heads
+// adjacent), which the memory system serves faster than one head at a time.
+// Occupancy: NRT = 1 runs 4 waves per SIMD with one slot each; NRT = 2, 2
+// waves with 2 slots; NRT = 4, 1 wave with 4 slots: the same bytes in flight
+// per CU (D = 128), with room for the larger accumulators.
 #pragma once
 
 #include <type_traits>
@@ -135,7 +133,7 @@ struct SplitArgs {
     T* out;
     float* ws_o;   // [slots][R][D]  unnormalised partial outputs
     float* ws_ml;  // [slots][R][2]  (max, sum) in base-2 units
-    int32_t* meta; // [B*KV][2]      first and last segment overlapping each unit
+    int32_t* meta; // [B][2]         first and last group overlapping each sequence
     SplitGeometry g;
     int H, causal, max_blocks, R;
     float qscale;  // scale * log2(e)
@@ -188,17 +186,18 @@ struct SlotLayout {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// ---- the stream of one segment's sub-pages: cursor, table windows, fetches ----
+// ---- the stream of one wave's sub-pages: cursor, table entries, fetches ----
 template <typename T, int D, int BS>
 struct SubPageStream {
     using Lay = SlotLayout<T, D>;
     static constexpr int KS = D / 32;    // load instructions per half (K or V)
     static constexpr int SUB = BS / 16;  // 16-key sub-pages per page
     static constexpr int kNewStride = D * (int)sizeof(T);  // row stride of new_k/new_v
+    static constexpr int kOps = 2 * KS;  // vector-memory instructions of one fetch
 
     struct Cur {
-        int b, kh, j;   // unit (b, kh), sub-page j of it
-        int nsub, nc;   // sub-pages of the unit; the first nc hold cached keys
+        int b, j;       // sequence b, its sub-page j (the head is the wave's)
+        int nsub, nc;   // sub-pages of the sequence; the first nc hold cached keys
         int L;          // cached keys of sequence b
     };
     struct Src {
@@ -211,14 +210,14 @@ struct SubPageStream {
     const int32_t* __restrict__ table;  // block table; entries are read with scalar loads
     const int* s_pref;
     const int* s_len;
-    int KV, NQ, nnew, tbytes, lane;
+    int KV, NQ, kh, nnew, tbytes, lane;
     int kfb;  // per-lane K fetch offset of a cached sub-page (instruction 0)
     int pre_b = -1, pre_page = 0, pre_phys = 0;  // table entry loaded ahead
 
     __device__ __forceinline__ SubPageStream(const SplitArgs<T>& args,
                                              const int32_t* __restrict__ tab, const int* pref,
-                                             const int* lens, int ln)
-        : a(args), table(tab), s_pref(pref), s_len(lens), KV(args.g.KV), NQ(args.g.NQ),
+                                             const int* lens, int head, int ln)
+        : a(args), table(tab), s_pref(pref), s_len(lens), KV(args.g.KV), NQ(args.g.NQ), kh(head),
           nnew((args.g.NQ + 15) / 16), tbytes(args.g.KV * D * (int)sizeof(T)), lane(ln) {
         kfb = Lay::k_fetch_base(lane, tbytes);
     }
@@ -231,16 +230,12 @@ struct SubPageStream {
         Cur c;
         c.b = split_find_seq(a.g, s_pref, x);
         enter_seq(c);
-        const int64_t off = x - (int64_t)KV * s_pref[c.b];
-        c.kh = (int)(off / c.nsub);
-        c.j = (int)(off - (int64_t)c.kh * c.nsub);
+        c.j = (int)(x - s_pref[c.b]);
         return c;
     }
-    __device__ __forceinline__ void step(Cur& c) const {  // next sub-page along the axis
+    __device__ __forceinline__ void step(Cur& c) const {  // next position along the axis
         if (++c.j < c.nsub) return;
         c.j = 0;
-        if (++c.kh < KV) return;
-        c.kh = 0;
         ++c.b;
         enter_seq(c);
     }
@@ -262,44 +257,40 @@ struct SubPageStream {
             const int page = c.j / SUB;
             const int64_t phys = (c.b == pre_b && page == pre_page) ? pre_phys : table_entry(c);
             const int64_t row0 = phys * BS + 16 * (c.j % SUB);
-            s.k = a.k_pool + (row0 * KV + c.kh) * D;
-            s.v = a.v_pool + (row0 * KV + c.kh) * D;
+            s.k = a.k_pool + (row0 * KV + kh) * D;
+            s.v = a.v_pool + (row0 * KV + kh) * D;
             s.rmax = 15;
         } else {
             const int t0 = 16 * (c.j - c.nc);
-            const int64_t r0 = ((int64_t)c.b * KV + c.kh) * NQ + t0;
+            const int64_t r0 = ((int64_t)c.b * KV + kh) * NQ + t0;
             s.k = a.new_k + r0 * D;
             s.v = a.new_v + r0 * D;
             s.rmax = min(15, NQ - t0 - 1);
         }
         return s;
     }
-    // Issues load instructions i = i0, i0 + istep, ... (< KS) of the K and the
-    // V half of sub-page `s` into the slot at `slot` (row-coalesced, 16 bytes
-    // per lane per instruction). Cached keys: pool row stride, no range check
-    // needed. New rows: all offsets in voffset and rows past nq clamped to the
-    // last one (they are masked later). (Offsets go in as plain int values: an
-    // array element or a dependent expression passed as is makes the host
+    // Issues the kOps load instructions of sub-page `s` (K half, then V half)
+    // into the slot at `slot` (row-coalesced, 16 bytes per lane per
+    // instruction). Cached keys: pool row stride, no range check needed,
+    // non-temporal. New rows: all offsets in voffset and rows past nq clamped to
+    // the last one (they are masked later). (Offsets go in as plain int values:
+    // an array element or a dependent expression passed as is makes the host
     // compilation pass drop the kernel's launch stub.)
-    template <int COUNT>
-    __device__ __forceinline__ void fetch(const Src& s, char* slot, int i0, int istep,
-                                          bool cached) const {
+    __device__ __forceinline__ void fetch(const Src& s, char* slot, bool cached) const {
         char* const k_lds = slot;
         char* const v_lds = slot + Lay::kKBytes;
         if (cached) {
             const __amdgpu_buffer_rsrc_t kr = make_rsrc(s.k, 16 * tbytes);
             const __amdgpu_buffer_rsrc_t vr = make_rsrc(s.v, 16 * tbytes);
 #pragma unroll
-            for (int t = 0; t < COUNT; ++t) {
-                const int i = i0 + istep * t;
+            for (int i = 0; i < KS; ++i) {
                 const int koff = kfb ^ (64 * i);
                 const int soff = i * Lay::kKeysPerOp * tbytes;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(k_lds + i * 1024), 16,
                                                          koff, soff, 0, kStreamPolicy);
             }
 #pragma unroll
-            for (int t = 0; t < COUNT; ++t) {
-                const int i = i0 + istep * t;
+            for (int i = 0; i < KS; ++i) {
                 const int voff = Lay::v_fetch_off(i, lane, tbytes);
                 const int soff = i * Lay::kKeysPerOp * tbytes;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(v_lds + i * 1024), 16,
@@ -311,8 +302,7 @@ struct SubPageStream {
             int ln = lane;
             asm volatile("" : "+v"(ln));  // computed here, not kept live across the loop
 #pragma unroll
-            for (int t = 0; t < COUNT; ++t) {
-                const int i = i0 + istep * t;
+            for (int i = 0; i < KS; ++i) {
                 const int row = Lay::kKeysPerOp * i + ln / Lay::kChunks;
                 const int rc = min(row, s.rmax);
                 const int koff = rc * kNewStride + (((ln % Lay::kChunks) ^ Lay::swz(row)) << 4);
@@ -323,10 +313,6 @@ struct SubPageStream {
                                                          voff, 0, 0, 0);
             }
         }
-    }
-    // axis position of the first sub-page of unit (c.b, c.kh)
-    __device__ __forceinline__ int64_t unit_start(const Cur& c) const {
-        return (int64_t)KV * s_pref[c.b] + (int64_t)c.kh * c.nsub;
     }
 };
 
@@ -356,16 +342,40 @@ struct RowTiles {
         const int G = a.H / a.g.KV;
         return ((int64_t)b * a.H + (int64_t)kh * G) * a.g.NQ;
     }
+    // Q rows of (b, kh) as the B operands, issued as inline assembly so that
+    // the compiler does not count them (it would wait for every pool load in
+    // flight before their first use); q_ready() must follow once they have
+    // landed. Rows past R load row R-1 (in bounds) and are zeroed by q_ready().
+    // The address is a scalar base (the unit's first row) plus a 32-bit
+    // per-lane byte offset, so no 64-bit per-lane pointer stays live.
     __device__ __forceinline__ void load_q(int b, int kh) {
-        const int64_t g0 = grow0(b, kh);
+        const uint64_t addr = reinterpret_cast<uint64_t>(a.q + grow0(b, kh) * D);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+        const T* base = reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
-            const int row = 16 * (rt0 + rt) + c16;
+            const int row = min(16 * (rt0 + rt) + c16, a.R - 1);
+            const uint32_t off = (uint32_t)(row * D + 8 * g16) * (uint32_t)sizeof(T);
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk)
-                qop[rt][kk] = row < a.R ? *reinterpret_cast<const u32x4_t*>(
-                                              a.q + (g0 + row) * D + 32 * kk + 8 * g16)
-                                        : u32x4_t{0, 0, 0, 0};
+                asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3"
+                             : "=v"(qop[rt][kk])
+                             : "v"(off), "s"(base), "i"(64 * kk)
+                             : "memory");
+        }
+    }
+    // After a wait that covers load_q's loads: makes their values visible to
+    // the code that follows and zeroes rows past R.
+    __device__ __forceinline__ void q_ready() {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            const bool live = 16 * (rt0 + rt) + c16 < a.R;
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                asm volatile("" : "+v"(qop[rt][kk]));
+                if (!live) qop[rt][kk] = u32x4_t{0, 0, 0, 0};
+            }
         }
     }
     __device__ __forceinline__ void reset() {
@@ -381,12 +391,16 @@ struct RowTiles {
     // 4*kk + g16 of key c16 sits at c16*R + (((g16 ^ swz(c16)) ^ 4*kk) << 4), so
     // the address of step kk is one base XOR (kk << 6); the base is recomputed
     // per call (opaque to the optimizer) rather than kept as KS live registers.
+    // (LDS-space pointers: a generic pointer would become a flat load, which
+    // the vector-memory counter also counts, so waiting for the operand would
+    // wait for every pool load in flight.)
     __device__ __forceinline__ void read_k(const char* slot, u32x4_t (&kop)[KS]) const {
-        uintptr_t base = reinterpret_cast<uintptr_t>(slot) + Lay::k_addr(c16, g16);
+        typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
+        uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(slot) + Lay::k_addr(c16, g16);
         asm volatile("" : "+v"(base));
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
-            kop[kk] = *reinterpret_cast<const u32x4_t*>(base ^ (uintptr_t)(kk << 6));
+            kop[kk] = *(lds_u32x4*)(uintptr_t)(base ^ (uint32_t)(kk << 6));
     }
     // V operands of the NT output tiles: B of O += P V for tile t is V[key
     // 4*g16 + j][d = 16*t + c16], j = 0..3, read with one transposing LDS read:
@@ -394,20 +408,28 @@ struct RowTiles {
     // 16*t + 4*(s%4) .. +3, and lane c16 receives column c16 of the 4 rows.
     // (Chunk 2*t + h of a row sits at ((2*t + h) ^ vswz) << 4 = base ^ (t << 5):
     // one base per call, recomputed per call like read_k's.)
+    // The reads are issued as inline assembly: the compiler treats its
+    // transposing-read builtin as possibly aliasing the buffer-to-LDS loads in
+    // flight and would wait for all of them first. The results are only valid
+    // after lds_wait(), which ties them to an LDS-counter wait.
     __device__ __forceinline__ void read_v(const char* slot, u32x2_t (&vt)[NT]) const {
-        typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
         const int s = c16;
         const int row = 4 * g16 + s / 4;
-        uintptr_t base = reinterpret_cast<uintptr_t>(slot) + Lay::kKBytes +
-                         Lay::v_addr(row, (s & 3) >> 1) + 8 * (s & 1);
+        uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(slot) + Lay::kKBytes +
+                        Lay::v_addr(row, (s & 3) >> 1) + 8 * (s & 1);
         asm volatile("" : "+v"(base));
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const uintptr_t p = base ^ (uintptr_t)(t << 5);
-            const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(__attribute__((address_space(3))) char*)(uintptr_t)(uint32_t)p);
-            vt[t] = __builtin_bit_cast(u32x2_t, v);
+            const uint32_t p = base ^ (uint32_t)(t << 5);
+            asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vt[t]) : "v"(p) : "memory");
         }
+    }
+    // Waits for every LDS read of this wave (and its scalar loads); values read
+    // by read_v are used only through this call's outputs.
+    __device__ __forceinline__ static void lds_wait(u32x2_t (&vt)[NT]) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(vt[t]));
     }
     // Visible-key limits of one sub-page: keys [0, valid) exist; for new rows
     // (is_new) key tau is new row t0 + tau, visible to a query row by causality.
@@ -466,12 +488,12 @@ struct RowTiles {
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) acc[rt][t] = M::pv(phi[rt], plo[rt], vt[t], acc[rt][t]);
     }
-    // The unit's finished output (whole unit attended here), or this piece's
-    // state for the combine (workspace slot u + segment).
-    __device__ __forceinline__ void emit(int b, int kh, int64_t segment, bool whole) const {
+    // The finished output of (b, kh) (its whole sequence attended here), or
+    // this piece's state for the combine (workspace slot (b + grp)*KV + kh).
+    __device__ __forceinline__ void emit(int b, int kh, int64_t grp, bool whole) const {
         const int64_t g0 = grow0(b, kh);
         const int R = a.R;
-        const int64_t slot = (int64_t)b * a.g.KV + kh + segment;
+        const int64_t slot = ((int64_t)b + grp) * a.g.KV + kh;
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
             float lrow = lsum[rt];
@@ -504,101 +526,9 @@ struct RowTiles {
     }
 };
 
-// The first piece of a unit records the segments [s0, s1] that overlap it.
-template <typename T, typename Stream>
-__device__ __forceinline__ void record_segments(const SplitArgs<T>& a, const Stream& st,
-                                                const typename Stream::Cur& c, int64_t sigma) {
-    const int64_t ustart = st.unit_start(c);
-    int32_t* mt = a.meta + 2 * ((int64_t)c.b * a.g.KV + c.kh);
-    mt[0] = (int32_t)(ustart / sigma);
-    mt[1] = (int32_t)((ustart + c.nsub - 1) / sigma);
-}
-
-// ---- one wave per segment (R <= 16) ----
-// The wave streams its segment's sub-pages through one LDS slot: it reads the
-// slot into registers and refills it with the next sub-page before computing,
-// so one sub-page per wave is in flight at all times (four waves per SIMD).
-template <typename T, int D, int BS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table) {
-    using Lay = SlotLayout<T, D>;
-    using Stream = SubPageStream<T, D, BS>;
-    using Rows = RowTiles<T, D, 1>;
-    using Cur = typename Stream::Cur;
-    constexpr int KS = D / 32;
-    static_assert(D % 32 == 0 && BS % 16 == 0 && Lay::kOps == KS, "shape");
-
-    // LDS: per wave one slot, then the prefix and lengths.
-    extern __shared__ __attribute__((aligned(1024))) char smem[];  // slots start 1 KiB aligned (XOR addressing)
-    int* s_pref = reinterpret_cast<int*>(smem + 4 * Lay::kBytes);
-    int* s_len = s_pref + a.g.B + 1;
-    build_prefix(a.context_lens, a.g, s_pref, s_len);
-    const int64_t W = split_total(a.g, s_pref);
-    const int64_t sigma = split_sigma(a.g, W);
-
-    // The wave index is uniform within a wave; saying so keeps every per-unit
-    // quantity (sequence, head, page, descriptors, LDS slot) in scalar registers.
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t gw = blockIdx.x * 4 + wave;  // this wave's segment
-    const int64_t x0 = gw * sigma;
-    if (x0 >= W) return;  // no barrier follows
-    const int n_total = (int)(min(W, x0 + sigma) - x0);  // sub-pages this wave attends
-    char* const slot = smem + wave * Lay::kBytes;
-
-    Stream st(a, table, s_pref, s_len, lane);
-    Rows rows(a, lane, 0);
-    Cur cc = st.seek(x0);  // the sub-page being attended
-    Cur pc = cc;           // the next sub-page to fetch
-    st.prefetch_table(cc);
-    st.template fetch<KS>(st.locate(cc), slot, 0, 1, cc.j < cc.nc);
-    if (n_total > 1) {
-        st.step(pc);
-        st.prefetch_table(pc);  // its table entry, one fetch ahead
-    }
-    rows.load_q(cc.b, cc.kh);
-    rows.reset();
-    bool piece_from_start = cc.j == 0;
-    for (int i = 0; i < n_total; ++i) {
-        const bool more = i + 1 < n_total;  // pc is the next sub-page of this wave
-        if (cc.j == 0 && lane == 0 && a.meta) record_segments(a, st, cc, sigma);
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);  // sub-page i and Q have landed
-        // Read the slot out, then refill it at once: the next fetch is in
-        // flight during this sub-page's arithmetic.
-        u32x4_t kop[KS];
-        u32x2_t vt[D / 16];
-        rows.read_k(slot, kop);
-        rows.read_v(slot, vt);
-        if (more) {
-            const typename Stream::Src sn = st.locate(pc);
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // slot read out
-            st.template fetch<KS>(sn, slot, 0, 1, pc.j < pc.nc);
-        }
-        const bool is_new = cc.j >= cc.nc;
-        const int t0 = 16 * (cc.j - cc.nc);
-        const int valid = is_new ? min(16, st.NQ - t0) : min(16, cc.L - 16 * cc.j);
-        int lim[1];
-        rows.limits(valid, is_new, t0, lim);
-        rows.scores(kop, lim);
-        if (more && pc.j == 0) rows.load_q(pc.b, pc.kh);  // Q of the next unit
-        rows.accumulate(vt, valid);
-        if (cc.j + 1 == cc.nsub || !more) {
-            rows.emit(cc.b, cc.kh, gw, piece_from_start && cc.j + 1 == cc.nsub);
-            rows.reset();
-            piece_from_start = true;
-        }
-        if (more) {
-            cc = pc;
-            if (i + 2 < n_total) {
-                st.step(pc);
-                st.prefetch_table(pc);
-            }
-        }
-    }
-}
-
-// ---- NW waves per segment, one row tile each, sharing a ring of sub-pages ----
-// Waits until at most `ahead` (<= MAXA) sub-pages' loads of OPS each are outstanding.
+// Waits until at most A vector-memory instructions of this wave are
+// outstanding, for A = OPS * ahead (ahead <= MAXA; a runtime value dispatched to
+// immediates).
 template <int OPS, int MAXA>
 __device__ __forceinline__ void wait_ahead(int ahead) {
     if constexpr (MAXA > 0) {
@@ -612,105 +542,125 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
     }
 }
 
-template <typename T, int D, int BS, int NW, int kRing>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table) {
+// ---- one wave per (group, KV head): NRT row tiles, a ring of NS slots ----
+// Sub-page i of the wave's run sits in slot i % NS. Iteration i waits until
+// sub-page i has landed (vector loads complete in issue order, so at most
+// kOps * (fetches issued after it) may be outstanding; Q loads and workspace
+// stores issued in between can only make that wait longer), reads the slot
+// into registers, refills it with sub-page i + NS (i + 1 when NS = 1: issued
+// before the arithmetic; otherwise after the scores, so that the next
+// sequence's Q, loaded after the scores, is older than the refill), then
+// computes. NS sub-pages per wave stay in flight.
+template <typename T, int D, int BS, int NRT, int NS, int WPS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPS, WPS)))
+void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table) {
     using Lay = SlotLayout<T, D>;
     using Stream = SubPageStream<T, D, BS>;
+    using Rows = RowTiles<T, D, NRT>;
     using Cur = typename Stream::Cur;
     constexpr int KS = D / 32;
-    constexpr int NWI = NW < KS ? NW : KS;  // waves that issue loads
-    constexpr int IPW = KS / NWI;           // instructions per half per issuing wave
-    static_assert(D % 32 == 0 && BS % 16 == 0 && Lay::kOps == KS && KS % NWI == 0, "shape");
-    static_assert(kRing >= 3, "ring");
+    static_assert(D % 32 == 0 && BS % 16 == 0 && Lay::kOps == KS, "shape");
+    static_assert(Stream::kOps * (NS - 1) <= 63, "vmcnt range");
 
+    // LDS: per wave NS slots, then the prefix and lengths.
     extern __shared__ __attribute__((aligned(1024))) char smem[];  // slots start 1 KiB aligned (XOR addressing)
-    int* s_pref = reinterpret_cast<int*>(smem + kRing * Lay::kBytes);
+    int* s_pref = reinterpret_cast<int*>(smem + 4 * NS * Lay::kBytes);
     int* s_len = s_pref + a.g.B + 1;
     build_prefix(a.context_lens, a.g, s_pref, s_len);
-    const int64_t W = split_total(a.g, s_pref);
-    const int64_t sigma = split_sigma(a.g, W);
+    const Cut cut(a.g, s_pref[a.g.B]);
 
+    // The wave index is uniform within a wave; saying so keeps every per-wave
+    // quantity (group, head, sequence, page, descriptors, LDS slot) scalar.
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t seg = blockIdx.x;  // this workgroup's segment
-    const int64_t x0 = seg * sigma;
-    if (x0 >= W) return;  // uniform over the workgroup: no barrier follows
-    const int n_total = (int)(min(W, x0 + sigma) - x0);
-    const bool issues = wave < NWI;  // this wave loads instructions wave, wave + NWI, ...
-    const bool has_rows = 16 * wave < a.R;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t grp = gw / a.g.KV;  // the KV waves of a group are consecutive
+    const int kh = (int)(gw - grp * a.g.KV);
+    if (grp >= cut.n) return;  // no barrier follows
+    const int64_t x0 = cut.start(grp);
+    const int n_total = (int)(cut.start(grp + 1) - x0);  // sub-pages this wave attends (>= 1)
+    char* const ring = smem + wave * NS * Lay::kBytes;
 
-    Stream st(a, table, s_pref, s_len, lane);
-    RowTiles<T, D, 1> rows(a, lane, wave);
-    Cur cc = st.seek(x0);
-    Cur pc = cc;  // next sub-page to fetch: kRing - 1 ahead of cc once primed
-    // prime the ring: sub-pages 0 .. kRing-2 into slots 0 .. kRing-2
-    int primed = 0;
-    for (; primed < kRing - 1 && primed < n_total; ++primed) {
+    Stream st(a, table, s_pref, s_len, kh, lane);
+    Rows rows(a, lane, 0);
+    Cur cc = st.seek(x0);  // the sub-page being attended
+    Cur pc = cc;           // the next sub-page to fetch
+    rows.load_q(cc.b, kh);  // older than every fetch: the first wait covers it
+    // prime the ring with sub-pages 0 .. min(NS, n_total) - 1
+    int nf = 0;
+    for (; nf < NS && nf < n_total; ++nf) {
         st.prefetch_table(pc);
-        const typename Stream::Src s0 = st.locate(pc);
-        if (issues) st.template fetch<IPW>(s0, smem + primed * Lay::kBytes, wave, NWI, pc.j < pc.nc);
-        if (primed + 1 < n_total) st.step(pc);
+        st.fetch(st.locate(pc), ring + nf * Lay::kBytes, pc.j < pc.nc);
+        if (nf + 1 < n_total) st.step(pc);
     }
-    st.prefetch_table(pc);
-    if (has_rows) rows.load_q(cc.b, cc.kh);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the ring is primed; Q and tables are in
+    if (nf < n_total) st.prefetch_table(pc);  // its table entry, one fetch ahead
     rows.reset();
     bool piece_from_start = cc.j == 0;
+    bool q_pending = true;   // load_q issued, q_ready not yet called
+    int q_younger = NS;      // fetches issued after the pending Q loads (upper bound)
     for (int i = 0; i < n_total; ++i) {
-        const int ahead = min(kRing - 2, n_total - 1 - i);  // sub-pages fetched after i
-        if (cc.j == 0 && lane == 0 && wave == 0 && a.meta) record_segments(a, st, cc, sigma);
-        // this wave's loads of sub-page i have landed (later ones may be in flight)
-        if (issues) {
-            wait_ahead<2 * IPW, kRing - 2>(ahead);
-        } else {
-            __builtin_amdgcn_s_waitcnt(kWaitVm0);  // Q and the table window
+        const bool more = i + 1 < n_total;
+        if (cc.j == 0 && kh == 0 && lane == 0 && a.meta) {
+            // the first piece of a sequence records the groups it spans
+            const int64_t s0 = s_pref[cc.b];
+            a.meta[2 * cc.b] = (int32_t)cut.group_of(s0);
+            a.meta[2 * cc.b + 1] = (int32_t)cut.group_of(s0 + cc.nsub - 1);
         }
-        // Every wave's part of sub-page i is in; slot i-1 is read out. A bare
-        // barrier: each wave has already waited for its own loads (LDS needs no
-        // flush within the CU), and a fenced barrier would also wait for the
-        // loads still in flight into the other slots.
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        // refill the slot of sub-page i - 1 with sub-page i + kRing - 1
-        const int nxt = i + kRing - 1;
-        if (nxt < n_total) {
-            const typename Stream::Src sn = st.locate(pc);
-            if (issues)
-                st.template fetch<IPW>(sn, smem + (nxt % kRing) * Lay::kBytes, wave, NWI, pc.j < pc.nc);
-            if (nxt + 1 < n_total) {
-                st.step(pc);
-                st.prefetch_table(pc);
+        // Sub-page i has landed once at most kOps * (fetches issued after it)
+        // vector loads are outstanding; pending Q loads need at most
+        // kOps * q_younger.
+        const int ahead = min(NS - 1, n_total - 1 - i);
+        wait_ahead<Stream::kOps, NS - 1>(q_pending ? min(ahead, q_younger) : ahead);
+        if (q_pending) {
+            rows.q_ready();
+            q_pending = false;
+        }
+        char* const slot = ring + (i % NS) * Lay::kBytes;
+        u32x4_t kop[KS];
+        u32x2_t vt[D / 16];
+        rows.read_k(slot, kop);
+        rows.read_v(slot, vt);
+        const bool refill = i + NS < n_total;  // sub-page i + NS exists (it is pc)
+        if constexpr (NS == 1) {
+            if (refill) {
+                const typename Stream::Src sn = st.locate(pc);
+                Rows::lds_wait(vt);  // slot read out
+                st.fetch(sn, slot, pc.j < pc.nc);
+            } else {
+                Rows::lds_wait(vt);
             }
+        } else {
+            Rows::lds_wait(vt);
         }
-        const char* slot = smem + (i % kRing) * Lay::kBytes;
         const bool is_new = cc.j >= cc.nc;
         const int t0 = 16 * (cc.j - cc.nc);
         const int valid = is_new ? min(16, st.NQ - t0) : min(16, cc.L - 16 * cc.j);
-        const bool unit_ends = cc.j + 1 == cc.nsub || i + 1 == n_total;
-        if (has_rows) {
-            u32x4_t kop[KS];
-            u32x2_t vt[D / 16];
-            rows.read_k(slot, kop);
-            rows.read_v(slot, vt);
-            int lim[1];
-            rows.limits(valid, is_new, t0, lim);
-            rows.scores(kop, lim);
-            rows.accumulate(vt, valid);
-            if (unit_ends) {
-                rows.emit(cc.b, cc.kh, seg, piece_from_start && cc.j + 1 == cc.nsub);
-                rows.reset();
+        int lim[NRT];
+        rows.limits(valid, is_new, t0, lim);
+        rows.scores(kop, lim);
+        const bool seq_ends = cc.j + 1 == cc.nsub;
+        if (more && seq_ends) {  // Q of the next sequence
+            rows.load_q(cc.b + 1, kh);
+            q_pending = true;
+            q_younger = 0;
+        }
+        if constexpr (NS > 1) {
+            if (refill) {
+                st.fetch(st.locate(pc), slot, pc.j < pc.nc);  // slot already read out
+                ++q_younger;
             }
         }
-        if (unit_ends) piece_from_start = true;
-        if (i + 1 < n_total) {
-            st.step(cc);
-            if (has_rows && cc.j == 0) {  // Q of the next unit (rare: waited for at once)
-                rows.load_q(cc.b, cc.kh);
-                __builtin_amdgcn_s_waitcnt(kWaitVm0);
-            }
+        if (refill && i + NS + 1 < n_total) {
+            st.step(pc);
+            st.prefetch_table(pc);
         }
+        rows.accumulate(vt, valid);
+        if (seq_ends || !more) {
+            rows.emit(cc.b, kh, grp, piece_from_start && seq_ends);
+            rows.reset();
+            piece_from_start = true;
+        }
+        if (more) st.step(cc);
     }
 }
 

@@ -40,11 +40,6 @@ int succeed() {
 
 constexpr int kMaxRows = 128;         // G * nq
 constexpr int kMfmaMaxRows = 64;      // the matrix-core family keeps <= 4 row tiles of 16
-// Resident waves per CU the matrix-core kernels reach on register use (their
-// occupancy attribute: 4 per SIMD). The balanced split gives every resident
-// wave (R <= 16) or workgroup (R > 16, one wave per row tile) one segment; LDS
-// can lower it further (mfma_segments_per_cu).
-constexpr int kMfmaWavesPerCu = 16;
 constexpr int kLdsPerCu = 160 * 1024;
 // A piece's saved state may be at most 1/kStateRatio of the K/V bytes it covers.
 constexpr int kStateRatio = 8;
@@ -129,46 +124,42 @@ int validate_problem(const pa_problem* p) {
 struct Plan {
     // VALU family: parts = key partitions per sequence, chunk = cached tokens per
     // partition (multiple of block_size). Matrix-core family (balanced split):
-    // parts = segments (waves) the work is cut into, chunk = 16 * min_seg.
+    // parts = groups the sequence axis is cut into (KV waves each), chunk =
+    // 16 * min_seg.
     int parts;
     int chunk;
-    int min_seg;  // matrix-core family: minimum segment length in 16-key groups
+    int min_seg;  // matrix-core family: minimum group length in 16-key positions
     int kernel;   // pa_kernel
-    int rt;       // VALU: query rows per workgroup (power of two <= 8); MFMA: 16-row tiles
+    int rt;       // VALU: query rows per workgroup (power of two <= 8); MFMA: 16-row tiles (1, 2, 4)
     int n_tiles;  // workgroups per KV head along the rows (1 for MFMA)
 };
 
-// Ring slots per workgroup of the cooperative kernel (R > 16).
-#ifndef PA_COOP_RING
-#define PA_COOP_RING 4
-#endif
-constexpr int kCoopRing = PA_COOP_RING;
-
-// Waves per workgroup of the matrix-core family: 4 single-wave segments for
-// R <= 16 (decode_mfma), else one wave per row tile, 2 or 4 (decode_mfma_coop).
-int mfma_group_waves(int row_tiles) { return row_tiles <= 2 ? (row_tiles == 1 ? 4 : 2) : 4; }
-
-// Dynamic LDS of a matrix-core workgroup: its sub-page slots (one per wave for
-// R <= 16; the ring for the cooperative kernel) and the per-sequence prefix of
-// the split and the sequence lengths.
-size_t mfma_lds_bytes(const pa_problem* p, int row_tiles) {
-    size_t group;
-    if (row_tiles == 1)
-        group = 4 * (size_t)(p->head_dim == 64 ? pa::SlotLayout<_Float16, 64>::kBytes
-                                               : pa::SlotLayout<_Float16, 128>::kBytes);
-    else
-        group = kCoopRing * (size_t)(p->head_dim == 64 ? pa::SlotLayout<_Float16, 64>::kBytes
-                                                       : pa::SlotLayout<_Float16, 128>::kBytes);
-    return group + (2 * (size_t)p->batch + 1) * sizeof(int);
+// Matrix-core family: waves per SIMD and LDS slots per wave for NRT row tiles:
+// NRT = 1: 4 waves/SIMD, NRT = 2: 2, NRT = 4: 1 (register use), each with
+// enough slots that a CU keeps 128 KiB of sub-pages in flight.
+int mfma_waves_per_simd(int nrt) { return nrt == 1 ? 4 : (nrt == 2 ? 2 : 1); }
+int mfma_slot_bytes(int head_dim) {
+    return head_dim == 64 ? pa::SlotLayout<_Float16, 64>::kBytes
+                          : pa::SlotLayout<_Float16, 128>::kBytes;
+}
+int mfma_slots_per_wave(int nrt, int head_dim) {
+    return (32 * 1024) / (mfma_waves_per_simd(nrt) * mfma_slot_bytes(head_dim));
 }
 
-// Segments one CU holds at once: waves (R <= 16) or workgroups (R > 16).
-int mfma_segments_per_cu(const pa_problem* p, int row_tiles) {
-    const int nw = mfma_group_waves(row_tiles);
-    const int waves = kMfmaWavesPerCu;
-    int groups = (int)(kLdsPerCu / mfma_lds_bytes(p, row_tiles));
-    if (groups > waves / nw) groups = waves / nw;
-    return row_tiles == 1 ? 4 * groups : groups;
+// Dynamic LDS of a matrix-core workgroup (4 waves): their slots, then the
+// per-sequence prefix of the split and the sequence lengths.
+size_t mfma_lds_bytes(const pa_problem* p, int nrt) {
+    return 4 * (size_t)mfma_slots_per_wave(nrt, p->head_dim) * mfma_slot_bytes(p->head_dim) +
+           (2 * (size_t)p->batch + 1) * sizeof(int);
+}
+
+// Waves one CU holds at once: the occupancy of the kernel, lowered by LDS.
+int mfma_waves_per_cu(const pa_problem* p, int nrt) {
+    int groups = (int)(kLdsPerCu / mfma_lds_bytes(p, nrt));  // 4-wave workgroups
+    const int by_regs = mfma_waves_per_simd(nrt);
+    if (groups > by_regs) groups = by_regs;
+    if (groups < 1) groups = 1;
+    return 4 * groups;
 }
 
 int plan_impl(const pa_problem* p, int num_cus, Plan* pl) {
@@ -183,19 +174,21 @@ int plan_impl(const pa_problem* p, int num_cus, Plan* pl) {
     pl->kernel = kernel;
     pl->min_seg = 1;
     if (kernel == PA_KERNEL_MFMA) {
-        pl->rt = (R + 15) / 16;
+        pl->rt = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
         pl->n_tiles = 1;
         const int64_t elem = p->dtype == PA_F32 ? 4 : 2;
         const int64_t state = (int64_t)R * (p->head_dim + 2) * 4;
         const int64_t kv_per_group = 16 * 2 * (int64_t)p->head_dim * elem;
         if (p->num_partitions > (1 << 22))
-            return fail(PA_ERR_UNSUPPORTED, "num_partitions = %d is more segments than supported "
+            return fail(PA_ERR_UNSUPPORTED, "num_partitions = %d is more groups than supported "
                         "(%d)", p->num_partitions, 1 << 22);
         if (p->num_partitions > 0) {
             pl->parts = p->num_partitions;
             pl->min_seg = 1;
         } else {
-            pl->parts = num_cus * mfma_segments_per_cu(p, pl->rt);
+            const int64_t waves = (int64_t)num_cus * mfma_waves_per_cu(p, pl->rt);
+            const int64_t groups = waves / p->num_kv_heads;
+            pl->parts = (int)(groups < 1 ? 1 : (groups > (1 << 22) ? (1 << 22) : groups));
             pl->min_seg = (int)ceil_div(kStateRatio * state, kv_per_group);
         }
         pl->chunk = 16 * pl->min_seg;
@@ -232,18 +225,18 @@ int plan_impl(const pa_problem* p, int num_cus, Plan* pl) {
 }
 
 // Workspace: VALU family [rows][parts][D] + [rows][parts][2]; matrix-core
-// family [slots][R][D] + [slots][R][2] with slots = B*KV + segments.
+// family [slots][R][D] + [slots][R][2] with slots = (B + groups)*KV.
 size_t state_floats(const pa_problem* p, const Plan& pl) {
     if (pl.kernel == PA_KERNEL_MFMA) {
         const size_t R = (size_t)(p->num_heads / p->num_kv_heads) * p->nq;
-        const size_t slots = (size_t)p->batch * p->num_kv_heads + (size_t)pl.parts;
+        const size_t slots = ((size_t)p->batch + (size_t)pl.parts) * p->num_kv_heads;
         return slots * R;
     }
     return (size_t)p->batch * p->num_heads * p->nq * (size_t)pl.parts;
 }
 
-// Matrix-core family: after the states, two int32 per (sequence, KV head): the
-// first and last segment that overlap the unit (written by pass 1).
+// Matrix-core family: after the states, two int32 per sequence: the first and
+// last group that overlap it (written by pass 1).
 size_t meta_offset(const pa_problem* p, const Plan& pl) {
     return state_floats(p, pl) * (size_t)(p->head_dim + 2) * sizeof(float);
 }
@@ -251,7 +244,7 @@ size_t meta_offset(const pa_problem* p, const Plan& pl) {
 size_t workspace_bytes_for(const pa_problem* p, const Plan& pl) {
     if (pl.parts <= 1) return 0;
     size_t bytes = meta_offset(p, pl);
-    if (pl.kernel == PA_KERNEL_MFMA) bytes += (size_t)p->batch * p->num_kv_heads * 2 * sizeof(int32_t);
+    if (pl.kernel == PA_KERNEL_MFMA) bytes += (size_t)p->batch * 2 * sizeof(int32_t);
     return bytes;
 }
 
@@ -326,18 +319,16 @@ void launch_valu(const Plan& pl, dim3 grid, hipStream_t s, const pa::DecodeArgs<
 }
 
 template <typename T, int D, int BS>
-void launch_mfma(const Plan& pl, size_t lds, hipStream_t s, const pa::SplitArgs<T>& a,
-                 const int32_t* table) {
-    if (pl.rt == 1) {
-        const dim3 grid((unsigned)ceil_div(pl.parts, 4));
-        hipLaunchKernelGGL((pa::decode_mfma<T, D, BS>), grid, dim3(256), lds, s, a, table);
-    } else if (mfma_group_waves(pl.rt) == 2) {
-        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2, kCoopRing>), dim3(pl.parts), dim3(128), lds, s, a,
-                           table);
-    } else {
-        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 4, kCoopRing>), dim3(pl.parts), dim3(256), lds, s, a,
-                           table);
-    }
+void launch_mfma(const pa_problem* p, const Plan& pl, size_t lds, hipStream_t s,
+                 const pa::SplitArgs<T>& a, const int32_t* table) {
+    const dim3 grid((unsigned)ceil_div((int64_t)pl.parts * p->num_kv_heads, 4));
+    constexpr int S1 = D == 128 ? 1 : 2;  // slots per wave at 4, 2, 1 waves per SIMD
+    if (pl.rt == 1)
+        hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 1, S1, 4>), grid, dim3(256), lds, s, a, table);
+    else if (pl.rt == 2)
+        hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 2, 2 * S1, 2>), grid, dim3(256), lds, s, a, table);
+    else
+        hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 4, 4 * S1, 1>), grid, dim3(256), lds, s, a, table);
 }
 
 pa::SplitGeometry split_geometry(const pa_problem* p, const Plan& pl) {
@@ -346,7 +337,7 @@ pa::SplitGeometry split_geometry(const pa_problem* p, const Plan& pl) {
     g.KV = p->num_kv_heads;
     g.NQ = p->nq;
     g.max_tokens = p->max_blocks_per_seq * p->block_size;
-    g.n_seg = pl.parts;
+    g.n_grp = pl.parts;
     g.min_seg = pl.min_seg;
     return g;
 }
@@ -377,11 +368,11 @@ void launch_pass1_mfma(const pa_problem* p, const Plan& pl, hipStream_t s,
     a.qscale = d.qscale;
     const size_t lds = mfma_lds_bytes(p, pl.rt);
     if (p->head_dim == 64) {
-        if (p->block_size == 16) launch_mfma<T, 64, 16>(pl, lds, s, a, d.block_table);
-        else launch_mfma<T, 64, 32>(pl, lds, s, a, d.block_table);
+        if (p->block_size == 16) launch_mfma<T, 64, 16>(p, pl, lds, s, a, d.block_table);
+        else launch_mfma<T, 64, 32>(p, pl, lds, s, a, d.block_table);
     } else {
-        if (p->block_size == 16) launch_mfma<T, 128, 16>(pl, lds, s, a, d.block_table);
-        else launch_mfma<T, 128, 32>(pl, lds, s, a, d.block_table);
+        if (p->block_size == 16) launch_mfma<T, 128, 16>(p, pl, lds, s, a, d.block_table);
+        else launch_mfma<T, 128, 32>(p, pl, lds, s, a, d.block_table);
     }
 }
 
@@ -419,10 +410,10 @@ void launch_combine(const pa_problem* p, const Plan& pl, hipStream_t s, const fl
         c.H = p->num_heads;
         c.NQ = p->nq;
         c.R = (p->num_heads / p->num_kv_heads) * p->nq;
-        // pieces per unit is data dependent; segments / units + 1 estimates it.
-        // Many pieces per row: four waves per row; else one wave per row.
+        // pieces per sequence is data dependent; groups / sequences + 1 estimates
+        // it. Many pieces per row: four waves per row; else one wave per row.
         const int64_t units = (int64_t)p->batch * p->num_kv_heads;
-        const int64_t pieces = pl.parts / units + 1;
+        const int64_t pieces = pl.parts / p->batch + 1;
         if (pieces >= 48) {
             const dim3 grid((unsigned)(units * c.R));
             if (p->head_dim == 64)

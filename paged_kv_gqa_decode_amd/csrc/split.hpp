@@ -1,18 +1,22 @@
-// Balanced split of the decode work over waves (used by the matrix-core family).
+// Balanced split of the decode work (used by the matrix-core family).
 //
-// The key lists of all (sequence b, KV head kh) units are laid end to end,
-// unit u = b*KV + kh, each as n_sub(b) = ceil(L_b/16) + ceil(NQ/16) "sub-pages"
-// of 16 keys (cached keys first, then the step's new rows). The concatenation
-// (W sub-pages) is cut into segments of sigma = max(min_seg, ceil(W / n_seg))
-// sub-pages; wave g of the grid attends segment g. The intersection of a
-// segment with a unit is a "piece". A unit covered by a single piece is
-// finished by that wave (output written directly); otherwise each piece's
-// online-softmax state goes to workspace slot u + g (one-to-one, because
-// segments and units are both ordered along the same axis) and the combine
-// kernel merges the unit's slots. This is the partition/merge scheme of the
+// The sequences are laid end to end along one axis, sequence b as n_sub(b) =
+// ceil(L_b/16) + ceil(NQ/16) positions (16-key "sub-pages": cached keys first,
+// then the step's new rows). The axis (W positions) is cut into n_grp groups
+// at positions start(g) = floor(g*W/n_grp), so group sizes differ by at most
+// one. Group g is attended by KV consecutive waves of the grid, wave (g, kh)
+// taking KV head kh of every position of the group: the KV waves of a group
+// stream the same pages at the same time, which keeps the pool reads of one
+// page (all heads of a token are adjacent in memory) close together.
+// The intersection of a group with a sequence is a "piece". A sequence inside
+// a single group is finished by that group's waves (output written directly);
+// otherwise each piece's online-softmax state of head kh goes to workspace slot
+// (b + g)*KV + kh (one-to-one: groups and sequences are ordered along the same
+// axis, so b + g grows at every new intersection) and the combine kernel merges
+// the slots of each (sequence, head). This is the partition/merge scheme of the
 // docs.rs page "onnxruntime-ep-mlx 0.31.1: src/ops/paged_attention.rs"
-// (VECTOR_PARTIALS, PARTIALS_REDUCE) with the cut placed by work rather than
-// by a fixed key stride, so ragged batches keep every wave equally busy.
+// (VECTOR_PARTIALS, PARTIALS_REDUCE) with cuts placed by work rather than by a
+// fixed key stride, so ragged batches keep every wave equally busy.
 #pragma once
 
 #include "pa_device.hpp"
@@ -23,8 +27,8 @@ constexpr int kMaxSplitBatch = 8192;  // sequences per call for the balanced spl
 
 struct SplitGeometry {
     int B, KV, NQ, max_tokens;  // max_tokens = max_blocks_per_seq * block_size
-    int n_seg;                  // segments the grid provides (waves)
-    int min_seg;                // minimum segment length, in sub-pages
+    int n_grp;                  // groups the grid provides (KV waves each)
+    int min_seg;                // minimum group length, in positions
 };
 
 // s_pref[b] = sum_{b' < b} n_sub(b'), b = 0..B (exclusive prefix in LDS), and
@@ -39,10 +43,14 @@ __device__ __forceinline__ void build_prefix(const int32_t* context_lens, const 
         int carry = 0;
         for (int base = 0; base < g.B; base += 512) {
             int n[8];
+            int raw[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)  // unconditional (clamped index): all 8 loads in flight
+                raw[r] = context_lens[min(base + 64 * r + lane, g.B - 1)];
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 const int b = base + 64 * r + lane;
-                const int L = b < g.B ? min(max(context_lens[b], 0), g.max_tokens) : 0;
+                const int L = b < g.B ? min(max(raw[r], 0), g.max_tokens) : 0;
                 if (b < g.B) s_len[b] = L;
                 n[r] = b < g.B ? (L + 15) / 16 + nnew : 0;
             }
@@ -64,22 +72,27 @@ __device__ __forceinline__ void build_prefix(const int32_t* context_lens, const 
     __syncthreads();
 }
 
-__device__ __forceinline__ int64_t split_total(const SplitGeometry& g, const int* s_pref) {
-    return (int64_t)g.KV * s_pref[g.B];
-}
+// The cut of an axis of W positions into groups.
+struct Cut {
+    int64_t W;
+    int64_t n;  // groups in use: n_grp, fewer when groups would be shorter than min_seg
+    __device__ __forceinline__ Cut(const SplitGeometry& g, int64_t total) : W(total) {
+        int64_t m = g.min_seg > 1 ? total / g.min_seg : total;
+        if (m < 1) m = 1;
+        n = m < g.n_grp ? m : g.n_grp;
+    }
+    __device__ __forceinline__ int64_t start(int64_t grp) const { return grp * W / n; }
+    // the group holding position x (largest g with start(g) <= x)
+    __device__ __forceinline__ int64_t group_of(int64_t x) const { return ((x + 1) * n - 1) / W; }
+};
 
-__device__ __forceinline__ int64_t split_sigma(const SplitGeometry& g, int64_t W) {
-    const int64_t s = (W + g.n_seg - 1) / g.n_seg;
-    return s > g.min_seg ? s : g.min_seg;
-}
-
-// Sequence whose units contain position x: largest b with KV*s_pref[b] <= x.
+// Sequence holding position x: largest b with s_pref[b] <= x.
 __device__ __forceinline__ int split_find_seq(const SplitGeometry& g, const int* s_pref,
                                               int64_t x) {
     int lo = 0, hi = g.B - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if ((int64_t)g.KV * s_pref[mid] <= x) lo = mid;
+        if ((int64_t)s_pref[mid] <= x) lo = mid;
         else hi = mid - 1;
     }
     return lo;

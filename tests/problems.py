@@ -80,21 +80,24 @@ def logical_rows(w: W.Workload, b: int, kh: int, r: int):
     return ks, vs
 
 
-def split_single_piece_units(context_lens, KV, NQ, n_seg, min_seg, max_tokens):
-    """Units (b, kh) that the balanced per-wave split leaves in one segment.
+def split_single_piece_units(context_lens, KV, NQ, n_grp, min_seg, max_tokens):
+    """Units (b, kh) that the balanced split leaves in one group.
 
-    Integer model of the split: unit u = b*KV + kh spans ceil(L_b/16) +
-    ceil(NQ/16) groups of 16 keys along one axis; segments are
-    sigma = max(min_seg, ceil(W / n_seg)) groups long."""
+    Integer model of the split: sequence b spans ceil(L_b/16) + ceil(NQ/16)
+    positions of 16 keys along one axis of W positions; n = min(n_grp,
+    max(1, W // min_seg)) groups start at floor(g*W/n), and every KV head of a
+    sequence shares its groups."""
     nnew = (NQ + 15) // 16
     nsub = [(min(max(int(L), 0), max_tokens) + 15) // 16 + nnew for L in context_lens]
-    W = KV * sum(nsub)
-    sigma = max(min_seg, -(-W // n_seg))
+    W = sum(nsub)
+    n = min(n_grp, max(1, W // min_seg if min_seg > 1 else W))
+
+    def group_of(x):
+        return ((x + 1) * n - 1) // W
+
     out, start = set(), 0
-    for b, n in enumerate(nsub):
-        for kh in range(KV):
-            s0, s1 = start // sigma, (start + n - 1) // sigma
-            if s0 == s1:
-                out.add((b, kh))
-            start += n
+    for b, m in enumerate(nsub):
+        if group_of(start) == group_of(start + m - 1):
+            out.update((b, kh) for kh in range(KV))
+        start += m
     return out

@@ -1,9 +1,14 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
 Tolerances (max-abs against the fp64 oracle): 1e-5 for fp32 I/O, 4e-3 for
-fp16/bf16 I/O. Block-table indexing must be bit-exact: outputs for the same
-logical cache stored in another physical block order are compared with
-torch.equal, and poisoned (NaN) unused pool space must not change a bit.
+fp16/bf16 I/O. Where half a unit in the last place of the output dtype at the
+expected value already exceeds the 16-bit bar (bf16 outputs of magnitude >= 1,
+fp16 >= 8: possible with only a few visible keys), rounding the exact result
+to the output dtype alone can use it up; there the bar per element is that
+half unit plus 1e-3 for the arithmetic. Block-table indexing must be
+bit-exact: outputs for the same logical cache stored in another physical block
+order are compared with torch.equal, and poisoned (NaN) unused pool space must
+not change a bit.
 """
 import numpy as np
 import pytest
@@ -44,16 +49,34 @@ def ref(w: W.Workload) -> np.ndarray:
     return oracle.paged_decode(*P.args(w), causal=w.spec.causal)
 
 
+MANTISSA_BITS = {"f16": 10, "bf16": 7}
+
+
+def allowed(expect: np.ndarray, dtype: str) -> np.ndarray:
+    """Per-element bar: TOL, or half an ulp of the output dtype at the expected
+    value plus 1e-3 where that half ulp is the larger."""
+    tol = np.full(expect.shape, TOL[dtype])
+    if dtype in MANTISSA_BITS:
+        mag = np.maximum(np.abs(expect), np.finfo(np.float64).tiny)
+        half_ulp = np.exp2(np.floor(np.log2(mag)) - MANTISSA_BITS[dtype] - 1)
+        tol = np.where(half_ulp > TOL[dtype] / 4 * 3, np.maximum(tol, half_ulp + 1e-3), tol)
+    return tol
+
+
 def max_err(out: torch.Tensor, expect: np.ndarray) -> float:
     return float(np.abs(out.detach().cpu().double().numpy() - expect).max()) if expect.size else 0.0
 
 
 def check(w, out, expect=None):
     expect = ref(w) if expect is None else expect
-    err = max_err(out, expect)
-    assert np.isfinite(out.detach().cpu().double().numpy()).all()
-    assert err <= TOL[w.spec.dtype], f"max-abs error {err} > {TOL[w.spec.dtype]}"
-    return err
+    got = out.detach().cpu().double().numpy()
+    assert np.isfinite(got).all()
+    err = np.abs(got - expect)
+    bar = allowed(expect, w.spec.dtype)
+    worst = np.unravel_index(np.argmax(err - bar), err.shape) if err.size else None
+    assert (err <= bar).all(), (f"error {err[worst]} > {bar[worst]} at {worst} "
+                                f"(expected {expect[worst]})")
+    return float(err.max()) if err.size else 0.0
 
 
 # ---------------------------------------------------------------------------
@@ -108,9 +131,13 @@ GEOMETRIES = [
     (2, 4, 4, 64, 16, 1, True, "f32", (0, 77)),        # MHA
     (3, 8, 1, 64, 32, 3, True, "f16", (15, 16, 33)),   # MQA, multi-row
     (2, 8, 2, 128, 32, 3, False, "bf16", (31, 64)),    # non-causal multi-row
-    (2, 16, 2, 128, 16, 8, True, "f16", (0, 333)),     # 64 rows per KV head
-    (2, 16, 2, 64, 16, 5, True, "bf16", (40, 250)),    # 40 rows, D=64: 2 of 4 waves load
-    (2, 16, 1, 128, 32, 3, True, "f16", (100, 1)),     # 48 rows: one wave without rows
+    (2, 16, 2, 128, 16, 8, True, "f16", (0, 333)),     # 64 rows per KV head: four row tiles
+    (2, 16, 2, 64, 16, 5, True, "bf16", (40, 250)),    # 40 rows, D=64: a padded fourth tile
+    (2, 16, 1, 128, 32, 3, True, "f16", (100, 1)),     # 48 rows: one padded tile
+    (3, 16, 2, 128, 16, 4, True, "bf16", (17, 0, 400)),  # 32 rows: two row tiles
+    (2, 12, 2, 64, 32, 4, False, "f16", (90, 33)),     # 24 rows: a half-filled second tile
+    (3, 12, 3, 128, 16, 1, True, "f16", (50, 300, 7)),   # KV=3: groups straddle workgroups
+    (2, 32, 16, 64, 16, 2, True, "bf16", (260, 19)),   # KV=16: a group spans 4 workgroups
     (1, 32, 2, 128, 16, 8, True, "bf16", (500,)),      # 128 rows per KV head
     (2, 4, 2, 64, 16, 2, True, "f32", (129, 1)),
     (2, 4, 2, 128, 32, 1, True, "f32", (700, 64)),
