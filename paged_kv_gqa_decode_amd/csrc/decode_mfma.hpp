@@ -269,28 +269,34 @@ struct SubPageStream {
         }
         return s;
     }
-    // Issues the kOps load instructions of sub-page `s` (K half, then V half)
-    // into the slot at `slot` (row-coalesced, 16 bytes per lane per
-    // instruction). Cached keys: pool row stride, no range check needed,
-    // non-temporal. New rows: all offsets in voffset and rows past nq clamped to
-    // the last one (they are masked later). (Offsets go in as plain int values:
-    // an array element or a dependent expression passed as is makes the host
-    // compilation pass drop the kernel's launch stub.)
-    __device__ __forceinline__ void fetch(const Src& s, char* slot, bool cached) const {
+    // Issues load instructions i = i0, i0 + istep, ... (COUNT of them, < KS) of
+    // the K and of the V half of sub-page `s` into the slot at `slot`
+    // (row-coalesced, 16 bytes per lane per instruction); COUNT = KS, i0 = 0,
+    // istep = 1 is the whole sub-page (kOps instructions). Cached keys: pool
+    // row stride, no range check needed, non-temporal. New rows: all offsets
+    // in voffset and rows past nq clamped to the last one (they are masked
+    // later). (Offsets go in as plain int values: an array element or a
+    // dependent expression passed as is makes the host compilation pass drop
+    // the kernel's launch stub.)
+    template <int COUNT = KS>
+    __device__ __forceinline__ void fetch(const Src& s, char* slot, bool cached, int i0 = 0,
+                                          int istep = 1) const {
         char* const k_lds = slot;
         char* const v_lds = slot + Lay::kKBytes;
         if (cached) {
             const __amdgpu_buffer_rsrc_t kr = make_rsrc(s.k, 16 * tbytes);
             const __amdgpu_buffer_rsrc_t vr = make_rsrc(s.v, 16 * tbytes);
 #pragma unroll
-            for (int i = 0; i < KS; ++i) {
+            for (int t = 0; t < COUNT; ++t) {
+                const int i = i0 + istep * t;
                 const int koff = kfb ^ (64 * i);
                 const int soff = i * Lay::kKeysPerOp * tbytes;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(k_lds + i * 1024), 16,
                                                          koff, soff, 0, kStreamPolicy);
             }
 #pragma unroll
-            for (int i = 0; i < KS; ++i) {
+            for (int t = 0; t < COUNT; ++t) {
+                const int i = i0 + istep * t;
                 const int voff = Lay::v_fetch_off(i, lane, tbytes);
                 const int soff = i * Lay::kKeysPerOp * tbytes;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(v_lds + i * 1024), 16,
@@ -302,7 +308,8 @@ struct SubPageStream {
             int ln = lane;
             asm volatile("" : "+v"(ln));  // computed here, not kept live across the loop
 #pragma unroll
-            for (int i = 0; i < KS; ++i) {
+            for (int t = 0; t < COUNT; ++t) {
+                const int i = i0 + istep * t;
                 const int row = Lay::kKeysPerOp * i + ln / Lay::kChunks;
                 const int rc = min(row, s.rmax);
                 const int koff = rc * kNewStride + (((ln % Lay::kChunks) ^ Lay::swz(row)) << 4);
@@ -661,6 +668,131 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table) {
             piece_from_start = true;
         }
         if (more) st.step(cc);
+    }
+}
+
+// ---- NW waves per (group, KV head), NRT row tiles each, sharing a ring ----
+// For R > 16 rows: the workgroup's waves split the row tiles (wave w owns tiles
+// w*NRT ..) and share a ring of kRing sub-page slots, so each sub-page is read
+// from HBM once and from LDS once per wave. Every wave issues its share of each
+// sub-page's load instructions (NWI waves issue; vmcnt thresholds count only a
+// wave's own loads); one bare s_barrier per sub-page publishes it and frees the
+// slot read in the previous iteration, which is refilled at once: kRing - 1
+// sub-pages per workgroup stay in flight during the arithmetic. A sequence
+// switch loads the waves' new Q after the arithmetic (it is waited for at the
+// next iteration, a rare full drain).
+template <typename T, int D, int BS, int NW, int NRT, int kRing, int WPS>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPS, WPS)))
+void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table) {
+    using Lay = SlotLayout<T, D>;
+    using Stream = SubPageStream<T, D, BS>;
+    using Rows = RowTiles<T, D, NRT>;
+    using Cur = typename Stream::Cur;
+    constexpr int KS = D / 32;
+    constexpr int NWI = NW < KS ? NW : KS;  // waves that issue loads
+    constexpr int IPW = KS / NWI;           // instructions per half per issuing wave
+    static_assert(D % 32 == 0 && BS % 16 == 0 && Lay::kOps == KS && KS % NWI == 0, "shape");
+    static_assert(kRing >= 3 && 2 * IPW * (kRing - 2) <= 63, "ring");
+
+    extern __shared__ __attribute__((aligned(1024))) char smem[];  // slots start 1 KiB aligned (XOR addressing)
+    int* s_pref = reinterpret_cast<int*>(smem + kRing * Lay::kBytes);
+    int* s_len = s_pref + a.g.B + 1;
+    build_prefix(a.context_lens, a.g, s_pref, s_len);
+    const Cut cut(a.g, s_pref[a.g.B]);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t grp = blockIdx.x / a.g.KV;  // the KV workgroups of a group are consecutive
+    const int kh = (int)(blockIdx.x - grp * a.g.KV);
+    if (grp >= cut.n) return;  // uniform over the workgroup: no barrier follows
+    const int64_t x0 = cut.start(grp);
+    const int n_total = (int)(cut.start(grp + 1) - x0);
+    const bool issues = wave < NWI;  // this wave loads instructions wave, wave + NWI, ...
+    const bool has_rows = 16 * NRT * wave < a.R;
+
+    Stream st(a, table, s_pref, s_len, kh, lane);
+    Rows rows(a, lane, wave * NRT);
+    Cur cc = st.seek(x0);
+    Cur pc = cc;  // next sub-page to fetch: kRing - 1 ahead of cc once primed
+    if (has_rows) rows.load_q(cc.b, kh);  // older than the ring's loads
+    int primed = 0;
+    for (; primed < kRing - 1 && primed < n_total; ++primed) {
+        st.prefetch_table(pc);
+        const typename Stream::Src s0 = st.locate(pc);
+        if (issues) st.template fetch<IPW>(s0, smem + primed * Lay::kBytes, pc.j < pc.nc, wave, NWI);
+        if (primed + 1 < n_total) st.step(pc);
+    }
+    st.prefetch_table(pc);
+    rows.reset();
+    bool q_pending = has_rows;  // load_q issued, q_ready not yet called
+    bool q_drain = false;       // pending Q is younger than the ring's loads
+    bool piece_from_start = cc.j == 0;
+    for (int i = 0; i < n_total; ++i) {
+        const int ahead = min(kRing - 2, n_total - 1 - i);  // sub-pages fetched after i
+        if (cc.j == 0 && lane == 0 && wave == 0 && kh == 0 && a.meta) {
+            const int64_t s0 = s_pref[cc.b];
+            a.meta[2 * cc.b] = (int32_t)cut.group_of(s0);
+            a.meta[2 * cc.b + 1] = (int32_t)cut.group_of(s0 + cc.nsub - 1);
+        }
+        // this wave's loads of sub-page i have landed (later ones may be in flight)
+        if (issues && !q_drain) {
+            wait_ahead<2 * IPW, kRing - 2>(ahead);
+        } else {
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        }
+        if (q_pending) {
+            rows.q_ready();
+            q_pending = false;
+            q_drain = false;
+        }
+        // Every wave's part of sub-page i is in; slot i-1 is read out. A bare
+        // barrier: each wave has already waited for its own loads (LDS needs no
+        // flush within the CU), and a fenced barrier would also wait for the
+        // loads still in flight into the other slots.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // refill the slot of sub-page i - 1 with sub-page i + kRing - 1
+        const int nxt = i + kRing - 1;
+        if (nxt < n_total) {
+            const typename Stream::Src sn = st.locate(pc);
+            if (issues)
+                st.template fetch<IPW>(sn, smem + (nxt % kRing) * Lay::kBytes, pc.j < pc.nc, wave, NWI);
+            if (nxt + 1 < n_total) {
+                st.step(pc);
+                st.prefetch_table(pc);
+            }
+        }
+        const char* slot = smem + (i % kRing) * Lay::kBytes;
+        const bool is_new = cc.j >= cc.nc;
+        const int t0 = 16 * (cc.j - cc.nc);
+        const int valid = is_new ? min(16, st.NQ - t0) : min(16, cc.L - 16 * cc.j);
+        const bool seq_ends = cc.j + 1 == cc.nsub;
+        const bool piece_ends = seq_ends || i + 1 == n_total;
+        if (has_rows) {
+            u32x4_t kop[KS];
+            u32x2_t vt[D / 16];
+            rows.read_k(slot, kop);
+            rows.read_v(slot, vt);
+            Rows::lds_wait(vt);
+            int lim[NRT];
+            rows.limits(valid, is_new, t0, lim);
+            rows.scores(kop, lim);
+            rows.accumulate(vt, valid);
+            if (piece_ends) {
+                rows.emit(cc.b, kh, grp, piece_from_start && seq_ends);
+                rows.reset();
+            }
+        }
+        if (piece_ends) piece_from_start = true;
+        if (i + 1 < n_total) {
+            st.step(cc);
+            if (has_rows && cc.j == 0) {  // Q of the next sequence
+                rows.load_q(cc.b, kh);
+                q_pending = true;
+                q_drain = true;
+            }
+        }
     }
 }
 

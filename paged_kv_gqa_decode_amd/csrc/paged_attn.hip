@@ -134,32 +134,52 @@ struct Plan {
     int n_tiles;  // workgroups per KV head along the rows (1 for MFMA)
 };
 
-// Matrix-core family: waves per SIMD and LDS slots per wave for NRT row tiles:
-// NRT = 1: 4 waves/SIMD, NRT = 2: 2, NRT = 4: 1 (register use), each with
-// enough slots that a CU keeps 128 KiB of sub-pages in flight.
-int mfma_waves_per_simd(int nrt) { return nrt == 1 ? 4 : (nrt == 2 ? 2 : 1); }
+// Matrix-core family launch shapes, by 16-row tiles per KV head (Plan::rt):
+//   rt = 1: decode_mfma, one wave per (group, head) with one row tile;
+//   rt = 2: decode_mfma with two row tiles per wave;
+//   rt = 4: decode_mfma_coop, two waves of two row tiles per (group, head)
+//           sharing a ring of four slots;
+// all at 2 waves per SIMD, each keeping about 128 KiB of sub-pages in flight
+// per CU (slots double for D = 64, whose slots are half as large). Measured
+// on the Llama-3-8B-shaped and ragged-serving workloads: 2 waves per SIMD with
+// 2 slots each beat 4 waves with 1 slot (oldest waves hog the memory path,
+// the last quarter of the kernel runs thin) and 1 wave with 4 slots; for 64
+// rows, 2 waves x 2 tiles beat 4 waves x 1 tile and 1 wave x 4 tiles.
+struct MfmaShape {
+    int nw;     // waves per (group, head): 1, or the cooperative workgroup
+    int nrt;    // row tiles per wave
+    int slots;  // LDS slots per wave (nw = 1) or ring slots per workgroup
+    int wps;    // waves per SIMD the kernel is built for
+};
+MfmaShape mfma_shape(int rt, int head_dim) {
+    const int s1 = head_dim == 128 ? 1 : 2;  // a D = 64 slot is half as large
+    if (rt == 1) return {1, 1, 2 * s1, 2};
+    if (rt == 2) return {1, 2, 2 * s1, 2};
+    return {2, 2, 4 * s1, 2};
+}
 int mfma_slot_bytes(int head_dim) {
     return head_dim == 64 ? pa::SlotLayout<_Float16, 64>::kBytes
                           : pa::SlotLayout<_Float16, 128>::kBytes;
 }
-int mfma_slots_per_wave(int nrt, int head_dim) {
-    return (32 * 1024) / (mfma_waves_per_simd(nrt) * mfma_slot_bytes(head_dim));
+
+// Dynamic LDS of one matrix-core workgroup: its slots (4 single waves' slots,
+// or the cooperative ring), then the per-sequence prefix and lengths.
+size_t mfma_lds_bytes(const pa_problem* p, int rt) {
+    const MfmaShape sh = mfma_shape(rt, p->head_dim);
+    const size_t slots = sh.nw == 1 ? 4 * (size_t)sh.slots : (size_t)sh.slots;
+    return slots * mfma_slot_bytes(p->head_dim) + (2 * (size_t)p->batch + 1) * sizeof(int);
 }
 
-// Dynamic LDS of a matrix-core workgroup (4 waves): their slots, then the
-// per-sequence prefix of the split and the sequence lengths.
-size_t mfma_lds_bytes(const pa_problem* p, int nrt) {
-    return 4 * (size_t)mfma_slots_per_wave(nrt, p->head_dim) * mfma_slot_bytes(p->head_dim) +
-           (2 * (size_t)p->batch + 1) * sizeof(int);
-}
-
-// Waves one CU holds at once: the occupancy of the kernel, lowered by LDS.
-int mfma_waves_per_cu(const pa_problem* p, int nrt) {
-    int groups = (int)(kLdsPerCu / mfma_lds_bytes(p, nrt));  // 4-wave workgroups
-    const int by_regs = mfma_waves_per_simd(nrt);
+// Streams (waves for nw = 1, workgroups otherwise) one CU holds at once: the
+// kernel's occupancy, lowered by LDS.
+int mfma_streams_per_cu(const pa_problem* p, int rt) {
+    const MfmaShape sh = mfma_shape(rt, p->head_dim);
+    const int wg_waves = sh.nw == 1 ? 4 : sh.nw;
+    int groups = (int)(kLdsPerCu / mfma_lds_bytes(p, rt));  // workgroups by LDS
+    const int by_regs = 4 * sh.wps / wg_waves;
     if (groups > by_regs) groups = by_regs;
     if (groups < 1) groups = 1;
-    return 4 * groups;
+    return sh.nw == 1 ? 4 * groups : groups;
 }
 
 int plan_impl(const pa_problem* p, int num_cus, Plan* pl) {
@@ -186,8 +206,8 @@ int plan_impl(const pa_problem* p, int num_cus, Plan* pl) {
             pl->parts = p->num_partitions;
             pl->min_seg = 1;
         } else {
-            const int64_t waves = (int64_t)num_cus * mfma_waves_per_cu(p, pl->rt);
-            const int64_t groups = waves / p->num_kv_heads;
+            const int64_t streams = (int64_t)num_cus * mfma_streams_per_cu(p, pl->rt);
+            const int64_t groups = streams / p->num_kv_heads;
             pl->parts = (int)(groups < 1 ? 1 : (groups > (1 << 22) ? (1 << 22) : groups));
             pl->min_seg = (int)ceil_div(kStateRatio * state, kv_per_group);
         }
@@ -321,14 +341,18 @@ void launch_valu(const Plan& pl, dim3 grid, hipStream_t s, const pa::DecodeArgs<
 template <typename T, int D, int BS>
 void launch_mfma(const pa_problem* p, const Plan& pl, size_t lds, hipStream_t s,
                  const pa::SplitArgs<T>& a, const int32_t* table) {
-    const dim3 grid((unsigned)ceil_div((int64_t)pl.parts * p->num_kv_heads, 4));
-    constexpr int S1 = D == 128 ? 1 : 2;  // slots per wave at 4, 2, 1 waves per SIMD
-    if (pl.rt == 1)
-        hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 1, S1, 4>), grid, dim3(256), lds, s, a, table);
-    else if (pl.rt == 2)
+    constexpr int S1 = D == 128 ? 1 : 2;  // slot counts of mfma_shape
+    const int64_t streams = (int64_t)pl.parts * p->num_kv_heads;
+    if (pl.rt == 1) {
+        const dim3 grid((unsigned)ceil_div(streams, 4));
+        hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 1, 2 * S1, 2>), grid, dim3(256), lds, s, a, table);
+    } else if (pl.rt == 2) {
+        const dim3 grid((unsigned)ceil_div(streams, 4));
         hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 2, 2 * S1, 2>), grid, dim3(256), lds, s, a, table);
-    else
-        hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 4, 4 * S1, 1>), grid, dim3(256), lds, s, a, table);
+    } else {
+        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2, 2, 4 * S1, 2>), dim3((unsigned)streams),
+                           dim3(128), lds, s, a, table);
+    }
 }
 
 pa::SplitGeometry split_geometry(const pa_problem* p, const Plan& pl) {

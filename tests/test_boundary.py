@@ -45,16 +45,16 @@ def spec_problem(spec: W.Spec, max_ctx: int, **kw) -> pa.PaProblem:
 
 # (config index, max_context_len) -> (kernel, partitions, chunk_tokens) on a 256-CU
 # device. VALU family: key partitions per sequence and cached tokens per
-# partition. Matrix-core family (balanced split): groups of KV waves (resident
-# waves / KV: 4 per SIMD with one 16-row tile, 1 per SIMD with four) and the
-# minimum group length in tokens (a piece's saved state is at most 1/8 of the
-# K/V bytes it covers).
+# partition. Matrix-core family (balanced split): groups of KV streams
+# (resident streams / KV: 2 waves per SIMD, one stream per wave up to 32 rows,
+# one per two-wave workgroup above) and the minimum group length in tokens (a
+# piece's saved state is at most 1/8 of the K/V bytes it covers).
 PLAN_TABLE = [
     (0, 100, pa.PA_KERNEL_VALU, 1, 112),
-    (1, 4096, pa.PA_KERNEL_MFMA, 512, 48),
-    (2, 131072, pa.PA_KERNEL_MFMA, 512, 48),
+    (1, 4096, pa.PA_KERNEL_MFMA, 256, 48),
+    (2, 131072, pa.PA_KERNEL_MFMA, 256, 48),
     (3, 8192, pa.PA_KERNEL_MFMA, 128, 16 * 33),
-    (4, 16384, pa.PA_KERNEL_MFMA, 512, 80),
+    (4, 16384, pa.PA_KERNEL_MFMA, 256, 80),
 ]
 
 
@@ -80,7 +80,7 @@ def test_workspace_size(lib):
     prob = spec_problem(W.CONFIGS[1], 4096)
     _, nbytes = pa.pa_workspace_size_ex(prob, 256)
     # slots = (B + groups)*KV, each R = 4 rows of D + 2 floats; then 2 int32 per sequence
-    assert nbytes == (32 + 512) * 8 * 4 * (128 + 2) * 4 + 32 * 2 * 4
+    assert nbytes == (32 + 256) * 8 * 4 * (128 + 2) * 4 + 32 * 2 * 4
     prob = spec_problem(W.CONFIGS[1], 4096, kernel=pa.PA_KERNEL_VALU)
     _, nbytes = pa.pa_workspace_size_ex(prob, 256)
     _, p, _, _ = pa.pa_plan_ex(prob, 256)
