@@ -11,14 +11,14 @@ paged_kv_gqa_decode_amd.workloads.CONFIGS (0..4).
 One step = one paged_attn_decode call (every kernel the step needs). W untimed
 steps, then K timed steps back to back, bracketed by torch.cuda.synchronize()
 and by two HIP events on the launch stream. Pools are rotated over `--replicas`
-copies so the working set exceeds the 256 MB Infinity Cache. A second pass of
-the same K steps with HIP events around each launch gives the per-kernel
-durations used for the roofline (events between kernels add their own drains,
-so that pass is not the timed region).
+copies so the working set exceeds the 256 MB Infinity Cache. The dominant
+kernel (pass 1) is then timed alone: K pass-1 launches back to back between
+two HIP events on the same stream (an event between two kernels would add its
+own drain), and the combine the same way.
 
 Prints ONE JSON line (stdout):
   value  = KV GB/s over the timed region, KV bytes = sum_b (L_b + NQ)*KV*D*2*s
-  roofline.achieved = KV bytes per launch / mean per-launch event duration
+  roofline.achieved = KV bytes per pass-1 launch / mean pass-1 launch duration
   cpu_baseline = the oracle (plain C, fp64) on this host's cores, same workload
 """
 import argparse
@@ -102,7 +102,7 @@ def cpu_baseline(w, seconds: float):
     run(nseq)  # warm-up
     times = []
     t_start = time.perf_counter()
-    while len(times) < 3 or (time.perf_counter() - t_start < seconds and len(times) < 50):
+    while len(times) < 3 or (time.perf_counter() - t_start < seconds and len(times) < 1000):
         times.append(run(nseq))
     t = statistics.median(times)
     s = w.spec
@@ -194,53 +194,46 @@ def main():
     log(f"[bench] kv bytes/step {kvb}, partitions {dec.partitions}, chunk {dec.chunk_tokens}, "
         f"kernel {KERNEL_NAMES.get(dec.kernel, dec.kernel)}, workspace {dec.workspace_bytes} B")
 
-    def step(i, ev=None):
+    def pass1(i):
         r = i % len(kpools)
-        if ev is not None:
-            ev[0].record(stream)
         dec(w.q, kpools[r], vpools[r], table, lens, w.new_k, w.new_v, w.scale, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+
+    def combine():
+        pa.paged_attn_combine(dec.problem, lens, dec.workspace, dec.workspace_bytes, dec.out,
+                              stream=stream)
+
+    def step(i):
+        pass1(i)
         if two:
-            pa.paged_attn_combine(dec.problem, lens, dec.workspace, dec.workspace_bytes, dec.out,
-                                  stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
+            combine()
+
+    def timed(fn, count):
+        """Mean ms per call of `count` calls of fn issued back to back between two
+        HIP events on the launch stream."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(count):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / count
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     K = args.steps
-    # Timed region: K steps back to back, HIP events only at its two ends (an
-    # event between two kernels drains the queue and would add its own gap).
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # Timed region: K steps back to back, HIP events only at its two ends.
     t0 = time.perf_counter()
-    r0.record(stream)
-    for i in range(K):
-        step(i)
-    r1.record(stream)
-    torch.cuda.synchronize()
+    ms_per_step = timed(step, K)
     wall = time.perf_counter() - t0
-    ms_per_step = r0.elapsed_time(r1) / K
-    # Per-kernel durations: the same K steps again with events around each launch
-    # on the launch stream (this pass is slower by the events' drains; only the
-    # per-launch durations are taken from it).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    torch.cuda.synchronize()
-    for i in range(K):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    pass1_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    comb_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    mean_pass1 = sum(pass1_ms) / K
-    mean_comb = sum(comb_ms) / K
+    # The dominant kernel alone, then the combine alone (same stream, same inputs).
+    mean_pass1 = timed(pass1, K)
+    mean_comb = timed(lambda i: combine(), K) if two else 0.0
     value = kvb / (ms_per_step / 1e3) / 1e9
     achieved = kvb / (mean_pass1 / 1e3) / 1e9
-    srt = sorted(pass1_ms)
-    log(f"[bench] {ms_per_step * 1e3:.2f} us/step (region), pass 1 {mean_pass1 * 1e3:.2f} us "
-        f"(p10 {srt[K // 10] * 1e3:.2f} p90 {srt[(9 * K) // 10] * 1e3:.2f}), combine "
-        f"{mean_comb * 1e3:.2f} us, wall {wall / K * 1e6:.2f} us/step, {value:.1f} GB/s")
+    log(f"[bench] {ms_per_step * 1e3:.2f} us/step (region), pass 1 {mean_pass1 * 1e3:.2f} us, "
+        f"combine {mean_comb * 1e3:.2f} us, wall {wall / K * 1e6:.2f} us/step, {value:.1f} GB/s")
 
     copy_gbps = copy_bandwidth(torch)
     log(f"[bench] device copy bandwidth {copy_gbps:.0f} GB/s (read+write)")
@@ -265,13 +258,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": spec.dtype,
         "data": "synthetic",
         "config": {
             "workload": spec.name,
             "batch": spec.B, "num_heads": spec.H, "num_kv_heads": spec.KV, "head_dim": spec.D,
             "block_size": spec.BS, "nq": spec.NQ, "causal": spec.causal, "io_dtype": spec.dtype,
             "context_lens": list(spec.lengths), "kv_bytes_per_step": kvb,
+            "accumulate": "f32",
             "partitions": dec.partitions, "chunk_tokens": dec.chunk_tokens,
             "kernel": KERNEL_NAMES.get(dec.kernel, dec.kernel), "pool_replicas": len(kpools),
             "parallelism": "single GPU",
@@ -283,7 +277,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": f"pass 1 ({KERNEL_NAMES.get(dec.kernel, dec.kernel)} decode kernel)",
+            "kernel": f"pass 1 ({KERNEL_NAMES.get(dec.kernel, dec.kernel)} decode kernel), timed "
+                      f"alone: {K} launches back to back between two HIP events",
             "mean_launch_us": round(mean_pass1 * 1e3, 3),
             "algorithmic_bytes_per_launch": kvb,
             "combine_mean_us": round(mean_comb * 1e3, 3) if two else 0.0,
