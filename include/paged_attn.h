@@ -113,11 +113,13 @@ typedef enum {
  * units of the device (the page's partitions() plays this role: it picks the
  * partition count from the context length and the number of query rows).
  * Outputs: kernel = pa_kernel family used for pass 1; for PA_KERNEL_MFMA,
- * partitions = segments the whole batch's keys are cut into (one per resident
- * wave; 1 = no merge) and chunk_tokens = 16 * the minimum segment length in
- * 16-key groups; for PA_KERNEL_VALU, partitions = key partitions per sequence
- * (1 = single pass) and chunk_tokens = cached tokens per partition (a multiple
- * of block_size). num_partitions > 0 in the problem fixes `partitions`.
+ * partitions = groups the batch's sequence axis is cut into (all sequences
+ * laid end to end in 16-key positions; each group is attended by one stream
+ * per KV head, so partitions = resident streams / num_kv_heads; 1 = no merge)
+ * and chunk_tokens = 16 * the minimum group length in positions; for
+ * PA_KERNEL_VALU, partitions = key partitions per sequence (1 = single pass)
+ * and chunk_tokens = cached tokens per partition (a multiple of block_size).
+ * num_partitions > 0 in the problem fixes `partitions`.
  * Any output pointer may be NULL. No HIP call is made.
  */
 int pa_plan_ex(const pa_problem* problem, int32_t num_cus, int32_t* partitions,
@@ -134,12 +136,13 @@ int pa_plan(const pa_problem* problem, int32_t* partitions, int32_t* chunk_token
  * fp32 online-softmax states (the page's VECTOR_PARTIALS state, in base-2
  * units): o = sum_i 2^(t_i - m) v_i (unnormalised), m = max_i t_i and
  * l = sum_i 2^(t_i - m), with t_i = s_i * log2(e) over some keys of a row.
- *   PA_KERNEL_MFMA (balanced split): all (sequence, KV head) key lists laid end
- *   to end in groups of 16 keys are cut into `partitions` equal segments; a
- *   segment's piece of unit u = b*KV + kh is slot u + segment. Layout:
- *   o[slots][R][head_dim], ml[slots][R][2], then int32 [B*KV][2] = first and
- *   last segment of each unit (written by pass 1); slots = B*KV + partitions,
- *   R = (H/KV)*nq (rows of one unit, r_local = (h % G)*nq + r).
+ *   PA_KERNEL_MFMA (balanced split): the sequences laid end to end in
+ *   positions of 16 keys (ceil(L_b/16) cached, then ceil(nq/16) new) are cut
+ *   into `partitions` groups of equal length (+-1); the piece of sequence b in
+ *   group g, for KV head kh, is slot (b + g)*num_kv_heads + kh. Layout:
+ *   o[slots][R][head_dim], ml[slots][R][2], then int32 [B][2] = first and last
+ *   group of each sequence (written by pass 1); slots = (B + partitions) *
+ *   num_kv_heads, R = (H/KV)*nq (rows of one KV head, r_local = (h % G)*nq + r).
  *   PA_KERNEL_VALU (chunks of chunk_tokens cached keys per sequence):
  *   o[rows][P][head_dim], ml[rows][P][2] with rows = B*H*nq, row = (b*H + h)*nq + r.
  * States that are not needed (a unit or sequence done in one piece) are not
