@@ -31,10 +31,25 @@ struct SplitGeometry {
     int min_seg;                // minimum group length, in positions
 };
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (no LDS round trips): within each 16-lane row by shifts of 1,
+// 2, 4 and 8, then lane 15 of each row into the next and lane 31 into the
+// upper half.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
+}
+
 // s_pref[b] = sum_{b' < b} n_sub(b'), b = 0..B (exclusive prefix in LDS), and
 // s_len[b] = the cached length of sequence b clamped to [0, max_tokens].
-// Every thread of the workgroup must call this; the first wave scans 64
-// sequences per round (8 rounds' loads in flight at once), one barrier at the end.
+// Every thread of the workgroup must call this; the first wave loads 512
+// lengths per round (all 8 loads in flight at once) and scans only the
+// 64-lane slices that hold sequences; one barrier at the end.
 __device__ __forceinline__ void build_prefix(const int32_t* context_lens, const SplitGeometry& g,
                                              int* s_pref, int* s_len) {
     if (threadIdx.x < 64) {
@@ -42,29 +57,22 @@ __device__ __forceinline__ void build_prefix(const int32_t* context_lens, const 
         const int nnew = (g.NQ + 15) / 16;
         int carry = 0;
         for (int base = 0; base < g.B; base += 512) {
-            int n[8];
             int raw[8];
 #pragma unroll
             for (int r = 0; r < 8; ++r)  // unconditional (clamped index): all 8 loads in flight
                 raw[r] = context_lens[min(base + 64 * r + lane, g.B - 1)];
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
+                if (base + 64 * r >= g.B) break;  // uniform: no sequences left
                 const int b = base + 64 * r + lane;
                 const int L = b < g.B ? min(max(raw[r], 0), g.max_tokens) : 0;
-                if (b < g.B) s_len[b] = L;
-                n[r] = b < g.B ? (L + 15) / 16 + nnew : 0;
-            }
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                int incl = n[r];  // inclusive scan over the wave
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const int v = __shfl_up(incl, off);
-                    if (lane >= off) incl += v;
+                const int n = b < g.B ? (L + 15) / 16 + nnew : 0;
+                const int incl = wave_inclusive_scan(n);
+                if (b < g.B) {
+                    s_len[b] = L;
+                    s_pref[b] = carry + incl - n;
                 }
-                const int b = base + 64 * r + lane;
-                if (b < g.B) s_pref[b] = carry + incl - n[r];
-                carry += __shfl(incl, 63);
+                carry += __builtin_amdgcn_readlane(incl, 63);
             }
         }
         if (lane == 0) s_pref[g.B] = carry;
