@@ -447,15 +447,36 @@ struct RowTiles {
     }
     // S^T and the online softmax for one sub-page; leaves the P operands in
     // phi/plo. Keys 4*g16 + i >= lim[rt] are not visible to this lane's row.
-    __device__ __forceinline__ void scores(const u32x4_t (&kop)[KS], const int (&lim)[NRT]) {
+    // `full`: every key of the sub-page is visible to every row (wave-uniform),
+    // so no score needs masking. The score products of all row tiles are
+    // issued before any is read (one tile: two independent half-chains over
+    // d), so the matrix-core latency of one chain is covered by the others.
+    __device__ __forceinline__ void scores(const u32x4_t (&kop)[KS], const int (&lim)[NRT],
+                                           bool full) {
+        constexpr int NC = NRT == 1 && KS % 2 == 0 ? 2 : 1;  // chains per tile
+        f32x4_t sc[NRT][NC];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) sc[rt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt)
+                sc[rt][kk % NC] = M::qk(kop[kk], qop[rt][kk], sc[rt][kk % NC]);
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
-            f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) s = M::qk(kop[kk], qop[rt][kk], s);
+            f32x4_t s = sc[rt][0];
+            if constexpr (NC == 2) s += sc[rt][1];
             float sv[4];
+            if (full) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sv[i] = 4 * g16 + i < lim[rt] ? s[i] * a.qscale : -__builtin_inff();
+                for (int i = 0; i < 4; ++i) sv[i] = s[i] * a.qscale;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sv[i] = 4 * g16 + i < lim[rt] ? s[i] * a.qscale : -__builtin_inff();
+            }
             // m[rt] is the same in the 4 lanes of a row (lanes c16 + 16*g).
             float tm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
             if (__any(tm > m[rt] + kSlack)) {
@@ -644,7 +665,7 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table) {
         const int valid = is_new ? min(16, st.NQ - t0) : min(16, cc.L - 16 * cc.j);
         int lim[NRT];
         rows.limits(valid, is_new, t0, lim);
-        rows.scores(kop, lim);
+        rows.scores(kop, lim, !is_new && valid == 16);
         const bool seq_ends = cc.j + 1 == cc.nsub;
         if (more && seq_ends) {  // Q of the next sequence
             rows.load_q(cc.b + 1, kh);
@@ -777,7 +798,7 @@ void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table) {
             Rows::lds_wait(vt);
             int lim[NRT];
             rows.limits(valid, is_new, t0, lim);
-            rows.scores(kop, lim);
+            rows.scores(kop, lim, !is_new && valid == 16);
             rows.accumulate(vt, valid);
             if (piece_ends) {
                 rows.emit(cc.b, kh, grp, piece_from_start && seq_ends);
