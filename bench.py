@@ -120,6 +120,14 @@ def cpu_baseline(w, seconds: float):
     }
 
 
+def percentile(sorted_values, q) -> float:
+    """Linear-interpolation percentile of an ascending list."""
+    x = (len(sorted_values) - 1) * q / 100.0
+    lo = int(x)
+    hi = min(lo + 1, len(sorted_values) - 1)
+    return sorted_values[lo] + (sorted_values[hi] - sorted_values[lo]) * (x - lo)
+
+
 def copy_bandwidth(torch, nbytes=1 << 30, reps=10) -> float:
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
     b = torch.empty_like(a)
@@ -141,6 +149,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="extra timed regions of K steps after the headline one, for the "
+                         "median / p10 / p90 of the per-step time")
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 valu, 2 mfma")
@@ -227,6 +238,8 @@ def main():
     t0 = time.perf_counter()
     ms_per_step = timed(step, K)
     wall = time.perf_counter() - t0
+    # Spread: further regions of K steps, each between its own two events.
+    reps = sorted(timed(step, K) * 1e3 for _ in range(args.repeats))
     # The dominant kernel alone, then the combine alone (same stream, same inputs).
     mean_pass1 = timed(pass1, K)
     mean_comb = timed(lambda i: combine(), K) if two else 0.0
@@ -282,6 +295,12 @@ def main():
             "mean_launch_us": round(mean_pass1 * 1e3, 3),
             "algorithmic_bytes_per_launch": kvb,
             "combine_mean_us": round(mean_comb * 1e3, 3) if two else 0.0,
+        },
+        "step_repeats": {
+            "regions": len(reps), "steps_each": K,
+            "median_us_per_step": round(statistics.median(reps), 2) if reps else None,
+            "p10_us_per_step": round(percentile(reps, 10), 2) if reps else None,
+            "p90_us_per_step": round(percentile(reps, 90), 2) if reps else None,
         },
         "device_copy_gbps": round(copy_gbps, 1),
         "cpu_baseline": cpu,

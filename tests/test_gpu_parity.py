@@ -154,6 +154,18 @@ def test_geometries(case):
         check(w, gpu_decode(w, num_partitions=parts), expect)
 
 
+def test_many_short_sequences():
+    # 4200 sequences of 0..39 cached keys: an LDS prefix of 33 KiB beside the
+    # slots, most sequences inside one group, several per wave
+    B = 4200
+    lens = tuple(int(x) for x in np.random.default_rng(21).integers(0, 40, size=B))
+    w = to_device(P.small(B=B, H=4, KV=2, D=64, BS=16, NQ=1, causal=True, dtype="f16",
+                          lens=lens, seed=22))
+    expect = ref(w)
+    for parts in (0, 5):
+        check(w, gpu_decode(w, num_partitions=parts), expect)
+
+
 # ---------------------------------------------------------------------------
 # Block-table indexing: bit-exact invariants
 # ---------------------------------------------------------------------------
@@ -243,7 +255,10 @@ def test_combine_remerges_the_workspace(kernel):
     w = to_device(W.make_workload(SMALL[0], device="cpu"))
     table = torch.from_numpy(w.block_table).to(DEV)
     lens = torch.from_numpy(w.context_lens).to(DEV)
-    parts = 5
+    # VALU: 5 key partitions per sequence; matrix-core: 20 groups, so the
+    # longer sequences straddle groups (combine) and the short ones are
+    # finished in pass 1
+    parts = 20 if kernel == pa.PA_KERNEL_MFMA else 5
     dec = pa.Decoder(w.q, w.k_pool, table, max_context_len=w.max_context_len,
                      num_partitions=parts, kernel=kernel)
     assert dec.partitions > 1 and dec.kernel == kernel
