@@ -212,7 +212,7 @@ struct SubPageStream {
     const int* s_len;
     int KV, NQ, kh, nnew, tbytes, lane;
     int kfb;  // per-lane K fetch offset of a cached sub-page (instruction 0)
-    int pre_b = -1, pre_page = 0, pre_phys = 0;  // table entry loaded ahead
+    int pre_phys = 0;  // table entry of the last prefetch_table() position
 
     __device__ __forceinline__ SubPageStream(const SplitArgs<T>& args,
                                              const int32_t* __restrict__ tab, const int* pref,
@@ -244,18 +244,29 @@ struct SubPageStream {
     __device__ __forceinline__ int table_entry(const Cur& c) const {
         return table[(int64_t)c.b * a.max_blocks + c.j / SUB];
     }
+    // Table entries of the positions c, c + 1, ... (n of them, n <= N) for
+    // priming a ring: their scalar loads go out back to back (one latency for
+    // the run instead of one per sub-page); entries of new-row positions are 0.
+    template <int N>
+    __device__ __forceinline__ void run_tables(Cur c, int n, int (&phys)[N]) const {
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            phys[k] = k < n && c.j < c.nc ? table_entry(c) : 0;
+            if (k + 1 < n) step(c);
+        }
+    }
     // Starts loading the table entry of c ahead of locate(c).
     __device__ __forceinline__ void prefetch_table(const Cur& c) {
         if (c.j >= c.nc) return;  // new rows: no table
-        pre_b = c.b;
-        pre_page = c.j / SUB;
         pre_phys = table_entry(c);
     }
-    __device__ __forceinline__ Src locate(const Cur& c) const {
+    // Source of sub-page c; a cached one must be the position of the last
+    // prefetch_table() (every fetch after the prime follows that order).
+    __device__ __forceinline__ Src locate(const Cur& c) const { return locate_at(c, pre_phys); }
+    // locate() with the table entry of a cached sub-page already at hand
+    __device__ __forceinline__ Src locate_at(const Cur& c, int64_t phys) const {
         Src s;
         if (c.j < c.nc) {
-            const int page = c.j / SUB;
-            const int64_t phys = (c.b == pre_b && page == pre_page) ? pre_phys : table_entry(c);
             const int64_t row0 = phys * BS + 16 * (c.j % SUB);
             s.k = a.k_pool + (row0 * KV + kh) * D;
             s.v = a.v_pool + (row0 * KV + kh) * D;
@@ -615,11 +626,16 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table) {
     Cur pc = cc;           // the next sub-page to fetch
     rows.load_q(cc.b, kh);  // older than every fetch: the first wait covers it
     // prime the ring with sub-pages 0 .. min(NS, n_total) - 1
-    int nf = 0;
-    for (; nf < NS && nf < n_total; ++nf) {
-        st.prefetch_table(pc);
-        st.fetch(st.locate(pc), ring + nf * Lay::kBytes, pc.j < pc.nc);
-        if (nf + 1 < n_total) st.step(pc);
+    const int nf = min(NS, n_total);
+    {
+        int phys[NS];
+        st.run_tables(cc, nf, phys);
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            if (k < nf) st.fetch(st.locate_at(pc, phys[k]), ring + k * Lay::kBytes, pc.j < pc.nc);
+            if (k + 1 < nf) st.step(pc);
+        }
+        if (nf < n_total) st.step(pc);
     }
     if (nf < n_total) st.prefetch_table(pc);  // its table entry, one fetch ahead
     rows.reset();
@@ -736,12 +752,17 @@ void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table) {
     Cur cc = st.seek(x0);
     Cur pc = cc;  // next sub-page to fetch: kRing - 1 ahead of cc once primed
     if (has_rows) rows.load_q(cc.b, kh);  // older than the ring's loads
-    int primed = 0;
-    for (; primed < kRing - 1 && primed < n_total; ++primed) {
-        st.prefetch_table(pc);
-        const typename Stream::Src s0 = st.locate(pc);
-        if (issues) st.template fetch<IPW>(s0, smem + primed * Lay::kBytes, pc.j < pc.nc, wave, NWI);
-        if (primed + 1 < n_total) st.step(pc);
+    {
+        const int np = min(kRing - 1, n_total);
+        int phys[kRing - 1];
+        st.run_tables(cc, np, phys);
+#pragma unroll
+        for (int k = 0; k < kRing - 1; ++k) {
+            if (k < np && issues)
+                st.template fetch<IPW>(st.locate_at(pc, phys[k]), smem + k * Lay::kBytes, pc.j < pc.nc,
+                                       wave, NWI);
+            if (k + 1 < n_total && k + 1 <= np) st.step(pc);
+        }
     }
     st.prefetch_table(pc);
     rows.reset();
