@@ -7,7 +7,9 @@ it, and this package never imports the product path.
 Two independent implementations live here:
   * `paged_decode` / `paged_decode_partitioned`: ctypes calls into the plain C
     oracle (liboracle.so, double precision): block-table gather in logical
-    order, then a textbook max-subtracted softmax.
+    order, then a textbook max-subtracted softmax. `paged_decode_append`: the
+    slot-patched step (new rows stored into their pool slots, then the same
+    gather).
   * `dense_reference` / `sdpa_reference`: brute force in torch float64 on the
     CPU. The paged cache is first materialised into a dense [B, KV, S, D]
     tensor by fancy indexing, query heads are expanded with repeat_interleave,
@@ -41,6 +43,8 @@ def load_library(path: str):
     lib.oracle_paged_decode.restype = i
     lib.oracle_paged_decode_partitioned.argtypes = [i] * 9 + [p] * 7 + [f, i, i, p, p, p, p]
     lib.oracle_paged_decode_partitioned.restype = i
+    lib.oracle_kv_append.argtypes = [i] * 7 + [p] * 5
+    lib.oracle_kv_append.restype = i
     lib.oracle_widen.argtypes = [p, ctypes.c_int64, i]
     lib.oracle_widen.restype = ctypes.c_double
     lib.oracle_num_threads.argtypes = []
@@ -130,6 +134,35 @@ def paged_decode_partitioned(q, k_pool, v_pool, block_table, context_lens, new_k
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     return (out, pm, pz, po) if want_parts else out
+
+
+def kv_append(k_pool, v_pool, new_k, new_v, slot_mapping, lib=None):
+    """Host copies of the pools with this step's new rows stored into their
+    slots (C oracle_kv_append); the inputs are not modified."""
+    kp, vp = _host(k_pool).clone(), _host(v_pool).clone()
+    nk, nv = _host(new_k), _host(new_v)
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int32)
+    NB, BS, KV, D = kp.shape
+    B, _, NQ, _ = nk.shape
+    assert slots.shape == (B, NQ), "slot_mapping must be [B, NQ]"
+    rc = _load(lib).oracle_kv_append(B, KV, D, BS, NB, NQ, _DT[kp.dtype],
+                                     ctypes.c_void_p(kp.data_ptr()), ctypes.c_void_p(vp.data_ptr()),
+                                     ctypes.c_void_p(nk.data_ptr()), ctypes.c_void_p(nv.data_ptr()),
+                                     slots.ctypes.data_as(ctypes.c_void_p))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return kp, vp
+
+
+def paged_decode_append(q, k_pool, v_pool, block_table, context_lens, new_k, new_v,
+                        slot_mapping, scale: float, causal: bool = True, lib=None):
+    """The slot-patched step: (out double [B, H, NQ, D], k_pool after, v_pool after).
+    New rows are stored into their slots first; the decode then reads the
+    updated pools (a cached position whose slot was written reads the new row)."""
+    kp, vp = kv_append(k_pool, v_pool, new_k, new_v, slot_mapping, lib=lib)
+    out = paged_decode(q, kp, vp, block_table, context_lens, new_k, new_v, scale,
+                       causal=causal, lib=lib)
+    return out, kp, vp
 
 
 # ----------------------------------------------------------------------------

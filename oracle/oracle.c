@@ -20,8 +20,14 @@
  *     rows 0..r when causal, all NQ new rows otherwise (VECTOR_BODY's `total`).
  *   - The softmax scale is the binary32 value passed in, widened to double
  *     (the page passes the fp32 bit pattern of the scale to the kernel).
- *   - The page's slot-patching of cached positions is not part of this
- *     operation: the pool is read-only and new rows never alias pool slots.
+ *   - Slot patching (oracle_kv_append): the page gives each new row j a pool
+ *     slot (block * BS + offset, negative = none) and makes a cached position
+ *     whose slot is one of them read that new row instead of the pool, the
+ *     last such j winning; the engine page writes the rows into those slots.
+ *     Both are the same as first storing every new row into its slot in
+ *     order (sequence, then j ascending: later stores replace earlier ones)
+ *     and then gathering as usual. Slots outside [0, num_blocks * BS) are
+ *     ignored.
  * No blocking, fusion or reordering beyond gathering one (sequence, KV head)
  * once and reusing it for the G*NQ query rows that read it.
  */
@@ -247,6 +253,34 @@ static int decode_impl(int B, int H, int KV, int D, int BS, int max_blocks, int 
         free(K); free(V); free(s); free(qrow); free(acc);
     }
     return failed ? -6 : 0;
+}
+
+int oracle_kv_append(int B, int KV, int D, int BS, int num_blocks, int NQ, int dtype,
+                     void* k_pool, void* v_pool, const void* new_k, const void* new_v,
+                     const int32_t* slot_mapping)
+{
+    if (B < 0 || KV <= 0 || D <= 0 || BS <= 0 || num_blocks < 0 || NQ < 0)
+        return -1;
+    if (dtype < 0 || dtype > 2)
+        return -3;
+    const int64_t elem = dtype == 0 ? 4 : 2;
+    const int64_t row_bytes = (int64_t)KV * D * elem; /* one token: every KV head */
+    const int64_t slots = (int64_t)num_blocks * BS;
+    for (int b = 0; b < B; ++b) {
+        for (int j = 0; j < NQ; ++j) {
+            const int64_t slot = slot_mapping[(int64_t)b * NQ + j];
+            if (slot < 0 || slot >= slots)
+                continue;
+            for (int kh = 0; kh < KV; ++kh) {
+                const int64_t row = ((int64_t)b * KV + kh) * NQ + j; /* new row j of (b, kh) */
+                const int64_t src = row * D * elem;
+                const int64_t dst = slot * row_bytes + (int64_t)kh * D * elem;
+                memcpy((char*)k_pool + dst, (const char*)new_k + src, (size_t)(D * elem));
+                memcpy((char*)v_pool + dst, (const char*)new_v + src, (size_t)(D * elem));
+            }
+        }
+    }
+    return 0;
 }
 
 int oracle_paged_decode(int B, int H, int KV, int D, int BS, int max_blocks, int NQ,

@@ -21,6 +21,7 @@
  *   block_table  int32 [B, max_blocks]
  *   context_lens int32 [B]   cached (past) length, new rows excluded
  *   new_k/new_v  [B, KV, NQ, D]
+ *   slot_mapping int32 [B, NQ] token slot of each new row, negative = none
  * Return value: 0 on success, a negative number on a malformed argument (no
  * partial output is guaranteed in that case).
  */
@@ -57,6 +58,17 @@ int oracle_paged_decode_partitioned(int B, int H, int KV, int D, int BS, int max
                                     const void* new_v, float scale, int chunk,
                                     int max_chunks, double* part_m, double* part_z,
                                     double* part_o, double* out);
+
+/*
+ * Stores this step's new rows into the pools: for b = 0..B-1, then j =
+ * 0..NQ-1 (later stores replace earlier ones), if 0 <= slot_mapping[b*NQ + j]
+ * < num_blocks*BS, token slot s = slot_mapping[b*NQ + j] (block s / BS, offset
+ * s % BS) receives new row j of sequence b for every KV head. Decoding the
+ * updated pools with oracle_paged_decode is the page's slot-patched read.
+ */
+int oracle_kv_append(int B, int KV, int D, int BS, int num_blocks, int NQ, int dtype,
+                     void* k_pool, void* v_pool, const void* new_k, const void* new_v,
+                     const int32_t* slot_mapping);
 
 /* Exact widening of one stored element (exported so tests can pin it). */
 double oracle_widen(const void* base, int64_t index, int dtype);

@@ -201,7 +201,7 @@ class Decoder:
         _, self.partitions, self.chunk_tokens, self.kernel = pa_plan(self.problem)
         _, self.workspace_bytes = pa_workspace_size(self.problem)
         dev = q.device
-        # zero-filled once: the library keeps its ticket counters at zero
+        # no initial contents are required (zero-filled for reproducible dumps)
         self.workspace = (torch.zeros(self.workspace_bytes, dtype=torch.uint8, device=dev)
                           if self.workspace_bytes else None)
         self.out = torch.empty_like(q)

@@ -101,3 +101,71 @@ def split_single_piece_units(context_lens, KV, NQ, n_grp, min_seg, max_tokens):
             out.update((b, kh) for kh in range(KV))
         start += m
     return out
+
+
+def append_problem(w: W.Workload, *, overwrite: int = 0, duplicate: bool = False,
+                   negative: int = 0, out_of_range: int = 0, seed: int = 0, fill=float("nan")):
+    """The same logical cache re-stored with room for this step's new rows, and a
+    slot mapping int32 [B, NQ] for them (inputs only, no attention arithmetic).
+
+    New row j of sequence b is mapped to the token slot of logical position
+    L_b + j: block table entry (L_b + j) // BS, offset (L_b + j) % BS; space past
+    each cached length holds `fill`. Then, chosen with the seed: `overwrite`
+    entries are re-pointed at the slot of a random cached position of the same
+    sequence; `duplicate` makes the last new row of each sequence (NQ > 1) share
+    the slot of its first; `negative` entries become -1 and `out_of_range`
+    entries point past the pool (neither is stored nor read).
+    Returns (workload, slot_mapping, reads) with reads[(b, p)] = j: cached
+    position p of sequence b is overwritten this step, by new row j (the
+    highest j that points at it)."""
+    s = w.spec
+    rng = np.random.default_rng(seed)
+    BS, NQ = s.BS, s.NQ
+    lens = [int(L) for L in w.context_lens]
+    pages = [max(1, (L + NQ + BS - 1) // BS) for L in lens]
+    nblocks = sum(pages) + 2
+    order = rng.permutation(nblocks)
+    max_blocks = max(pages)
+    table = np.zeros((s.B, max_blocks), dtype=np.int32)
+    kp = torch.full((nblocks, BS, s.KV, s.D), fill, dtype=w.k_pool.dtype)
+    vp = torch.full_like(kp, fill)
+    src_k, src_v = w.k_pool.cpu(), w.v_pool.cpu()
+    nxt = 0
+    for b, L in enumerate(lens):
+        for n in range(pages[b]):
+            table[b, n] = int(order[nxt])
+            nxt += 1
+        for i in range(L):
+            sp = int(w.block_table[b, i // s.BS])
+            kp[table[b, i // BS], i % BS] = src_k[sp, i % s.BS]
+            vp[table[b, i // BS], i % BS] = src_v[sp, i % s.BS]
+
+    def slot_of(b, i):
+        return int(table[b, i // BS]) * BS + i % BS
+
+    slots = np.array([[slot_of(b, lens[b] + j) for j in range(NQ)] for b in range(s.B)],
+                     dtype=np.int32).reshape(s.B, NQ)
+    entries = [(b, j) for b in range(s.B) for j in range(NQ)]
+    with_past = [(b, j) for (b, j) in entries if lens[b] > 0]
+    for k in rng.permutation(len(with_past))[:overwrite]:
+        b, j = with_past[k]
+        slots[b, j] = slot_of(b, int(rng.integers(0, lens[b])))
+    if duplicate and NQ > 1:
+        slots[:, NQ - 1] = slots[:, 0]
+    for k in rng.permutation(len(entries))[:negative]:
+        b, j = entries[k]
+        slots[b, j] = -1
+    for k in rng.permutation(len(entries))[:out_of_range]:
+        b, j = entries[k]
+        slots[b, j] = nblocks * BS + int(rng.integers(0, 3 * BS))
+    reads = {}
+    for b, L in enumerate(lens):
+        where = {slot_of(b, p): p for p in range(L)}
+        for j in range(NQ):
+            p = where.get(int(slots[b, j]))
+            if p is not None:
+                reads[(b, p)] = j  # j ascending: the highest j stays
+    spec = s.replace(max_blocks=max_blocks, pool=("fixed", nblocks))
+    w2 = W.Workload(spec, w.context_lens.copy(), table, nblocks, w.q.cpu(), kp, vp,
+                    w.new_k.cpu(), w.new_v.cpu(), w.scale)
+    return w2, slots, reads

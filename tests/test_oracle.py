@@ -10,6 +10,11 @@ and PARTIALS_REDUCE: merge of partial states). The pins are:
   * invariants: physical block order, block size, partitioning and causality
     do not change the result,
   * exact widening of stored binary16 / bfloat16 bit patterns,
+  * slot patching: rows stored by the append come back through the block
+    table at their logical positions, nothing else in the pools changes, and
+    a cached position whose slot is re-written reads the new row (the highest
+    j pointing at it) -- against SDPA on the dense problem with that position
+    replaced directly,
   * mutation check: plausible mistakes planted in a copy of the oracle's C
     source each make at least one of these pins fail.
 """
@@ -205,6 +210,97 @@ def test_rejects_malformed_arguments():
 
 
 # --------------------------------------------------------------------------
+# Slot patching: the step's new rows stored into their pool slots
+# --------------------------------------------------------------------------
+APPEND_CASES = [
+    # (B, H, KV, D, BS, NQ, causal, dtype, lens)
+    (3, 8, 2, 64, 16, 1, True, "f16", (0, 15, 40)),
+    (2, 16, 2, 128, 16, 8, True, "bf16", (5, 33)),
+    (2, 4, 1, 64, 32, 3, False, "f32", (31, 64)),
+    (2, 6, 3, 64, 16, 4, True, "f32", (16, 47)),
+]
+
+
+def _bits(t: torch.Tensor) -> torch.Tensor:
+    """Bit patterns of a tensor (NaN-safe exact comparison)."""
+    return t.contiguous().view(torch.int32 if t.element_size() == 4 else torch.int16)
+
+
+def _dense_with_reads(w, reads, causal):
+    """Brute force of the patched step: the dense problem of the cache as
+    stored, with cached position p of sequence b replaced by new row j for each
+    reads[(b, p)] = j, through torch's SDPA in float64."""
+    qd, Kh, Vh, vis = oracle._dense_problem(*P.args(w)[:7], causal)
+    G = w.spec.H // w.spec.KV
+    nk, nv = w.new_k.cpu().double(), w.new_v.cpu().double()
+    for (b, p), j in reads.items():
+        Kh[b, :, p] = nk[b, :, j].repeat_interleave(G, dim=0)
+        Vh[b, :, p] = nv[b, :, j].repeat_interleave(G, dim=0)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qd, Kh, Vh, attn_mask=vis, scale=float(np.float32(w.scale)))
+    return out.numpy()
+
+
+def _append_case(case, **kw):
+    B, H, KV, D, BS, NQ, causal, dtype, lens = case
+    w = P.small(B=B, H=H, KV=KV, D=D, BS=BS, NQ=NQ, causal=causal, dtype=dtype, lens=lens,
+                seed=13 + NQ)
+    return P.append_problem(w, **kw)
+
+
+def _append(w, slots, lib=None):
+    return oracle.paged_decode_append(*P.args(w)[:7], slots, w.scale, causal=w.spec.causal,
+                                      lib=lib)
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=lambda c: "-".join(map(str, c[:8])))
+def test_append_rows_come_back_through_the_block_table(case):
+    w, slots, reads = _append_case(case, seed=3)
+    assert not reads
+    out, kp, vp = _append(w, slots)
+    s = w.spec
+    written = np.zeros((w.num_blocks, s.BS), dtype=bool)
+    for b, L in enumerate(w.context_lens):
+        for j in range(s.NQ):
+            i = int(L) + j  # logical position of new row j, read through the table
+            phys = int(w.block_table[b, i // s.BS])
+            assert torch.equal(_bits(kp[phys, i % s.BS]), _bits(w.new_k[b, :, j]))
+            assert torch.equal(_bits(vp[phys, i % s.BS]), _bits(w.new_v[b, :, j]))
+            written[phys, i % s.BS] = True
+    keep = torch.from_numpy(~written)
+    assert torch.equal(_bits(kp)[keep], _bits(w.k_pool)[keep])
+    assert torch.equal(_bits(vp)[keep], _bits(w.v_pool)[keep])
+    # nothing cached was re-written, so the attention is the plain step's
+    assert np.array_equal(out, _ora(w))
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=lambda c: "-".join(map(str, c[:8])))
+def test_overwritten_cached_positions_read_the_new_row(case):
+    w, slots, reads = _append_case(case, overwrite=3, duplicate=True, seed=4)
+    assert reads
+    out, _, _ = _append(w, slots)
+    assert np.abs(out - _dense_with_reads(w, reads, w.spec.causal)).max() < 1e-12
+    # and differs from the unpatched step
+    assert np.abs(out - _ora(w)).max() > 1e-6
+
+
+def test_negative_and_out_of_range_slots_are_neither_stored_nor_read():
+    case = APPEND_CASES[1]
+    w, slots, reads = _append_case(case, overwrite=2, negative=3, out_of_range=3, seed=6)
+    out, kp, vp = _append(w, slots)
+    s = w.spec
+    n_slots = w.num_blocks * s.BS
+    changed = (_bits(kp) != _bits(w.k_pool)).reshape(n_slots, -1).any(dim=1)
+    expect = torch.zeros(n_slots, dtype=torch.bool)
+    for b in range(s.B):
+        for j in range(s.NQ):
+            if 0 <= slots[b, j] < n_slots:
+                expect[int(slots[b, j])] = True
+    assert torch.equal(changed, expect)
+    assert np.abs(out - _dense_with_reads(w, reads, s.causal)).max() < 1e-12
+
+
+# --------------------------------------------------------------------------
 # Mutation check: each planted mistake must trip at least one pin.
 # --------------------------------------------------------------------------
 def _pins(lib):
@@ -236,6 +332,16 @@ def _pins(lib):
                 or oracle.widen(h16.view(torch.float16), 1, lib) != 2.0 ** -24
                 or oracle.widen(h16.view(torch.float16), 0, lib) != 1.0):
             failed.append("widen")
+        w, slots, _ = _append_case(APPEND_CASES[1], seed=3)
+        _, kp, _ = _append(w, slots, lib)
+        L = int(w.context_lens[1])
+        phys = int(w.block_table[1, (L + 2) // w.spec.BS])
+        if not torch.equal(_bits(kp[phys, (L + 2) % w.spec.BS]), _bits(w.new_k[1, :, 2])):
+            failed.append("append_round_trip")
+        w, slots, reads = _append_case(APPEND_CASES[1], overwrite=3, duplicate=True, seed=4)
+        out, _, _ = _append(w, slots, lib)
+        if np.abs(out - _dense_with_reads(w, reads, True)).max() > 1e-12:
+            failed.append("append_overwrite")
     except ValueError:
         failed.append("rejected")
     return failed
@@ -257,6 +363,14 @@ MUTATIONS = {
     "bf16_shift": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
     "half_exponent_bias": ("exponent - 25", "exponent - 24"),
     "new_rows_from_wrong_head": ("(((int64_t)b * KV + kh) * NQ + j) * D", "(((int64_t)b * KV) * NQ + j) * D"),
+    "append_rows_in_reverse": ("for (int j = 0; j < NQ; ++j) {\n            const int64_t slot",
+                               "for (int j = NQ - 1; j >= 0; --j) {\n            const int64_t slot"),
+    "append_slot_as_block": ("const int64_t dst = slot * row_bytes",
+                             "const int64_t dst = (slot / BS) * row_bytes"),
+    "append_first_head_only": ("for (int kh = 0; kh < KV; ++kh) {\n                const int64_t row",
+                               "for (int kh = 0; kh < 1; ++kh) {\n                const int64_t row"),
+    "append_rows_of_head_0": ("const int64_t row = ((int64_t)b * KV + kh) * NQ + j;",
+                              "const int64_t row = ((int64_t)b * KV) * NQ + j;"),
 }
 
 
