@@ -148,7 +148,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--repeats", type=int, default=5,
                     help="extra timed regions of K steps after the headline one, for the "
                          "median / p10 / p90 of the per-step time")
@@ -248,6 +248,34 @@ def main():
     log(f"[bench] {ms_per_step * 1e3:.2f} us/step (region), pass 1 {mean_pass1 * 1e3:.2f} us, "
         f"combine {mean_comb * 1e3:.2f} us, wall {wall / K * 1e6:.2f} us/step, {value:.1f} GB/s")
 
+    # The slot-patched step (paged_attn_decode_append): the same step also
+    # storing every new row into a spare slot past the cached blocks (the pools
+    # get ceil(B*NQ/BS) extra blocks; nothing cached is overwritten, so no read
+    # is patched): what the store and the per-sub-page slot checks cost.
+    spare = -(-(spec.B * spec.NQ) // spec.BS)
+    nb = kpools[0].shape[0]
+    kpools = [torch.cat([p, p.new_zeros((spare,) + tuple(p.shape[1:]))]) for p in kpools]
+    vpools = [torch.cat([p, p.new_zeros((spare,) + tuple(p.shape[1:]))]) for p in vpools]
+    flat = torch.arange(spec.B * spec.NQ, device=dev, dtype=torch.int64)
+    slots = ((nb + flat // spec.BS) * spec.BS + flat % spec.BS).to(torch.int32).view(spec.B, spec.NQ)
+    dec_a = pa.Decoder(w.q, kpools[0], table, max_context_len=w.max_context_len,
+                       causal=spec.causal, num_partitions=args.partitions, kernel=args.kernel)
+
+    def step_append(i):
+        r = i % len(kpools)
+        dec_a(w.q, kpools[r], vpools[r], table, lens, w.new_k, w.new_v, w.scale, stream=stream,
+              slot_mapping=slots)
+
+    for i in range(args.warmup):
+        step_append(i)
+    ms_append = timed(step_append, K)
+    ms_plain_ext = timed(step, K)  # the plain step on the same (extended) pools
+    elem = 4 if spec.dtype == "f32" else 2
+    stored = spec.B * spec.NQ * spec.KV * spec.D * 2 * elem
+    log(f"[bench] slot-patched step {ms_append * 1e3:.2f} us/step "
+        f"({kvb / (ms_append / 1e3) / 1e9:.1f} GB/s of KV reads, {stored} B stored); "
+        f"plain step on the same pools {ms_plain_ext * 1e3:.2f} us/step")
+
     copy_gbps = copy_bandwidth(torch)
     log(f"[bench] device copy bandwidth {copy_gbps:.0f} GB/s (read+write)")
     traffic = measured_traffic(spec.name, kvb)
@@ -301,6 +329,14 @@ def main():
             "median_us_per_step": round(statistics.median(reps), 2) if reps else None,
             "p10_us_per_step": round(percentile(reps, 10), 2) if reps else None,
             "p90_us_per_step": round(percentile(reps, 90), 2) if reps else None,
+        },
+        "append_step": {
+            "entry_point": "paged_attn_decode_append",
+            "us_per_step": round(ms_append * 1e3, 2),
+            "plain_step_same_pools_us": round(ms_plain_ext * 1e3, 2),
+            "kv_gbps": round(kvb / (ms_append / 1e3) / 1e9, 2),
+            "stored_bytes_per_step": stored,
+            "slots": "every new row into a spare slot past the cached blocks (no read patched)",
         },
         "device_copy_gbps": round(copy_gbps, 1),
         "cpu_baseline": cpu,

@@ -20,7 +20,8 @@
  * Conventions shared by every entry point
  *   - All pointers to tensors are DEVICE pointers owned by the caller; the
  *     library never allocates, frees, copies to the host or synchronises in
- *     paged_attn_decode / paged_attn_combine. Tensors are contiguous row-major.
+ *     paged_attn_decode / paged_attn_decode_append / paged_attn_combine.
+ *     Tensors are contiguous row-major.
  *   - Element type of q, pools, new_k, new_v and out: pa_problem.dtype.
  *   - Layouts:
  *       q, out        [batch, num_heads, nq, head_dim]
@@ -169,6 +170,37 @@ int paged_attn_decode(const pa_problem* problem, const void* q, const void* k_po
                       pa_stream_t stream);
 
 /*
+ * The slot-patched step: one decode-attention step that also stores this
+ * step's new rows into the pools (page: VECTOR_BODY's `position` slots, where
+ * a cached position whose token slot is named by a new row reads that row;
+ * the docs.rs page "onnxruntime-ep-mlx 0.31.1: src/engine.rs",
+ * write_back_input_patches, copies such rows back into their cache slots, one
+ * complete token row per slot).
+ *   slot_mapping  int32 [batch, nq], device: token slot s = block * block_size
+ *                 + offset of new row j of sequence b; negative, or >=
+ *                 num_blocks * block_size: the row is neither stored nor read
+ *                 back.
+ * Effects, as if the rows were stored first and then the step ran:
+ *   - k_pool/v_pool[s / block_size, s % block_size, kh, :] = new_k/new_v[b, kh,
+ *     j, :] for every KV head; when several rows of one sequence name the same
+ *     slot, the highest j is the one stored;
+ *   - a cached position i < context_lens[b] of sequence b whose slot (through
+ *     the block table) some new row of sequence b names reads that row (the
+ *     highest such j) instead of the pool; the new rows themselves are attended
+ *     exactly as in paged_attn_decode.
+ * The pools are written (the other arguments as in paged_attn_decode). Caller
+ * contract (not checked on the device): a slot named by one sequence is neither
+ * named by nor a cached position of another sequence in the same call. Errors:
+ * those of paged_attn_decode, and PA_ERR_INVALID_ARG for a NULL or misaligned
+ * slot_mapping.
+ */
+int paged_attn_decode_append(const pa_problem* problem, const void* q, void* k_pool,
+                             void* v_pool, const int32_t* block_table,
+                             const int32_t* context_lens, const void* new_k, const void* new_v,
+                             const int32_t* slot_mapping, float scale, void* out,
+                             void* workspace, size_t workspace_bytes, pa_stream_t stream);
+
+/*
  * Merge step alone (page: PARTIALS_REDUCE), as its own kernel. Reads the
  * partial states a partitioned paged_attn_decode left in `workspace` for the
  * same problem and
@@ -187,7 +219,7 @@ int paged_attn_combine(const pa_problem* problem, const int32_t* context_lens,
 const char* paged_attn_last_error(void);
 
 /* ABI version of this header (major * 100 + minor). */
-int paged_attn_version(void);  /* 101: pa_problem.flags */
+int paged_attn_version(void);  /* 102: paged_attn_decode_append */
 
 #ifdef __cplusplus
 }

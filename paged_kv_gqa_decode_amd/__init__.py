@@ -23,8 +23,8 @@ PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
 PA_FLAG_DEFER_COMBINE = 1
 
 EXPORTED = ("pa_plan_ex", "pa_plan", "pa_workspace_size", "pa_workspace_size_ex",
-            "paged_attn_decode", "paged_attn_combine", "paged_attn_last_error",
-            "paged_attn_version")
+            "paged_attn_decode", "paged_attn_decode_append", "paged_attn_combine",
+            "paged_attn_last_error", "paged_attn_version")
 
 
 class PaProblem(ctypes.Structure):
@@ -67,6 +67,9 @@ def library(path: Optional[str] = None):
     lib.pa_workspace_size_ex.argtypes = [P, ctypes.c_int32, szp]
     lib.paged_attn_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
                                       ctypes.c_size_t, vp]
+    lib.paged_attn_decode_append.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
+                                             vp, vp, ctypes.c_size_t, vp]
+    lib.paged_attn_decode_append.restype = ctypes.c_int
     lib.paged_attn_combine.argtypes = [P, vp, vp, ctypes.c_size_t, vp, vp]
     lib.paged_attn_last_error.argtypes = []
     lib.paged_attn_last_error.restype = ctypes.c_char_p
@@ -153,6 +156,19 @@ def paged_attn_decode(problem: PaProblem, q, k_pool, v_pool, block_table, contex
     return rc
 
 
+def paged_attn_decode_append(problem: PaProblem, q, k_pool, v_pool, block_table, context_lens,
+                             new_k, new_v, slot_mapping, scale: float, out, workspace=None,
+                             workspace_bytes: int = 0, stream=None,
+                             raise_on_error: bool = True) -> int:
+    rc = library().paged_attn_decode_append(
+        ctypes.byref(problem), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+        _ptr(context_lens), _ptr(new_k), _ptr(new_v), _ptr(slot_mapping), ctypes.c_float(scale),
+        _ptr(out), _ptr(workspace), ctypes.c_size_t(workspace_bytes), _stream(stream))
+    if raise_on_error:
+        _check(rc)
+    return rc
+
+
 def paged_attn_combine(problem: PaProblem, context_lens, workspace, workspace_bytes: int, out,
                        stream=None, raise_on_error: bool = True) -> int:
     rc = library().paged_attn_combine(ctypes.byref(problem), _ptr(context_lens), _ptr(workspace),
@@ -207,13 +223,22 @@ class Decoder:
         self.out = torch.empty_like(q)
 
     def __call__(self, q, k_pool, v_pool, block_table, context_lens, new_k, new_v, scale,
-                 out=None, stream=None):
+                 out=None, stream=None, slot_mapping=None):
+        """One step; with slot_mapping (int32 [B, NQ]) the slot-patched step that
+        also stores the new rows into the pools."""
         import torch
         out = self.out if out is None else out
         if stream is None:
             stream = torch.cuda.current_stream()
-        paged_attn_decode(self.problem, q, k_pool, v_pool, block_table, context_lens, new_k,
-                          new_v, scale, out, self.workspace, self.workspace_bytes, stream)
+        if slot_mapping is None:
+            paged_attn_decode(self.problem, q, k_pool, v_pool, block_table, context_lens, new_k,
+                              new_v, scale, out, self.workspace, self.workspace_bytes, stream)
+        else:
+            assert slot_mapping.dtype == torch.int32 and slot_mapping.is_contiguous()
+            assert tuple(slot_mapping.shape) == (q.shape[0], q.shape[2])
+            paged_attn_decode_append(self.problem, q, k_pool, v_pool, block_table, context_lens,
+                                     new_k, new_v, slot_mapping, scale, out, self.workspace,
+                                     self.workspace_bytes, stream)
         return out
 
 
@@ -225,3 +250,13 @@ def decode(q, k_pool, v_pool, block_table, context_lens, new_k, new_v, scale: fl
                   num_partitions=num_partitions, kernel=kernel)
     return dec(q, k_pool, v_pool, block_table, context_lens, new_k, new_v, scale, out=out,
                stream=stream)
+
+
+def decode_append(q, k_pool, v_pool, block_table, context_lens, new_k, new_v, slot_mapping,
+                  scale: float, *, max_context_len: int, causal: bool = True,
+                  num_partitions: int = 0, kernel: int = PA_KERNEL_AUTO, out=None, stream=None):
+    """The slot-patched step: returns out and stores the new rows into k_pool/v_pool."""
+    dec = Decoder(q, k_pool, block_table, max_context_len=max_context_len, causal=causal,
+                  num_partitions=num_partitions, kernel=kernel)
+    return dec(q, k_pool, v_pool, block_table, context_lens, new_k, new_v, scale, out=out,
+               stream=stream, slot_mapping=slot_mapping)

@@ -137,6 +137,7 @@ struct SplitArgs {
     SplitGeometry g;
     int H, causal, max_blocks, R;
     float qscale;  // scale * log2(e)
+    AppendArgs ap; // slot-patched step (ap.slots == nullptr: plain step)
 };
 
 // LDS layout of one sub-page slot (16 keys), filled by row-coalesced 16-byte
@@ -208,16 +209,20 @@ struct SubPageStream {
 
     const SplitArgs<T>& a;
     const int32_t* __restrict__ table;  // block table; entries are read with scalar loads
+    const int32_t* __restrict__ slots;  // slot-patched step: [B][NQ] (a.ap.slots), else nullptr
     const int* s_pref;
     const int* s_len;
     int KV, NQ, kh, nnew, tbytes, lane;
     int kfb;  // per-lane K fetch offset of a cached sub-page (instruction 0)
     int pre_phys = 0;  // table entry of the last prefetch_table() position
+    int pat_b = -1;    // slot-patched step: sequence whose slot range is held
+    int64_t pat_lo = 0, pat_hi = -1;  // smallest and largest slot its new rows name
 
     __device__ __forceinline__ SubPageStream(const SplitArgs<T>& args,
-                                             const int32_t* __restrict__ tab, const int* pref,
+                                             const int32_t* __restrict__ tab,
+                                             const int32_t* __restrict__ sl, const int* pref,
                                              const int* lens, int head, int ln)
-        : a(args), table(tab), s_pref(pref), s_len(lens), KV(args.g.KV), NQ(args.g.NQ), kh(head),
+        : a(args), table(tab), slots(sl), s_pref(pref), s_len(lens), KV(args.g.KV), NQ(args.g.NQ), kh(head),
           nnew((args.g.NQ + 15) / 16), tbytes(args.g.KV * D * (int)sizeof(T)), lane(ln) {
         kfb = Lay::k_fetch_base(lane, tbytes);
     }
@@ -329,6 +334,96 @@ struct SubPageStream {
                                                          koff, 0, 0, 0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(v_lds + i * 1024), 16,
                                                          voff, 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- slot-patched step (AppendArgs) ----
+    // Whether a new row of sequence c.b names the slot of a valid key of cached
+    // sub-page c in block `phys` (wave-uniform). The range of slots the
+    // sequence's rows name is kept per sequence, so the rows themselves are
+    // only compared for sub-pages inside it.
+    __device__ __forceinline__ bool patched(const Cur& c, int64_t phys) {
+        if (c.j >= c.nc) return false;
+        const int32_t* sl = slots + (int64_t)c.b * NQ;
+        if (c.b != pat_b) {
+            pat_b = c.b;
+            pat_lo = INT64_MAX;
+            pat_hi = -1;
+            for (int j = 0; j < NQ; ++j) {
+                pat_lo = min(pat_lo, (int64_t)sl[j]);
+                pat_hi = max(pat_hi, (int64_t)sl[j]);
+            }
+        }
+        const int64_t base = phys * BS + 16 * (c.j % SUB);
+        const int valid = min(16, c.L - 16 * c.j);
+        if (base + valid <= pat_lo || base > pat_hi) return false;
+        bool any = false;
+        for (int j = 0; j < NQ; ++j) {
+            const int64_t t = (int64_t)sl[j] - base;
+            any = any || (t >= 0 && t < valid);
+        }
+        return any;
+    }
+    // Overwrites, in LDS slot `slot` holding cached sub-page c, each key whose
+    // pool slot a new row of the sequence names with that row (rows in order,
+    // so the last one naming a slot stays). Lanes 0 .. kChunks - 1 move the K
+    // row's 16-byte chunks, the next kChunks lanes the V row's. A rare, slow
+    // path: it ends with every vector-memory operation of the wave complete.
+    __device__ __forceinline__ void patch(const Cur& c, char* slot) const {
+        typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+        const int64_t base = (int64_t)table_entry(c) * BS + 16 * (c.j % SUB);
+        const int valid = min(16, c.L - 16 * c.j);
+        const int32_t* sl = slots + (int64_t)c.b * NQ;
+        const uint32_t slot_lds = (uint32_t)reinterpret_cast<uintptr_t>(slot);
+        for (int j = 0; j < NQ; ++j) {
+            const int64_t t = (int64_t)sl[j] - base;
+            if (t < 0 || t >= valid) continue;
+            const int64_t row = (((int64_t)c.b * KV + kh) * NQ + j) * D;
+            if (lane < Lay::kChunks) {
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.new_k + row + 8 * lane);
+                *(lds_u32x4*)(uintptr_t)(slot_lds + Lay::k_addr((int)t, lane)) = v;
+            } else if (lane < 2 * Lay::kChunks) {
+                const int ch = lane - Lay::kChunks;
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.new_v + row + 8 * ch);
+                *(lds_u32x4*)(uintptr_t)(slot_lds + Lay::kKBytes + Lay::v_addr((int)t, ch)) = v;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
+    // Stores the new rows of sub-page c (new rows, in LDS slot `slot`) that the
+    // step keeps into their pool slots, head kh of each: row j goes to slot s =
+    // slots[b][j] when 0 <= s < n_slot and no later row of the sequence names
+    // s. The sequence's slots are loaded once, lane l holding rows l and 64 + l,
+    // and the later rows are found with a ballot (nq <= 128). Their load is
+    // waited for at once on every path (one drain of the wave's loads per unit);
+    // the stores are not waited for.
+    __device__ __forceinline__ void store_new(const Cur& c, const char* slot) const {
+        typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
+        const int t0 = 16 * (c.j - c.nc);
+        const int valid = min(16, NQ - t0);
+        const int32_t* sl = slots + (int64_t)c.b * NQ;
+        int32_t m0 = lane < NQ ? sl[lane] : -1;
+        int32_t m1 = 64 + lane < NQ ? sl[64 + lane] : -1;
+        asm volatile("" : "+v"(m0), "+v"(m1));  // consumed here, whatever the loop below does
+        const uint32_t slot_lds = (uint32_t)reinterpret_cast<uintptr_t>(slot);
+        T* const kd = static_cast<T*>(a.ap.k_dst);
+        T* const vd = static_cast<T*>(a.ap.v_dst);
+        for (int t = 0; t < valid; ++t) {
+            const int j = t0 + t;
+            const int32_t s = __builtin_amdgcn_readlane(j < 64 ? m0 : m1, j & 63);
+            const bool later = __ballot(lane > j && lane < NQ && m0 == s) != 0 ||
+                               __ballot(64 + lane > j && 64 + lane < NQ && m1 == s) != 0;
+            if (s < 0 || s >= a.ap.n_slot || later) continue;
+            const int64_t row = ((int64_t)s * KV + kh) * D;
+            if (lane < Lay::kChunks) {
+                const u32x4_t v = *(lds_u32x4*)(uintptr_t)(slot_lds + Lay::k_addr(t, lane));
+                *reinterpret_cast<u32x4_t*>(kd + row + 8 * lane) = v;
+            } else if (lane < 2 * Lay::kChunks) {
+                const int ch = lane - Lay::kChunks;
+                const u32x4_t v =
+                    *(lds_u32x4*)(uintptr_t)(slot_lds + Lay::kKBytes + Lay::v_addr(t, ch));
+                *reinterpret_cast<u32x4_t*>(vd + row + 8 * ch) = v;
             }
         }
     }
@@ -590,9 +685,10 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
 // before the arithmetic; otherwise after the scores, so that the next
 // sequence's Q, loaded after the scores, is older than the refill), then
 // computes. NS sub-pages per wave stay in flight.
-template <typename T, int D, int BS, int NRT, int NS, int WPS>
+template <typename T, int D, int BS, int NRT, int NS, int WPS, bool APPEND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPS, WPS)))
-void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table) {
+void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table,
+                 const int32_t* __restrict__ slots) {
     using Lay = SlotLayout<T, D>;
     using Stream = SubPageStream<T, D, BS>;
     using Rows = RowTiles<T, D, NRT>;
@@ -620,19 +716,24 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table) {
     const int n_total = (int)(cut.start(grp + 1) - x0);  // sub-pages this wave attends (>= 1)
     char* const ring = smem + wave * NS * Lay::kBytes;
 
-    Stream st(a, table, s_pref, s_len, kh, lane);
+    Stream st(a, table, slots, s_pref, s_len, kh, lane);
     Rows rows(a, lane, 0);
     Cur cc = st.seek(x0);  // the sub-page being attended
     Cur pc = cc;           // the next sub-page to fetch
     rows.load_q(cc.b, kh);  // older than every fetch: the first wait covers it
     // prime the ring with sub-pages 0 .. min(NS, n_total) - 1
     const int nf = min(NS, n_total);
+    uint32_t pmask = 0;  // bit k: the sub-page in slot k has keys to patch (slot-patched step)
     {
         int phys[NS];
         st.run_tables(cc, nf, phys);
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
-            if (k < nf) st.fetch(st.locate_at(pc, phys[k]), ring + k * Lay::kBytes, pc.j < pc.nc);
+            if (k < nf) {
+                if constexpr (APPEND)
+                    if (st.patched(pc, phys[k])) pmask |= 1u << k;
+                st.fetch(st.locate_at(pc, phys[k]), ring + k * Lay::kBytes, pc.j < pc.nc);
+            }
             if (k + 1 < nf) st.step(pc);
         }
         if (nf < n_total) st.step(pc);
@@ -660,6 +761,10 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table) {
             q_pending = false;
         }
         char* const slot = ring + (i % NS) * Lay::kBytes;
+        if constexpr (APPEND) {
+            if ((pmask >> (i % NS)) & 1u) st.patch(cc, slot);  // cached keys re-written this step
+            if (cc.j >= cc.nc) st.store_new(cc, slot);         // this step's rows into the pools
+        }
         u32x4_t kop[KS];
         u32x2_t vt[D / 16];
         rows.read_k(slot, kop);
@@ -668,6 +773,7 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table) {
         if constexpr (NS == 1) {
             if (refill) {
                 const typename Stream::Src sn = st.locate(pc);
+                if constexpr (APPEND) pmask = st.patched(pc, st.pre_phys) ? 1u : 0u;
                 Rows::lds_wait(vt);  // slot read out
                 st.fetch(sn, slot, pc.j < pc.nc);
             } else {
@@ -690,6 +796,10 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table) {
         }
         if constexpr (NS > 1) {
             if (refill) {
+                if constexpr (APPEND) {
+                    const uint32_t bit = 1u << (i % NS);
+                    pmask = st.patched(pc, st.pre_phys) ? (pmask | bit) : (pmask & ~bit);
+                }
                 st.fetch(st.locate(pc), slot, pc.j < pc.nc);  // slot already read out
                 ++q_younger;
             }
@@ -718,9 +828,10 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table) {
 // sub-pages per workgroup stay in flight during the arithmetic. A sequence
 // switch loads the waves' new Q after the arithmetic (it is waited for at the
 // next iteration, a rare full drain).
-template <typename T, int D, int BS, int NW, int NRT, int kRing, int WPS>
+template <typename T, int D, int BS, int NW, int NRT, int kRing, int WPS, bool APPEND>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPS, WPS)))
-void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table) {
+void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table,
+                      const int32_t* __restrict__ slots) {
     using Lay = SlotLayout<T, D>;
     using Stream = SubPageStream<T, D, BS>;
     using Rows = RowTiles<T, D, NRT>;
@@ -747,20 +858,25 @@ void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table) {
     const bool issues = wave < NWI;  // this wave loads instructions wave, wave + NWI, ...
     const bool has_rows = 16 * NRT * wave < a.R;
 
-    Stream st(a, table, s_pref, s_len, kh, lane);
+    Stream st(a, table, slots, s_pref, s_len, kh, lane);
     Rows rows(a, lane, wave * NRT);
     Cur cc = st.seek(x0);
     Cur pc = cc;  // next sub-page to fetch: kRing - 1 ahead of cc once primed
     if (has_rows) rows.load_q(cc.b, kh);  // older than the ring's loads
+    uint32_t pmask = 0;  // bit k: the sub-page in slot k has keys to patch (slot-patched step)
     {
         const int np = min(kRing - 1, n_total);
         int phys[kRing - 1];
         st.run_tables(cc, np, phys);
 #pragma unroll
         for (int k = 0; k < kRing - 1; ++k) {
-            if (k < np && issues)
-                st.template fetch<IPW>(st.locate_at(pc, phys[k]), smem + k * Lay::kBytes, pc.j < pc.nc,
-                                       wave, NWI);
+            if (k < np) {
+                if constexpr (APPEND)
+                    if (st.patched(pc, phys[k])) pmask |= 1u << k;
+                if (issues)
+                    st.template fetch<IPW>(st.locate_at(pc, phys[k]), smem + k * Lay::kBytes,
+                                           pc.j < pc.nc, wave, NWI);
+            }
             if (k + 1 < n_total && k + 1 <= np) st.step(pc);
         }
     }
@@ -794,9 +910,23 @@ void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
+        if constexpr (APPEND) {
+            char* const cur = smem + (i % kRing) * Lay::kBytes;
+            if ((pmask >> (i % kRing)) & 1u) {  // cached keys re-written this step (uniform)
+                if (wave == 0) st.patch(cc, cur);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+            }
+            if (cc.j >= cc.nc && wave == 0) st.store_new(cc, cur);  // into the pools
+        }
         // refill the slot of sub-page i - 1 with sub-page i + kRing - 1
         const int nxt = i + kRing - 1;
         if (nxt < n_total) {
+            if constexpr (APPEND) {
+                const uint32_t bit = 1u << (nxt % kRing);
+                pmask = st.patched(pc, st.pre_phys) ? (pmask | bit) : (pmask & ~bit);
+            }
             const typename Stream::Src sn = st.locate(pc);
             if (issues)
                 st.template fetch<IPW>(sn, smem + (nxt % kRing) * Lay::kBytes, pc.j < pc.nc, wave, NWI);

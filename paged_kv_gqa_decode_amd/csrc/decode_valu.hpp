@@ -102,7 +102,7 @@ __device__ __forceinline__ void valu_attend(const uint4 (&kr)[NTOK], const uint4
     }
 }
 
-template <typename T, int D, int BS, int RT>
+template <typename T, int D, int BS, int RT, bool APPEND>
 __global__ __launch_bounds__(256) void decode_valu(DecodeArgs<T> a) {
     using E = Elem<T>;
     constexpr int VEC = E::kVec;
@@ -155,14 +155,27 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs<T> a) {
     const int pg_end = tok_end > tok_begin ? (tok_end + BS - 1) / BS : pg_begin;
     int n = pg_begin + wave;
     if (n < pg_end) {
+        // Slot-patched step: a key whose pool slot a new row of the sequence
+        // names reads that row (the last one naming it) instead of the pool.
+        const int32_t* sl = APPEND ? a.ap.slots + (int64_t)b * a.NQ : nullptr;
+        const int64_t nrow0 = ((int64_t)b * a.KV + kh) * a.NQ;
         auto load_page = [&](int page, uint4(&kr)[NTOK], uint4(&vr)[NTOK]) {
             const int64_t phys = trow[page];
             const int64_t off = (phys * BS * a.KV + kh) * D + j * VEC;
 #pragma unroll
             for (int i = 0; i < NTOK; ++i) {
                 const int64_t t = g + TPI * i;
-                kr[i] = load16(a.k_pool + off + t * tstride);
-                vr[i] = load16(a.v_pool + off + t * tstride);
+                int src = -1;
+                if constexpr (APPEND)
+                    for (int jn = 0; jn < a.NQ; ++jn)
+                        if (sl[jn] == phys * BS + t) src = jn;
+                if (src < 0) {
+                    kr[i] = load16(a.k_pool + off + t * tstride);
+                    vr[i] = load16(a.v_pool + off + t * tstride);
+                } else {
+                    kr[i] = load16(a.new_k + (nrow0 + src) * D + j * VEC);
+                    vr[i] = load16(a.new_v + (nrow0 + src) * D + j * VEC);
+                }
             }
         };
         uint4 kr[NTOK], vr[NTOK];
@@ -200,6 +213,15 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeArgs<T> a) {
                 if (t < a.NQ) {
                     kr[i] = load16(a.new_k + nbase + (int64_t)t * D);
                     vr[i] = load16(a.new_v + nbase + (int64_t)t * D);
+                    // slot-patched step: row t into its pool slot (one tile stores it)
+                    if (APPEND && tile == 0) {
+                        const int32_t* sr = a.ap.slots + (int64_t)b * a.NQ;
+                        if (stores_row(sr, a.NQ, t, a.ap.n_slot)) {
+                            const int64_t dst = ((int64_t)sr[t] * a.KV + kh) * D + j * VEC;
+                            *reinterpret_cast<uint4*>(static_cast<T*>(a.ap.k_dst) + dst) = kr[i];
+                            *reinterpret_cast<uint4*>(static_cast<T*>(a.ap.v_dst) + dst) = vr[i];
+                        }
+                    }
                 } else {
                     kr[i] = make_uint4(0, 0, 0, 0);
                     vr[i] = make_uint4(0, 0, 0, 0);

@@ -27,6 +27,7 @@ struct DecodeArgs {
     float* ws_ml;        // [rows][n_parts][2]  (max, sum) in base-2 units
     int H, KV, NQ, causal, max_blocks, chunk, n_parts, n_tiles;
     float qscale;        // scale * log2(e)
+    AppendArgs ap;       // slot-patched step (ap.slots == nullptr: plain step)
 };
 
 // Partitions sequence b uses: one per `chunk` cached keys (at least one, for

@@ -128,4 +128,28 @@ __device__ __forceinline__ float across_groups_sum(float x) {
 __device__ __forceinline__ float wave_max(float x) { return across_groups_max<1>(x); }
 __device__ __forceinline__ float wave_sum(float x) { return across_groups_sum<1>(x); }
 
+// The slot-patched step (docs.rs page "onnxruntime-ep-mlx 0.31.1:
+// src/ops/paged_attention.rs", VECTOR_BODY's `position` slots; the page
+// "onnxruntime-ep-mlx 0.31.1: src/engine.rs", write_back_input_patches): new row j of sequence b is stored into token
+// slot slots[b*NQ + j] (block * BS + offset) of both pools, every KV head, and
+// a cached position of sequence b whose slot one of its new rows names reads
+// that row instead of the pool (the highest such j). Slots outside [0, n_slot)
+// are neither stored nor read.
+struct AppendArgs {
+    const int32_t* slots;  // [B][NQ]; nullptr: the plain step (pools read only)
+    void* k_dst;           // the pools, written (the same memory as k_pool / v_pool)
+    void* v_dst;
+    int64_t n_slot;        // num_blocks * block_size
+};
+
+// New row j is the one stored in slot s: s is a real slot and no later new row
+// of the sequence names it (sl = the sequence's NQ slots).
+__device__ __forceinline__ bool stores_row(const int32_t* sl, int NQ, int j, int64_t n_slot) {
+    const int32_t s = sl[j];
+    if (s < 0 || s >= n_slot) return false;
+    for (int jj = j + 1; jj < NQ; ++jj)
+        if (sl[jj] == s) return false;
+    return true;
+}
+
 }  // namespace pa

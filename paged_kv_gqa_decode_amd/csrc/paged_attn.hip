@@ -328,31 +328,48 @@ int validate_tensors(const pa_problem* p, const void* q, const void* k_pool, con
 // ---------------------------------------------------------------------------
 // Kernel dispatch over the compile-time shapes.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int BS>
-void launch_valu(const Plan& pl, dim3 grid, hipStream_t s, const pa::DecodeArgs<T>& a) {
+template <typename T, int D, int BS, bool APPEND>
+void launch_valu_k(const Plan& pl, dim3 grid, hipStream_t s, const pa::DecodeArgs<T>& a) {
     switch (pl.rt) {
-        case 1: hipLaunchKernelGGL((pa::decode_valu<T, D, BS, 1>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((pa::decode_valu<T, D, BS, 2>), grid, dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((pa::decode_valu<T, D, BS, 4>), grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((pa::decode_valu<T, D, BS, 8>), grid, dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((pa::decode_valu<T, D, BS, 1, APPEND>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((pa::decode_valu<T, D, BS, 2, APPEND>), grid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((pa::decode_valu<T, D, BS, 4, APPEND>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((pa::decode_valu<T, D, BS, 8, APPEND>), grid, dim3(256), 0, s, a); break;
     }
 }
 
 template <typename T, int D, int BS>
-void launch_mfma(const pa_problem* p, const Plan& pl, size_t lds, hipStream_t s,
-                 const pa::SplitArgs<T>& a, const int32_t* table) {
+void launch_valu(const Plan& pl, dim3 grid, hipStream_t s, const pa::DecodeArgs<T>& a) {
+    if (a.ap.slots) launch_valu_k<T, D, BS, true>(pl, grid, s, a);
+    else launch_valu_k<T, D, BS, false>(pl, grid, s, a);
+}
+
+template <typename T, int D, int BS, bool APPEND>
+void launch_mfma_k(const pa_problem* p, const Plan& pl, size_t lds, hipStream_t s,
+                   const pa::SplitArgs<T>& a, const int32_t* table) {
     constexpr int S1 = D == 128 ? 1 : 2;  // slot counts of mfma_shape
     const int64_t streams = (int64_t)pl.parts * p->num_kv_heads;
     if (pl.rt == 1) {
         const dim3 grid((unsigned)ceil_div(streams, 4));
-        hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 1, 2 * S1, 2>), grid, dim3(256), lds, s, a, table);
+        hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 1, 2 * S1, 2, APPEND>), grid, dim3(256), lds,
+                           s, a, table, a.ap.slots);
     } else if (pl.rt == 2) {
         const dim3 grid((unsigned)ceil_div(streams, 4));
-        hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 2, 2 * S1, 2>), grid, dim3(256), lds, s, a, table);
+        hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 2, 2 * S1, 2, APPEND>), grid, dim3(256), lds,
+                           s, a, table, a.ap.slots);
     } else {
-        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2, 2, 4 * S1, 2>), dim3((unsigned)streams),
-                           dim3(128), lds, s, a, table);
+        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2, 2, 4 * S1, 2, APPEND>),
+                           dim3((unsigned)streams), dim3(128), lds, s, a, table, a.ap.slots);
     }
+}
+
+// The plain step and the slot-patched step are separate instantiations, so the
+// plain kernels carry none of the patching code.
+template <typename T, int D, int BS>
+void launch_mfma(const pa_problem* p, const Plan& pl, size_t lds, hipStream_t s,
+                 const pa::SplitArgs<T>& a, const int32_t* table) {
+    if (a.ap.slots) launch_mfma_k<T, D, BS, true>(p, pl, lds, s, a, table);
+    else launch_mfma_k<T, D, BS, false>(p, pl, lds, s, a, table);
 }
 
 pa::SplitGeometry split_geometry(const pa_problem* p, const Plan& pl) {
@@ -390,6 +407,7 @@ void launch_pass1_mfma(const pa_problem* p, const Plan& pl, hipStream_t s,
     a.max_blocks = p->max_blocks_per_seq;
     a.R = (p->num_heads / p->num_kv_heads) * p->nq;
     a.qscale = d.qscale;
+    a.ap = d.ap;
     const size_t lds = mfma_lds_bytes(p, pl.rt);
     if (p->head_dim == 64) {
         if (p->block_size == 16) launch_mfma<T, 64, 16>(p, pl, lds, s, a, d.block_table);
@@ -474,8 +492,12 @@ template <typename T>
 int run_decode(const pa_problem* p, const Plan& pl, const void* q, const void* k_pool,
                const void* v_pool, const int32_t* block_table, const int32_t* context_lens,
                const void* new_k, const void* new_v, float scale, void* out, void* workspace,
-               hipStream_t s) {
+               hipStream_t s, const int32_t* slots = nullptr) {
     pa::DecodeArgs<T> a;
+    a.ap.slots = slots;
+    a.ap.k_dst = slots ? const_cast<void*>(k_pool) : nullptr;  // written only when appending
+    a.ap.v_dst = slots ? const_cast<void*>(v_pool) : nullptr;
+    a.ap.n_slot = (int64_t)p->num_blocks * p->block_size;
     const int64_t rows = (int64_t)p->batch * p->num_heads * p->nq;
     a.q = static_cast<const T*>(q);
     a.k_pool = static_cast<const T*>(k_pool);
@@ -507,6 +529,42 @@ int run_decode(const pa_problem* p, const Plan& pl, const void* q, const void* k
                         hipGetErrorString(e));
     }
     return succeed();
+}
+
+int decode_entry(const pa_problem* problem, const void* q, const void* k_pool,
+                 const void* v_pool, const int32_t* block_table, const int32_t* context_lens,
+                 const void* new_k, const void* new_v, const int32_t* slots, float scale,
+                 void* out, void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+    if (int rc = validate_problem(problem)) return rc;
+    if (problem->batch == 0) return succeed();
+    if (int rc = validate_tensors(problem, q, k_pool, v_pool, block_table, context_lens, new_k,
+                                  new_v, out))
+        return rc;
+    if (workspace && misaligned(workspace, 16))
+        return fail(PA_ERR_INVALID_ARG, "workspace (%p) is not 16-byte aligned", workspace);
+    int cus = 0;
+    if (int rc = current_device_cus(&cus)) return rc;
+    Plan pl;
+    if (int rc = plan_impl(problem, cus, &pl)) return rc;
+    const size_t need = workspace_bytes_for(problem, pl);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes at %p is smaller than the %zu bytes "
+                    "this plan needs (%d partitions); verify pa_workspace_size",
+                    workspace_bytes, workspace, need, pl.parts);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    switch (problem->dtype) {
+        case PA_F32:
+            return run_decode<float>(problem, pl, q, k_pool, v_pool, block_table, context_lens,
+                                     new_k, new_v, scale, out, workspace, s, slots);
+        case PA_F16:
+            return run_decode<_Float16>(problem, pl, q, k_pool, v_pool, block_table,
+                                        context_lens, new_k, new_v, scale, out, workspace, s,
+                                        slots);
+        default:
+            return run_decode<pa::bf16_t>(problem, pl, q, k_pool, v_pool, block_table,
+                                          context_lens, new_k, new_v, scale, out, workspace, s,
+                                          slots);
+    }
 }
 
 }  // namespace
@@ -552,34 +610,23 @@ int paged_attn_decode(const pa_problem* problem, const void* q, const void* k_po
                       const int32_t* context_lens, const void* new_k, const void* new_v,
                       float scale, void* out, void* workspace, size_t workspace_bytes,
                       pa_stream_t stream) {
-    if (int rc = validate_problem(problem)) return rc;
-    if (problem->batch == 0) return succeed();
-    if (int rc = validate_tensors(problem, q, k_pool, v_pool, block_table, context_lens, new_k,
-                                  new_v, out))
-        return rc;
-    if (workspace && misaligned(workspace, 16))
-        return fail(PA_ERR_INVALID_ARG, "workspace (%p) is not 16-byte aligned", workspace);
-    int cus = 0;
-    if (int rc = current_device_cus(&cus)) return rc;
-    Plan pl;
-    if (int rc = plan_impl(problem, cus, &pl)) return rc;
-    const size_t need = workspace_bytes_for(problem, pl);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes at %p is smaller than the %zu bytes "
-                    "this plan needs (%d partitions); verify pa_workspace_size",
-                    workspace_bytes, workspace, need, pl.parts);
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    switch (problem->dtype) {
-        case PA_F32:
-            return run_decode<float>(problem, pl, q, k_pool, v_pool, block_table, context_lens,
-                                     new_k, new_v, scale, out, workspace, s);
-        case PA_F16:
-            return run_decode<_Float16>(problem, pl, q, k_pool, v_pool, block_table,
-                                        context_lens, new_k, new_v, scale, out, workspace, s);
-        default:
-            return run_decode<pa::bf16_t>(problem, pl, q, k_pool, v_pool, block_table,
-                                          context_lens, new_k, new_v, scale, out, workspace, s);
-    }
+    return decode_entry(problem, q, k_pool, v_pool, block_table, context_lens, new_k, new_v,
+                        nullptr, scale, out, workspace, workspace_bytes, stream);
+}
+
+int paged_attn_decode_append(const pa_problem* problem, const void* q, void* k_pool,
+                             void* v_pool, const int32_t* block_table,
+                             const int32_t* context_lens, const void* new_k, const void* new_v,
+                             const int32_t* slot_mapping, float scale, void* out,
+                             void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+    if (problem && problem->batch > 0 && !slot_mapping)
+        return fail(PA_ERR_INVALID_ARG, "slot_mapping is NULL; pass int32 [batch, nq] slots "
+                    "(negative = row not stored) or call paged_attn_decode");
+    if (misaligned(slot_mapping, 4))
+        return fail(PA_ERR_INVALID_ARG, "slot_mapping (%p) is not 4-byte aligned",
+                    (const void*)slot_mapping);
+    return decode_entry(problem, q, k_pool, v_pool, block_table, context_lens, new_k, new_v,
+                        slot_mapping, scale, out, workspace, workspace_bytes, stream);
 }
 
 int paged_attn_combine(const pa_problem* problem, const int32_t* context_lens,
@@ -616,6 +663,6 @@ int paged_attn_combine(const pa_problem* problem, const int32_t* context_lens,
 
 const char* paged_attn_last_error(void) { return t_error.c_str(); }
 
-int paged_attn_version(void) { return 101; }
+int paged_attn_version(void) { return 102; }
 
 }  // extern "C"

@@ -167,6 +167,80 @@ def test_many_short_sequences():
 
 
 # ---------------------------------------------------------------------------
+# Slot-patched step (paged_attn_decode_append): out against the oracle, and
+# the pools afterwards bit for bit against the oracle's stored rows
+# ---------------------------------------------------------------------------
+APPEND_GPU = [
+    # B, H, KV, D, BS, NQ, causal, dtype, lens, kernel
+    (3, 8, 2, 128, 16, 1, True, "f16", (0, 15, 300), pa.PA_KERNEL_MFMA),    # one row tile
+    (2, 32, 8, 128, 16, 1, True, "bf16", (700, 33), pa.PA_KERNEL_MFMA),     # Llama-3-8B heads
+    (2, 16, 2, 128, 16, 8, True, "f16", (5, 333), pa.PA_KERNEL_MFMA),       # 64 rows: cooperative
+    (2, 16, 2, 64, 32, 3, True, "bf16", (40, 250), pa.PA_KERNEL_MFMA),      # 24 rows, D=64, BS=32
+    (2, 4, 2, 64, 16, 2, True, "f32", (129, 1), pa.PA_KERNEL_AUTO),         # fp32: vector ALU
+    (2, 8, 2, 128, 32, 3, False, "f16", (31, 64), pa.PA_KERNEL_VALU),       # forced vector ALU
+]
+APPEND_SCENARIOS = {
+    "natural": dict(seed=3),
+    "overwrite": dict(overwrite=3, duplicate=True, seed=4),
+    "ignored": dict(overwrite=1, negative=2, out_of_range=2, seed=6),
+}
+
+
+def _bits(t):
+    t = t.detach().cpu().contiguous()
+    return t.view(torch.int32 if t.element_size() == 4 else torch.int16)
+
+
+def gpu_decode_append(w, slots, num_partitions=0, kernel=0):
+    table = torch.from_numpy(np.ascontiguousarray(w.block_table)).to(DEV)
+    lens = torch.from_numpy(np.ascontiguousarray(w.context_lens)).to(DEV)
+    kp, vp = w.k_pool.to(DEV).clone(), w.v_pool.to(DEV).clone()
+    print(f"[gpu] append {w.spec.name} B={w.spec.B} dtype={w.spec.dtype} parts={num_partitions} "
+          f"kernel={kernel}", flush=True)
+    out = pa.decode_append(w.q.to(DEV), kp, vp, table, lens, w.new_k.to(DEV), w.new_v.to(DEV),
+                           torch.from_numpy(slots).to(DEV), w.scale,
+                           max_context_len=w.max_context_len, causal=w.spec.causal,
+                           num_partitions=num_partitions, kernel=kernel)
+    torch.cuda.synchronize()
+    return out, kp, vp
+
+
+@pytest.mark.parametrize("scenario", sorted(APPEND_SCENARIOS))
+@pytest.mark.parametrize("case", APPEND_GPU, ids=lambda c: "-".join(map(str, c[:8])) + f"-k{c[9]}")
+def test_append_matches_the_oracle(case, scenario):
+    B, H, KV, D, BS, NQ, causal, dtype, lens, kernel = case
+    w = P.small(B=B, H=H, KV=KV, D=D, BS=BS, NQ=NQ, causal=causal, dtype=dtype, lens=lens,
+                seed=41)
+    w, slots, reads = P.append_problem(w, **APPEND_SCENARIOS[scenario])
+    if scenario == "overwrite":
+        assert reads
+    expect, kp_ref, vp_ref = oracle.paged_decode_append(*P.args(w)[:7], slots, w.scale,
+                                                        causal=causal)
+    for parts in (0, 1, 3):
+        out, kp, vp = gpu_decode_append(w, slots, num_partitions=parts, kernel=kernel)
+        check(w, out, expect)
+        assert torch.equal(_bits(kp), _bits(kp_ref)) and torch.equal(_bits(vp), _bits(vp_ref))
+
+
+def test_append_with_every_slot_negative_is_the_plain_step():
+    w = P.small(B=3, H=8, KV=2, D=128, BS=16, NQ=2, causal=True, dtype="bf16", lens=(20, 0, 90),
+                seed=42)
+    w, slots, _ = P.append_problem(w, seed=7)
+    slots[:] = -1
+    for kernel in (pa.PA_KERNEL_MFMA, pa.PA_KERNEL_VALU):
+        out, kp, vp = gpu_decode_append(w, slots, num_partitions=3, kernel=kernel)
+        assert torch.equal(out, gpu_decode(to_device(w), num_partitions=3, kernel=kernel))
+        assert torch.equal(_bits(kp), _bits(w.k_pool)) and torch.equal(_bits(vp), _bits(w.v_pool))
+
+
+def test_plain_step_leaves_the_pools_alone():
+    w = to_device(P.small(B=2, H=8, KV=2, D=128, BS=16, NQ=1, dtype="f16", lens=(70, 5), seed=43))
+    k0, v0 = w.k_pool.clone(), w.v_pool.clone()
+    gpu_decode(w, num_partitions=2)
+    assert torch.equal(w.k_pool, k0) and torch.equal(w.v_pool, v0)
+
+
+# ---------------------------------------------------------------------------
 # Block-table indexing: bit-exact invariants
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
