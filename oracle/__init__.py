@@ -45,6 +45,8 @@ def load_library(path: str):
     lib.oracle_paged_decode_partitioned.restype = i
     lib.oracle_kv_append.argtypes = [i] * 7 + [p] * 5
     lib.oracle_kv_append.restype = i
+    lib.oracle_dense_attention.argtypes = [i] * 7 + [p] * 3 + [i, p, p, i, f, p]
+    lib.oracle_dense_attention.restype = i
     lib.oracle_widen.argtypes = [p, ctypes.c_int64, i]
     lib.oracle_widen.restype = ctypes.c_double
     lib.oracle_num_threads.argtypes = []
@@ -163,6 +165,40 @@ def paged_decode_append(q, k_pool, v_pool, block_table, context_lens, new_k, new
     out = paged_decode(q, kp, vp, block_table, context_lens, new_k, new_v, scale,
                        causal=causal, lib=lib)
     return out, kp, vp
+
+
+MASK_NONE, MASK_BOOL, MASK_ADD = 0, 1, 2
+
+
+def dense_attention(q, k, v, scale: float, mask=None, causal: bool = False,
+                    lib=None) -> np.ndarray:
+    """Dense GQA forward (C oracle_dense_attention): q [B, HQ, SQ, D], k/v
+    [B, HK, SK, D]; `mask` a 4-D tensor [mb, mh, mq, mw] (bool: visible where
+    True; float32: additive bias), each dim 1 or full size, mw <= SK. Returns
+    double [B, HQ, SQ, D]."""
+    q, k, v = _host(q), _host(k), _host(v)
+    B, HQ, SQ, D = q.shape
+    _, HK, SK, _ = k.shape
+    kind, mptr, dims, keep = MASK_NONE, None, None, None
+    if mask is not None:
+        m = _host(mask)
+        assert m.dim() == 4, "mask must be 4-D [mb, mh, mq, mw]"
+        if m.dtype == torch.bool:
+            kind, keep = MASK_BOOL, m.to(torch.uint8).contiguous()
+        else:
+            kind, keep = MASK_ADD, m.to(torch.float32).contiguous()
+        mptr = ctypes.c_void_p(keep.data_ptr())
+        dims = np.ascontiguousarray(list(m.shape), dtype=np.int32)
+    out = np.zeros((B, HQ, SQ, D), dtype=np.float64)
+    rc = _load(lib).oracle_dense_attention(
+        B, HQ, HK, SQ, SK, D, _DT[q.dtype], ctypes.c_void_p(q.data_ptr()),
+        ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()), kind, mptr,
+        dims.ctypes.data_as(ctypes.c_void_p) if dims is not None else None, int(causal),
+        ctypes.c_float(scale), out.ctypes.data_as(ctypes.c_void_p))
+    del keep
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return out
 
 
 # ----------------------------------------------------------------------------

@@ -309,3 +309,101 @@ int oracle_paged_decode_partitioned(int B, int H, int KV, int D, int BS, int max
                        block_table, context_lens, new_k, new_v, scale, chunk, max_chunks,
                        part_m, part_z, part_o, out);
 }
+
+/*
+ * Dense GQA attention forward: the forward half of the docs.rs page
+ * "onnxruntime-ep-mlx 0.31.1: src/ops/attention_vjp/dense.rs", execute() (score
+ * matrix, mask bias, causal mask, softmax with empty rows set to zero; the
+ * output is p V). Readings where the page leaves a step open:
+ *   - the page multiplies q and k each by sqrt(scale); in exact arithmetic that
+ *     is scale * <q, k>, computed here as the binary32 scale times the double
+ *     dot product;
+ *   - mask_kind 1 is boolean (nonzero = visible: bias 0, else -inf), 2 is an
+ *     additive binary32 bias; the mask has dims [mb, mh, mq, mw], a dim of 1
+ *     repeating over batch, query head, query position or key; when 1 < mw < SK
+ *     keys j >= mw get -inf (the page pads the last axis with -inf);
+ *   - causal: key j is visible to query i only if j <= i (the page compares the
+ *     two aranges: top-left alignment).
+ */
+int oracle_dense_attention(int B, int HQ, int HK, int SQ, int SK, int D, int dtype,
+                           const void* q, const void* k, const void* v, int mask_kind,
+                           const void* mask, const int32_t* mask_dims, int causal,
+                           float scale, double* out)
+{
+    if (B < 0 || HQ <= 0 || HK <= 0 || SQ < 0 || SK < 0 || D <= 0 || HQ % HK != 0)
+        return -1;
+    if (dtype < 0 || dtype > 2 || mask_kind < 0 || mask_kind > 2)
+        return -3;
+    int mb = 1, mh = 1, mq = 1, mw = 1;
+    if (mask_kind) {
+        if (!mask || !mask_dims)
+            return -7;
+        mb = mask_dims[0]; mh = mask_dims[1]; mq = mask_dims[2]; mw = mask_dims[3];
+        if ((mb != 1 && mb != B) || (mh != 1 && mh != HQ) || (mq != 1 && mq != SQ) || mw < 1 ||
+            mw > (SK > 0 ? SK : 1))
+            return -8;
+    }
+    const int G = HQ / HK;
+    const double sc = (double)scale;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t row = 0; row < (int64_t)B * HQ * SQ; ++row) {
+        const int b = (int)(row / ((int64_t)HQ * SQ));
+        const int h = (int)(row / SQ % HQ);
+        const int i = (int)(row % SQ);
+        const int kh = h / G; /* query head h = kh*G + g */
+        double* s = (double*)malloc(sizeof(double) * (size_t)(SK > 0 ? SK : 1));
+        double* qr = (double*)malloc(sizeof(double) * (size_t)D);
+        if (!s || !qr) {
+#pragma omp atomic write
+            failed = 1;
+            free(s); free(qr);
+            continue;
+        }
+        for (int d = 0; d < D; ++d)
+            qr[d] = oracle_widen(q, row * D + d, dtype);
+        double m = -INFINITY;
+        for (int j = 0; j < SK; ++j) {
+            const int64_t krow = ((int64_t)b * HK + kh) * SK + j;
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d)
+                dot += qr[d] * oracle_widen(k, krow * D + d, dtype);
+            double bias = 0.0;
+            if (mask_kind) {
+                if (mw != 1 && j >= mw) {
+                    bias = -INFINITY;
+                } else {
+                    const int64_t mi = (((int64_t)(mb == 1 ? 0 : b) * mh + (mh == 1 ? 0 : h)) * mq +
+                                        (mq == 1 ? 0 : i)) * mw + (mw == 1 ? 0 : j);
+                    if (mask_kind == 1)
+                        bias = ((const uint8_t*)mask)[mi] ? 0.0 : -INFINITY;
+                    else
+                        bias = (double)((const float*)mask)[mi];
+                }
+            }
+            if (causal && j > i)
+                bias = -INFINITY;
+            s[j] = sc * dot + bias;
+            if (s[j] > m)
+                m = s[j];
+        }
+        for (int d = 0; d < D; ++d)
+            out[row * D + d] = 0.0;
+        if (m != -INFINITY) { /* rows with every key masked stay zero */
+            double z = 0.0;
+            for (int j = 0; j < SK; ++j) {
+                const double w = exp(s[j] - m);
+                if (w == 0.0)
+                    continue;
+                z += w;
+                const int64_t krow = ((int64_t)b * HK + kh) * SK + j;
+                for (int d = 0; d < D; ++d)
+                    out[row * D + d] += w * oracle_widen(v, krow * D + d, dtype);
+            }
+            for (int d = 0; d < D; ++d)
+                out[row * D + d] /= z;
+        }
+        free(s); free(qr);
+    }
+    return failed ? -6 : 0;
+}

@@ -70,6 +70,20 @@ int oracle_kv_append(int B, int KV, int D, int BS, int num_blocks, int NQ, int d
                      void* k_pool, void* v_pool, const void* new_k, const void* new_v,
                      const int32_t* slot_mapping);
 
+/*
+ * Dense GQA attention forward (docs.rs page "onnxruntime-ep-mlx 0.31.1:
+ * src/ops/attention_vjp/dense.rs", execute()): q [B, HQ, SQ, D], k/v
+ * [B, HK, SK, D], out double [B, HQ, SQ, D]. s = scale * <q_i, k_j> plus the
+ * mask bias (mask_kind 0: none; 1: boolean bytes, nonzero = visible; 2:
+ * additive binary32) broadcast from dims mask_dims[4] = [mb, mh, mq, mw] (each
+ * 1 or the full size; keys j >= mw masked when 1 < mw < SK); causal: j <= i
+ * only. Rows whose every key is masked give zeros.
+ */
+int oracle_dense_attention(int B, int HQ, int HK, int SQ, int SK, int D, int dtype,
+                           const void* q, const void* k, const void* v, int mask_kind,
+                           const void* mask, const int32_t* mask_dims, int causal,
+                           float scale, double* out);
+
 /* Exact widening of one stored element (exported so tests can pin it). */
 double oracle_widen(const void* base, int64_t index, int dtype);
 

@@ -15,6 +15,10 @@ and PARTIALS_REDUCE: merge of partial states). The pins are:
     a cached position whose slot is re-written reads the new row (the highest
     j pointing at it) -- against SDPA on the dense problem with that position
     replaced directly,
+  * dense GQA forward with masks: torch's SDPA on heads-expanded K/V with the
+    mask broadcast, right-padded and causal-limited by the test itself; fully
+    masked rows are zero; one visible key returns its value; a per-row additive
+    constant changes nothing and an additive -inf equals a boolean False,
   * mutation check: plausible mistakes planted in a copy of the oracle's C
     source each make at least one of these pins fail.
 """
@@ -301,6 +305,115 @@ def test_negative_and_out_of_range_slots_are_neither_stored_nor_read():
 
 
 # --------------------------------------------------------------------------
+# Dense GQA forward with masks
+# --------------------------------------------------------------------------
+def _dense_inputs(B, HQ, HK, SQ, SK, D, dtype="f32", seed=0):
+    g = torch.Generator().manual_seed(seed)
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    q = torch.randn(B, HQ, SQ, D, generator=g).to(dt)
+    k = torch.randn(B, HK, SK, D, generator=g).to(dt)
+    v = torch.randn(B, HK, SK, D, generator=g).to(dt)
+    return q, k, v
+
+
+def _sdpa_dense(q, k, v, scale, mask=None, causal=False):
+    """torch SDPA (float64) on K/V repeated to every query head, with the mask
+    turned into a full [B, HQ, SQ, SK] bias here; rows with no visible key are
+    returned as NaN by SDPA and reported in `empty`."""
+    B, HQ, SQ, D = q.shape
+    HK, SK = k.shape[1], k.shape[2]
+    G = HQ // HK
+    bias = torch.zeros(B, HQ, SQ, SK, dtype=torch.float64)
+    if mask is not None:
+        mw = mask.shape[3]
+        m = mask if mask.dtype != torch.bool else torch.where(
+            mask, torch.tensor(0.0), torch.tensor(float("-inf")))
+        m = m.double()
+        if mw != 1 and mw < SK:  # keys past the mask's width are hidden
+            m = torch.cat([m, torch.full(m.shape[:3] + (SK - mw,), float("-inf"),
+                                         dtype=torch.float64)], dim=3)
+        bias = bias + m.expand(B, HQ, SQ, SK)
+    if causal:
+        hide = torch.arange(SK)[None, :] > torch.arange(SQ)[:, None]
+        bias = bias.masked_fill(hide, float("-inf"))
+    empty = torch.isinf(bias).all(dim=-1) & (bias.amax(dim=-1) < 0)
+    kh = k.double().repeat_interleave(G, dim=1)
+    vh = v.double().repeat_interleave(G, dim=1)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        q.double(), kh, vh, attn_mask=bias, scale=float(np.float32(scale)))
+    return out.numpy(), empty.numpy()
+
+
+def _mask(kind, dims, seed=0, p=0.7):
+    g = torch.Generator().manual_seed(seed)
+    if kind == "bool":
+        return torch.rand(dims, generator=g) < p
+    return torch.randn(dims, generator=g).float() * 2.0
+
+
+DENSE_CASES = [
+    # (B, HQ, HK, SQ, SK, D, dtype, mask kind, mask dims, causal)
+    (2, 4, 2, 5, 9, 64, "f32", None, None, False),
+    (2, 4, 2, 9, 9, 64, "f16", None, None, True),           # square causal
+    (1, 8, 2, 12, 7, 64, "bf16", None, None, True),         # SQ > SK: top-left
+    (2, 4, 1, 6, 11, 32, "f32", "bool", (2, 4, 6, 11), False),
+    (2, 4, 2, 6, 11, 64, "f32", "bool", (1, 1, 6, 11), True),
+    (2, 6, 3, 5, 13, 64, "f16", "add", (2, 1, 1, 13), False),
+    (1, 4, 2, 7, 16, 64, "f32", "add", (1, 4, 7, 10), False),   # padded past width 10
+    (2, 4, 2, 4, 8, 64, "bf16", "bool", (2, 1, 4, 1), True),    # width 1: broadcast over keys
+]
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=lambda c: "-".join(map(str, c[:8])) + ("-c" if c[9] else ""))
+def test_dense_matches_sdpa(case):
+    B, HQ, HK, SQ, SK, D, dtype, kind, dims, causal = case
+    q, k, v = _dense_inputs(B, HQ, HK, SQ, SK, D, dtype, seed=SQ + SK)
+    mask = _mask(kind, dims, seed=3) if kind else None
+    ref = oracle.dense_attention(q, k, v, 0.2, mask=mask, causal=causal)
+    exp, empty = _sdpa_dense(q, k, v, 0.2, mask=mask, causal=causal)
+    assert np.abs(ref[~empty] - exp[~empty]).max() < 1e-12
+    assert (ref[empty] == 0).all()
+
+
+def test_dense_fully_masked_rows_are_zero():
+    q, k, v = _dense_inputs(2, 4, 2, 6, 8, 64, seed=1)
+    mask = torch.ones(2, 1, 6, 8, dtype=torch.bool)
+    mask[1, 0, 2] = False          # row 2 of batch 1 sees nothing
+    mask[0, 0, :, 5:] = False      # batch 0: only keys 0..4
+    out = oracle.dense_attention(q, k, v, 0.3, mask=mask, causal=False)
+    assert (out[1, :, 2] == 0).all() and np.abs(out[1, :, 3]).max() > 0
+    exp, empty = _sdpa_dense(q, k, v, 0.3, mask=mask)
+    assert empty[1, :, 2].all() and not empty[0].any()
+    assert np.abs(out[~empty] - exp[~empty]).max() < 1e-12
+
+
+def test_dense_single_visible_key_returns_its_value():
+    B, HQ, HK, SQ, SK, D = 1, 4, 2, 5, 9, 64
+    q, k, v = _dense_inputs(B, HQ, HK, SQ, SK, D, seed=2)
+    pick = [3, 0, 8, 5, 1]
+    mask = torch.zeros(1, 1, SQ, SK, dtype=torch.bool)
+    for i, j in enumerate(pick):
+        mask[0, 0, i, j] = True
+    out = oracle.dense_attention(q, k, v, 0.5, mask=mask)
+    for h in range(HQ):
+        for i, j in enumerate(pick):
+            assert np.array_equal(out[0, h, i], v[0, h // (HQ // HK), j].double().numpy())
+
+
+def test_dense_additive_bias_semantics():
+    q, k, v = _dense_inputs(2, 4, 2, 6, 10, 64, seed=4)
+    base = torch.round(_mask("add", (2, 4, 6, 10), seed=5) * 64) / 64  # exact in float32
+    shifted = base + torch.arange(6, dtype=torch.float32)[None, None, :, None] * 3.0
+    a = oracle.dense_attention(q, k, v, 0.25, mask=base)
+    b = oracle.dense_attention(q, k, v, 0.25, mask=shifted)   # a constant per row: no change
+    assert np.abs(a - b).max() < 1e-12
+    vis = _mask("bool", (2, 1, 6, 10), seed=6)
+    add = torch.where(vis, torch.tensor(0.0), torch.tensor(float("-inf"))).float()
+    assert np.array_equal(oracle.dense_attention(q, k, v, 0.25, mask=vis),
+                          oracle.dense_attention(q, k, v, 0.25, mask=add))
+
+
+# --------------------------------------------------------------------------
 # Mutation check: each planted mistake must trip at least one pin.
 # --------------------------------------------------------------------------
 def _pins(lib):
@@ -342,6 +455,15 @@ def _pins(lib):
         out, _, _ = _append(w, slots, lib)
         if np.abs(out - _dense_with_reads(w, reads, True)).max() > 1e-12:
             failed.append("append_overwrite")
+        for case in (DENSE_CASES[2], DENSE_CASES[4], DENSE_CASES[6], DENSE_CASES[7]):
+            B, HQ, HK, SQ, SK, D, dtype, kind, dims, causal = case
+            q, k, v = _dense_inputs(B, HQ, HK, SQ, SK, D, dtype, seed=SQ + SK)
+            mask = _mask(kind, dims, seed=3) if kind else None
+            ref = oracle.dense_attention(q, k, v, 0.2, mask=mask, causal=causal, lib=lib)
+            exp, empty = _sdpa_dense(q, k, v, 0.2, mask=mask, causal=causal)
+            if np.abs(ref[~empty] - exp[~empty]).max() > 1e-12 or (ref[empty] != 0).any():
+                failed.append("dense")
+                break
     except ValueError:
         failed.append("rejected")
     return failed
@@ -371,6 +493,12 @@ MUTATIONS = {
                                "for (int kh = 0; kh < 1; ++kh) {\n                const int64_t row"),
     "append_rows_of_head_0": ("const int64_t row = ((int64_t)b * KV + kh) * NQ + j;",
                               "const int64_t row = ((int64_t)b * KV) * NQ + j;"),
+    "dense_causal_bottom_right": ("if (causal && j > i)", "if (causal && j > i + SK - SQ)"),
+    "dense_head_mapping": ("const int kh = h / G; /* query head h = kh*G + g */",
+                           "const int kh = h % HK; /* query head h = kh*G + g */"),
+    "dense_pad_off_by_one": ("if (mw != 1 && j >= mw) {", "if (mw != 1 && j > mw) {"),
+    "dense_mask_head_index": ("(mh == 1 ? 0 : h)) * mq", "(mh == 1 ? 0 : kh)) * mq"),
+    "dense_bias_scaled": ("s[j] = sc * dot + bias;", "s[j] = sc * (dot + bias);"),
 }
 
 
