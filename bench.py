@@ -120,6 +120,44 @@ def cpu_baseline(w, seconds: float):
     }
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix-core peak
+
+
+def dense_prefill(torch, pa, timed, warmup: int) -> dict:
+    """pa_dense_attention on a Llama-3-8B-shaped causal prefill (one sequence of
+    2048 tokens, 32 query heads over 8 KV heads, D = 128, fp16, synthetic):
+    algorithmic flops 4*D per visible (query, key) pair, against the fp16
+    matrix-core peak."""
+    B, HQ, HK, S, D = 1, 32, 8, 2048, 128
+    g = torch.Generator(device="cuda:0").manual_seed(1100)
+    q = torch.randn(B, HQ, S, D, generator=g, device="cuda:0").half()
+    k = torch.randn(B, HK, S, D, generator=g, device="cuda:0").half()
+    v = torch.randn(B, HK, S, D, generator=g, device="cuda:0").half()
+    out = torch.empty_like(q)
+    scale = 1.0 / D ** 0.5
+
+    def call(i):
+        pa.dense_attention(q, k, v, scale, causal=True, out=out)
+
+    for i in range(min(warmup, 50)):
+        call(i)
+    ms = timed(call, 50)
+    flop = 4 * D * HQ * B * S * (S + 1) // 2
+    tflops = flop / (ms / 1e3) / 1e12
+    log(f"[bench] dense causal prefill {ms * 1e3:.1f} us, {tflops:.1f} TFLOP/s")
+    return {
+        "entry_point": "pa_dense_attention",
+        "config": {"workload": "causal prefill", "batch": B, "num_heads": HQ,
+                   "num_kv_heads": HK, "q_len": S, "kv_len": S, "head_dim": D,
+                   "dtype": "f16", "causal": True, "mask": None},
+        "us_per_call": round(ms * 1e3, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                     "algorithmic_flop_per_call": flop},
+    }
+
+
 def percentile(sorted_values, q) -> float:
     """Linear-interpolation percentile of an ascending list."""
     x = (len(sorted_values) - 1) * q / 100.0
@@ -276,6 +314,8 @@ def main():
         f"({kvb / (ms_append / 1e3) / 1e9:.1f} GB/s of KV reads, {stored} B stored); "
         f"plain step on the same pools {ms_plain_ext * 1e3:.2f} us/step")
 
+    dense = dense_prefill(torch, pa, timed, args.warmup)
+
     copy_gbps = copy_bandwidth(torch)
     log(f"[bench] device copy bandwidth {copy_gbps:.0f} GB/s (read+write)")
     traffic = measured_traffic(spec.name, kvb)
@@ -338,6 +378,7 @@ def main():
             "stored_bytes_per_step": stored,
             "slots": "every new row into a spare slot past the cached blocks (no read patched)",
         },
+        "dense_prefill": dense,
         "device_copy_gbps": round(copy_gbps, 1),
         "cpu_baseline": cpu,
     }

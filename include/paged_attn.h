@@ -214,12 +214,52 @@ int paged_attn_combine(const pa_problem* problem, const int32_t* context_lens,
                        const void* workspace, size_t workspace_bytes, void* out,
                        pa_stream_t stream);
 
+/*
+ * Dense (prefill) GQA attention forward: the forward half of the docs.rs page
+ * "onnxruntime-ep-mlx 0.31.1: src/ops/attention_vjp/dense.rs", execute()
+ * (score matrix, mask bias, causal mask, softmax with fully masked rows set to
+ * zero), times V. For sequence b, query head h (KV head kh = h / (HQ/HK)) and
+ * query position i:
+ *   s_j = scale * <q[b,h,i,:], k[b,kh,j,:]> + bias(b,h,i,j),  j < kv_len
+ *   bias = 0 / -inf from a boolean mask (nonzero = visible) or the value of an
+ *          additive binary32 mask, broadcast from mask_dims = [mb, mh, mq, mw]
+ *          (a dim of 1 repeats; when 1 < mw < kv_len, keys j >= mw get -inf,
+ *          as the page pads the mask's last axis); 0 without a mask
+ *   causal: s_j = -inf for j > i (top-left alignment: query i sees keys 0..i)
+ *   out[b,h,i,:] = softmax(s) . v[b,kh,:,:], or 0 where every s_j is -inf
+ * Layouts: q, out [batch, num_heads, q_len, head_dim]; k, v [batch,
+ * num_kv_heads, kv_len, head_dim]; mask [mb, mh, mq, mw] uint8 (PA_MASK_BOOL)
+ * or float32 (PA_MASK_ADD), row-major. Device pointers owned by the caller;
+ * out is written, nothing else. Asynchronous on `stream`. Supported: fp16/bf16,
+ * head_dim 64/128, num_heads/num_kv_heads <= 64. Errors: PA_ERR_INVALID_ARG for
+ * NULL/misaligned pointers or inconsistent sizes/mask dims, PA_ERR_UNSUPPORTED
+ * outside the supported shapes (fp32 included), PA_ERR_DEVICE, PA_ERR_LAUNCH.
+ */
+typedef enum { PA_MASK_NONE = 0, PA_MASK_BOOL = 1, PA_MASK_ADD = 2 } pa_mask_kind;
+
+typedef struct {
+    int32_t batch;        /* >= 0 */
+    int32_t num_heads;    /* HQ >= 1 */
+    int32_t num_kv_heads; /* HK >= 1, HQ % HK == 0 */
+    int32_t head_dim;     /* 64 or 128 */
+    int32_t q_len;        /* SQ >= 0 */
+    int32_t kv_len;       /* SK >= 0 */
+    int32_t causal;       /* 1: key j visible to query i only if j <= i */
+    int32_t dtype;        /* PA_F16 or PA_BF16 */
+    int32_t mask_kind;    /* pa_mask_kind */
+    int32_t mask_dims[4]; /* [mb, mh, mq, mw] when mask_kind != PA_MASK_NONE */
+} pa_dense_problem;
+
+int pa_dense_attention(const pa_dense_problem* problem, const void* q, const void* k,
+                       const void* v, const void* mask, float scale, void* out,
+                       pa_stream_t stream);
+
 /* Message of the last failing call on this thread ("" if none). Valid until the
  * next call on this thread. */
 const char* paged_attn_last_error(void);
 
 /* ABI version of this header (major * 100 + minor). */
-int paged_attn_version(void);  /* 102: paged_attn_decode_append */
+int paged_attn_version(void);  /* 103: pa_dense_attention */
 
 #ifdef __cplusplus
 }

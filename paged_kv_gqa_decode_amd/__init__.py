@@ -21,10 +21,11 @@ PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_DEVICE, 
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
 PA_FLAG_DEFER_COMBINE = 1
+PA_MASK_NONE, PA_MASK_BOOL, PA_MASK_ADD = 0, 1, 2
 
 EXPORTED = ("pa_plan_ex", "pa_plan", "pa_workspace_size", "pa_workspace_size_ex",
             "paged_attn_decode", "paged_attn_decode_append", "paged_attn_combine",
-            "paged_attn_last_error", "paged_attn_version")
+            "pa_dense_attention", "paged_attn_last_error", "paged_attn_version")
 
 
 class PaProblem(ctypes.Structure):
@@ -32,6 +33,12 @@ class PaProblem(ctypes.Structure):
         "batch", "num_heads", "num_kv_heads", "head_dim", "block_size", "num_blocks",
         "max_blocks_per_seq", "nq", "causal", "dtype", "max_context_len", "num_partitions",
         "kernel", "flags")]
+
+
+class PaDenseProblem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "num_heads", "num_kv_heads", "head_dim", "q_len", "kv_len", "causal", "dtype",
+        "mask_kind")] + [("mask_dims", ctypes.c_int32 * 4)]
 
 
 class PagedAttnError(RuntimeError):
@@ -71,6 +78,9 @@ def library(path: Optional[str] = None):
                                              vp, vp, ctypes.c_size_t, vp]
     lib.paged_attn_decode_append.restype = ctypes.c_int
     lib.paged_attn_combine.argtypes = [P, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.pa_dense_attention.argtypes = [ctypes.POINTER(PaDenseProblem), vp, vp, vp, vp,
+                                       ctypes.c_float, vp, vp]
+    lib.pa_dense_attention.restype = ctypes.c_int
     lib.paged_attn_last_error.argtypes = []
     lib.paged_attn_last_error.restype = ctypes.c_char_p
     lib.paged_attn_version.argtypes = []
@@ -179,6 +189,16 @@ def paged_attn_combine(problem: PaProblem, context_lens, workspace, workspace_by
     return rc
 
 
+def pa_dense_attention(problem: PaDenseProblem, q, k, v, mask, scale: float, out, stream=None,
+                       raise_on_error: bool = True) -> int:
+    rc = library().pa_dense_attention(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(mask), ctypes.c_float(scale), _ptr(out),
+                                      _stream(stream))
+    if raise_on_error:
+        _check(rc)
+    return rc
+
+
 def paged_attn_version() -> int:
     return library().paged_attn_version()
 
@@ -260,3 +280,33 @@ def decode_append(q, k_pool, v_pool, block_table, context_lens, new_k, new_v, sl
                   num_partitions=num_partitions, kernel=kernel)
     return dec(q, k_pool, v_pool, block_table, context_lens, new_k, new_v, scale, out=out,
                stream=stream, slot_mapping=slot_mapping)
+
+
+def make_dense_problem(q, k, *, causal: bool = False, mask=None) -> PaDenseProblem:
+    B, HQ, SQ, D = q.shape
+    _, HK, SK, _ = k.shape
+    p = PaDenseProblem(batch=B, num_heads=HQ, num_kv_heads=HK, head_dim=D, q_len=SQ, kv_len=SK,
+                       causal=int(causal), dtype=_dtype_code(q), mask_kind=PA_MASK_NONE)
+    if mask is not None:
+        import torch
+        assert mask.dim() == 4, "mask must be 4-D [mb, mh, mq, mw]"
+        p.mask_kind = PA_MASK_BOOL if mask.dtype in (torch.bool, torch.uint8) else PA_MASK_ADD
+        for i in range(4):
+            p.mask_dims[i] = mask.shape[i]
+    return p
+
+
+def dense_attention(q, k, v, scale: float, *, mask=None, causal: bool = False, out=None,
+                    stream=None):
+    """Dense GQA attention forward; q [B, HQ, SQ, D], k/v [B, HK, SK, D]; mask 4-D
+    [mb, mh, mq, mw], bool (True = visible) or float32 additive. Returns out."""
+    import torch
+    if mask is not None:
+        mask = mask.to(torch.uint8) if mask.dtype == torch.bool else mask.to(torch.float32)
+        mask = mask.contiguous()
+    prob = make_dense_problem(q, k, causal=causal, mask=mask)
+    out = torch.empty_like(q) if out is None else out
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    pa_dense_attention(prob, q, k, v, mask, scale, out, stream)
+    return out

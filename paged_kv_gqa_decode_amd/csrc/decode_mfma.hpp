@@ -187,6 +187,36 @@ struct SlotLayout {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Loads rows 0..15 (row stride D elements; rows past rmax repeat row rmax) of
+// K and V starting at k and v into the slot at `slot` in the slot layout,
+// instructions i = i0, i0 + istep, ... (COUNT of each half); 16 bytes per lane
+// per instruction. All offsets are in voffset, so the descriptors cover exactly
+// rmax + 1 rows.
+template <typename T, int D, int COUNT>
+__device__ __forceinline__ void fetch_rows(const T* k, const T* v, int rmax, char* slot, int lane,
+                                           int i0 = 0, int istep = 1) {
+    using Lay = SlotLayout<T, D>;
+    constexpr int kStride = D * (int)sizeof(T);
+    char* const k_lds = slot;
+    char* const v_lds = slot + Lay::kKBytes;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(k, (rmax + 1) * kStride);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(v, (rmax + 1) * kStride);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // computed here, not kept live across the loop
+#pragma unroll
+    for (int t = 0; t < COUNT; ++t) {
+        const int i = i0 + istep * t;
+        const int row = Lay::kKeysPerOp * i + ln / Lay::kChunks;
+        const int rc = min(row, rmax);
+        const int koff = rc * kStride + (((ln % Lay::kChunks) ^ Lay::swz(row)) << 4);
+        const int voff = rc * kStride + (((ln % Lay::kChunks) ^ Lay::vswz(row)) << 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(k_lds + i * 1024), 16, koff, 0,
+                                                 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(v_lds + i * 1024), 16, voff, 0,
+                                                 0, 0);
+    }
+}
+
 // ---- the stream of one wave's sub-pages: cursor, table entries, fetches ----
 template <typename T, int D, int BS>
 struct SubPageStream {
@@ -319,22 +349,7 @@ struct SubPageStream {
                                                          voff, soff, 0, kStreamPolicy);
             }
         } else {
-            const __amdgpu_buffer_rsrc_t kr = make_rsrc(s.k, (s.rmax + 1) * kNewStride);
-            const __amdgpu_buffer_rsrc_t vr = make_rsrc(s.v, (s.rmax + 1) * kNewStride);
-            int ln = lane;
-            asm volatile("" : "+v"(ln));  // computed here, not kept live across the loop
-#pragma unroll
-            for (int t = 0; t < COUNT; ++t) {
-                const int i = i0 + istep * t;
-                const int row = Lay::kKeysPerOp * i + ln / Lay::kChunks;
-                const int rc = min(row, s.rmax);
-                const int koff = rc * kNewStride + (((ln % Lay::kChunks) ^ Lay::swz(row)) << 4);
-                const int voff = rc * kNewStride + (((ln % Lay::kChunks) ^ Lay::vswz(row)) << 4);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(k_lds + i * 1024), 16,
-                                                         koff, 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(v_lds + i * 1024), 16,
-                                                         voff, 0, 0, 0);
-            }
+            fetch_rows<T, D, COUNT>(s.k, s.v, s.rmax, slot, lane, i0, istep);
         }
     }
 
@@ -462,14 +477,21 @@ struct RowTiles {
     // The address is a scalar base (the unit's first row) plus a 32-bit
     // per-lane byte offset, so no 64-bit per-lane pointer stays live.
     __device__ __forceinline__ void load_q(int b, int kh) {
-        const uint64_t addr = reinterpret_cast<uint64_t>(a.q + grow0(b, kh) * D);
+        uint32_t rows[NRT];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) rows[rt] = (uint32_t)min(16 * (rt0 + rt) + c16, a.R - 1) * D;
+        load_q_at(a.q + grow0(b, kh) * D, rows);
+    }
+    // load_q with this lane's row of tile rt at element offset row_off[rt] from
+    // `first` (a wave-uniform address; offsets < 2^31 bytes).
+    __device__ __forceinline__ void load_q_at(const T* first, const uint32_t (&row_off)[NRT]) {
+        const uint64_t addr = reinterpret_cast<uint64_t>(first);
         const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
         const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
         const T* base = reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
-            const int row = min(16 * (rt0 + rt) + c16, a.R - 1);
-            const uint32_t off = (uint32_t)(row * D + 8 * g16) * (uint32_t)sizeof(T);
+            const uint32_t off = (row_off[rt] + 8 * g16) * (uint32_t)sizeof(T);
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk)
                 asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3"
@@ -557,8 +579,11 @@ struct RowTiles {
     // so no score needs masking. The score products of all row tiles are
     // issued before any is read (one tile: two independent half-chains over
     // d), so the matrix-core latency of one chain is covered by the others.
+    // BIAS: bias[rt][i] (base-2 units, -inf hides) is added to the score of
+    // key 4*g16 + i of this lane's row.
+    template <bool BIAS = false>
     __device__ __forceinline__ void scores(const u32x4_t (&kop)[KS], const int (&lim)[NRT],
-                                           bool full) {
+                                           bool full, const float (*bias)[4] = nullptr) {
         constexpr int NC = NRT == 1 && KS % 2 == 0 ? 2 : 1;  // chains per tile
         f32x4_t sc[NRT][NC];
 #pragma unroll
@@ -582,6 +607,10 @@ struct RowTiles {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     sv[i] = 4 * g16 + i < lim[rt] ? s[i] * a.qscale : -__builtin_inff();
+            }
+            if constexpr (BIAS) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sv[i] += bias[rt][i];
             }
             // m[rt] is the same in the 4 lanes of a row (lanes c16 + 16*g).
             float tm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
@@ -621,6 +650,28 @@ struct RowTiles {
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) acc[rt][t] = M::pv(phi[rt], plo[rt], vt[t], acc[rt][t]);
+    }
+    // Normalised rows (all of their keys attended): output row r, held in
+    // acc[rt][*][i] for r = 16*(rt0 + rt) + 4*g16 + i, goes to `base` + off(r)
+    // (elements) unless off(r) < 0; 0 where nothing was visible.
+    template <typename F>
+    __device__ __forceinline__ void emit_rows(T* base, F&& off) const {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            float lrow = lsum[rt];
+            lrow += __shfl_xor(lrow, 16);
+            lrow += __shfl_xor(lrow, 32);  // l of row 16*(rt0+rt) + c16
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float l_r = __shfl(lrow, 4 * g16 + i);
+                const int64_t o = off(16 * (rt0 + rt) + 4 * g16 + i);
+                if (o < 0) continue;
+                const float inv = l_r != 0.f ? 1.f / l_r : 0.f;
+                T* dst = base + o + c16;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) Elem<T>::store(dst + 16 * t, acc[rt][t][i] * inv);
+            }
+        }
     }
     // The finished output of (b, kh) (its whole sequence attended here), or
     // this piece's state for the combine (workspace slot (b + grp)*KV + kh).

@@ -1,0 +1,171 @@
+// Dense (prefill) GQA attention forward on the matrix cores (gfx950, fp16/bf16).
+//
+// Operation: the forward half of the docs.rs page "onnxruntime-ep-mlx 0.31.1:
+// src/ops/attention_vjp/dense.rs", execute(): scores scale * q k^T, plus an
+// optional boolean or additive mask broadcast over [B, HQ, SQ, SK] (keys past a
+// shorter mask width hidden), the top-left causal limit (key j visible to query
+// i only if j <= i), softmax, rows with no visible key set to zero, times V.
+// GQA: query head h = kh*G + g reads KV head kh.
+//
+// A workgroup takes (sequence b, KV head kh, a block of P = 64/G query
+// positions), so it holds R = G*P <= 64 rows: every query head of the group at
+// those positions, and each K/V tile of the KV head is read once for all of
+// them. The keys stream through a ring of kRing 16-key LDS slots as in the
+// cooperative decode kernel (two waves of two row tiles, each wave issuing its
+// share of every slot's loads, one barrier per slot); the causal limit and the
+// mask width shorten the stream. Mask values are read per score element from
+// global memory: waiting for them drains the wave's ring, so masked runs are
+// correct but not tuned.
+#pragma once
+
+#include "decode_mfma.hpp"
+
+namespace pa {
+
+struct DenseGeometry {
+    int B, HQ, HK, SQ, SK;
+    int G, P, nblk;  // heads per KV head, query positions per workgroup, blocks per (b, kh)
+    int causal;
+};
+
+template <typename T>
+struct DenseArgs {
+    const T* q;        // [B, HQ, SQ, D]
+    const T* k;        // [B, HK, SK, D]
+    const T* v;
+    T* out;            // [B, HQ, SQ, D]
+    const void* mask;  // uint8 (nonzero = visible) or float32 bias, dims [mb, mh, mq, mw]
+    int mb, mh, mq, mw;
+    DenseGeometry g;
+    float qscale;      // scale * log2(e)
+};
+
+// MASK: 0 none, 1 boolean, 2 additive.
+template <typename T, int D, int NW, int NRT, int kRing, int MASK>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dense_mfma(DenseArgs<T> d) {
+    using Lay = SlotLayout<T, D>;
+    using Rows = RowTiles<T, D, NRT>;
+    constexpr int KS = D / 32;
+    constexpr int NWI = NW < KS ? NW : KS;  // waves that issue loads
+    constexpr int IPW = KS / NWI;           // instructions per half per issuing wave
+    static_assert(D % 32 == 0 && Lay::kOps == KS && KS % NWI == 0, "shape");
+    static_assert(kRing >= 3 && 2 * IPW * (kRing - 2) <= 63, "ring");
+    constexpr float kLog2e = 1.4426950408889634f;
+
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const int lane = threadIdx.x & 63, c16 = lane & 15, g16 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const DenseGeometry& g = d.g;
+    const int blk = blockIdx.x % g.nblk;
+    const int kh = (blockIdx.x / g.nblk) % g.HK;
+    const int b = blockIdx.x / (g.nblk * g.HK);
+    const int i0 = blk * g.P;                // first query position of the block
+    const int R = g.G * g.P;                 // rows: r = gg*P + p -> head kh*G + gg, position i0 + p
+    const int pend = min(g.P, g.SQ - i0);    // positions of the block that exist (>= 1)
+    int kend = g.SK;                         // keys any row of the block may see
+    if (g.causal) kend = min(kend, i0 + pend);
+    if (MASK && d.mw != 1 && d.mw < g.SK) kend = min(kend, d.mw);
+    const int n_sub = (kend + 15) / 16;
+    const bool issues = wave < NWI;
+    const bool has_rows = 16 * NRT * wave < R;
+
+    // The row tiles take the row count and the score scale from split arguments.
+    SplitArgs<T> sa{};
+    sa.R = R;
+    sa.qscale = d.qscale;
+    sa.g.NQ = 1;
+    sa.g.KV = 1;
+    sa.H = 1;
+    Rows rows(sa, lane, wave * NRT);
+
+    // This lane's S^T row of tile rt (row c16 of the tile), clamped to a real one.
+    int srow_p[NRT], srow_h[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+        const int r = min(16 * (wave * NRT + rt) + c16, R - 1);
+        srow_p[rt] = min(r % g.P, pend - 1);
+        srow_h[rt] = kh * g.G + r / g.P;
+    }
+    const int64_t head0 = (int64_t)b * g.HQ + (int64_t)kh * g.G;  // first query head of the group
+    if (has_rows) {
+        uint32_t qoff[NRT];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+            qoff[rt] = (uint32_t)(((srow_h[rt] - kh * g.G) * g.SQ + i0 + srow_p[rt]) * D);
+        rows.load_q_at(d.q + head0 * g.SQ * D, qoff);  // older than the ring's loads
+    }
+    const int64_t kv0 = ((int64_t)b * g.HK + kh) * g.SK * D;
+    const T* const kb = d.k + kv0;
+    const T* const vb = d.v + kv0;
+    for (int s = 0; s < kRing - 1 && s < n_sub; ++s)
+        if (issues)
+            fetch_rows<T, D, IPW>(kb + (int64_t)16 * s * D, vb + (int64_t)16 * s * D,
+                                  min(15, g.SK - 1 - 16 * s), smem + s * Lay::kBytes, lane, wave, NWI);
+    rows.reset();
+    bool q_pending = has_rows;
+    for (int i = 0; i < n_sub; ++i) {
+        const int ahead = min(kRing - 2, n_sub - 1 - i);  // sub-pages fetched after i
+        if (issues) wait_ahead<2 * IPW, kRing - 2>(ahead);
+        else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        if (q_pending) {
+            rows.q_ready();
+            q_pending = false;
+        }
+        // every wave's part of sub-page i is in; slot i - 1 is read out
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const int nxt = i + kRing - 1;
+        if (nxt < n_sub && issues)
+            fetch_rows<T, D, IPW>(kb + (int64_t)16 * nxt * D, vb + (int64_t)16 * nxt * D,
+                                  min(15, g.SK - 1 - 16 * nxt), smem + (nxt % kRing) * Lay::kBytes,
+                                  lane, wave, NWI);
+        if (!has_rows) continue;
+        const char* slot = smem + (i % kRing) * Lay::kBytes;
+        u32x4_t kop[KS];
+        u32x2_t vt[D / 16];
+        rows.read_k(slot, kop);
+        rows.read_v(slot, vt);
+        Rows::lds_wait(vt);
+        const int key0 = 16 * i;
+        const int valid = min(16, kend - key0);
+        int lim[NRT];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+            lim[rt] = g.causal ? max(0, min(valid, i0 + srow_p[rt] - key0 + 1)) : valid;
+        if constexpr (MASK != 0) {
+            float bias[NRT][4];
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+                const int64_t mrow = (((int64_t)(d.mb == 1 ? 0 : b) * d.mh +
+                                       (d.mh == 1 ? 0 : srow_h[rt])) * d.mq +
+                                      (d.mq == 1 ? 0 : i0 + srow_p[rt])) * d.mw;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = d.mw == 1 ? 0 : min(key0 + 4 * g16 + e, d.mw - 1);
+                    if constexpr (MASK == 1)
+                        bias[rt][e] = static_cast<const uint8_t*>(d.mask)[mrow + j]
+                                          ? 0.f : -__builtin_inff();
+                    else
+                        bias[rt][e] = static_cast<const float*>(d.mask)[mrow + j] * kLog2e;
+                }
+            }
+            rows.template scores<true>(kop, lim, false, bias);
+        } else {
+            // every key visible to every row: whole sub-page, and causally
+            // below the block's first query
+            const bool full = valid == 16 && (!g.causal || key0 + 15 <= i0);
+            rows.scores(kop, lim, full);
+        }
+        rows.accumulate(vt, valid);
+    }
+    if (q_pending) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no keys: Q was never waited for
+    if (has_rows)
+        rows.emit_rows(d.out + head0 * g.SQ * D, [&](int r) -> int64_t {
+            if (r >= R || r % g.P >= pend) return -1;
+            return ((int64_t)(r / g.P) * g.SQ + i0 + r % g.P) * D;
+        });
+}
+
+}  // namespace pa

@@ -18,6 +18,7 @@
 #include "combine.hpp"
 #include "decode_mfma.hpp"
 #include "decode_valu.hpp"
+#include "dense_mfma.hpp"
 
 namespace {
 
@@ -567,9 +568,119 @@ int decode_entry(const pa_problem* problem, const void* q, const void* k_pool,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Dense GQA attention forward
+// ---------------------------------------------------------------------------
+int validate_dense(const pa_dense_problem* p) {
+    if (!p) return fail(PA_ERR_INVALID_ARG, "problem is NULL");
+    if (p->batch < 0 || p->q_len < 0 || p->kv_len < 0)
+        return fail(PA_ERR_INVALID_ARG, "batch (%d), q_len (%d) and kv_len (%d) must be >= 0",
+                    p->batch, p->q_len, p->kv_len);
+    if (p->num_heads < 1 || p->num_kv_heads < 1 || p->num_heads % p->num_kv_heads != 0)
+        return fail(PA_ERR_INVALID_ARG, "num_heads (%d) must be a positive multiple of "
+                    "num_kv_heads (%d)", p->num_heads, p->num_kv_heads);
+    if (p->num_heads / p->num_kv_heads > 64)
+        return fail(PA_ERR_UNSUPPORTED, "at most 64 query heads per KV head (got %d)",
+                    p->num_heads / p->num_kv_heads);
+    if (p->head_dim != 64 && p->head_dim != 128)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim %d: supported are 64 and 128", p->head_dim);
+    if (p->dtype != PA_F16 && p->dtype != PA_BF16)
+        return fail(p->dtype == PA_F32 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARG,
+                    "dtype %d: the dense kernel takes fp16 or bf16", p->dtype);
+    if (p->causal != 0 && p->causal != 1)
+        return fail(PA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (p->mask_kind < PA_MASK_NONE || p->mask_kind > PA_MASK_ADD)
+        return fail(PA_ERR_INVALID_ARG, "mask_kind %d is not a pa_mask_kind", p->mask_kind);
+    if (p->mask_kind != PA_MASK_NONE) {
+        const int32_t* m = p->mask_dims;
+        if ((m[0] != 1 && m[0] != p->batch) || (m[1] != 1 && m[1] != p->num_heads) ||
+            (m[2] != 1 && m[2] != p->q_len) || m[3] < 1 || m[3] > (p->kv_len > 0 ? p->kv_len : 1))
+            return fail(PA_ERR_INVALID_ARG, "mask_dims [%d, %d, %d, %d] must be [1|batch, "
+                        "1|num_heads, 1|q_len, 1..kv_len]", m[0], m[1], m[2], m[3]);
+    }
+    // query rows of one KV head are addressed with 32-bit byte offsets
+    const int64_t span = (int64_t)(p->num_heads / p->num_kv_heads) * p->q_len * p->head_dim * 2;
+    if (span >= (1LL << 31))
+        return fail(PA_ERR_UNSUPPORTED, "(num_heads/num_kv_heads) * q_len * head_dim is too "
+                    "large for one call; split the query length");
+    return PA_OK;
+}
+
+template <typename T, int D, int MASK>
+void launch_dense_k(const pa::DenseArgs<T>& a, unsigned grid, hipStream_t s) {
+    constexpr int kRing = D == 128 ? 4 : 8;
+    const size_t lds = (size_t)kRing * pa::SlotLayout<T, D>::kBytes;
+    hipLaunchKernelGGL((pa::dense_mfma<T, D, 2, 2, kRing, MASK>), dim3(grid), dim3(128), lds, s, a);
+}
+
+template <typename T>
+int run_dense(const pa_dense_problem* p, const void* q, const void* k, const void* v,
+              const void* mask, float scale, void* out, hipStream_t s) {
+    pa::DenseArgs<T> a;
+    a.q = static_cast<const T*>(q);
+    a.k = static_cast<const T*>(k);
+    a.v = static_cast<const T*>(v);
+    a.out = static_cast<T*>(out);
+    a.mask = mask;
+    a.mb = p->mask_dims[0];
+    a.mh = p->mask_dims[1];
+    a.mq = p->mask_dims[2];
+    a.mw = p->mask_dims[3];
+    a.g.B = p->batch;
+    a.g.HQ = p->num_heads;
+    a.g.HK = p->num_kv_heads;
+    a.g.SQ = p->q_len;
+    a.g.SK = p->kv_len;
+    a.g.G = p->num_heads / p->num_kv_heads;
+    a.g.P = 64 / a.g.G;
+    a.g.nblk = (int)ceil_div(p->q_len, a.g.P);
+    a.g.causal = p->causal;
+    a.qscale = (float)((double)scale * 1.4426950408889634);
+    const int64_t grid = (int64_t)p->batch * p->num_kv_heads * a.g.nblk;
+    if (grid >= (1LL << 31))
+        return fail(PA_ERR_UNSUPPORTED, "too many workgroups (%lld) for one call",
+                    (long long)grid);
+    const int mk = p->mask_kind;
+    if (p->head_dim == 64) {
+        if (mk == PA_MASK_BOOL) launch_dense_k<T, 64, 1>(a, (unsigned)grid, s);
+        else if (mk == PA_MASK_ADD) launch_dense_k<T, 64, 2>(a, (unsigned)grid, s);
+        else launch_dense_k<T, 64, 0>(a, (unsigned)grid, s);
+    } else {
+        if (mk == PA_MASK_BOOL) launch_dense_k<T, 128, 1>(a, (unsigned)grid, s);
+        else if (mk == PA_MASK_ADD) launch_dense_k<T, 128, 2>(a, (unsigned)grid, s);
+        else launch_dense_k<T, 128, 0>(a, (unsigned)grid, s);
+    }
+    if (hipError_t e = hipGetLastError(); e != hipSuccess)
+        return fail(PA_ERR_LAUNCH, "dense attention launch failed: %s; verify the device state",
+                    hipGetErrorString(e));
+    return succeed();
+}
+
 }  // namespace
 
 extern "C" {
+
+int pa_dense_attention(const pa_dense_problem* problem, const void* q, const void* k,
+                       const void* v, const void* mask, float scale, void* out,
+                       pa_stream_t stream) {
+    if (int rc = validate_dense(problem)) return rc;
+    const pa_dense_problem* p = problem;
+    if (p->batch == 0 || p->q_len == 0) return succeed();
+    if (!q || !out || (p->kv_len > 0 && (!k || !v)))
+        return fail(PA_ERR_INVALID_ARG, "a tensor pointer is NULL (q %p, k %p, v %p, out %p)", q,
+                    k, v, out);
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16))
+        return fail(PA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+    if (p->mask_kind != PA_MASK_NONE &&
+        (!mask || (p->mask_kind == PA_MASK_ADD && misaligned(mask, 4))))
+        return fail(PA_ERR_INVALID_ARG, "mask is NULL or (additive) not 4-byte aligned");
+    int cus = 0;
+    if (int rc = current_device_cus(&cus)) return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (p->dtype == PA_F16) return run_dense<_Float16>(p, q, k, v, mask, scale, out, s);
+    return run_dense<pa::bf16_t>(p, q, k, v, mask, scale, out, s);
+}
+
 
 int pa_plan_ex(const pa_problem* problem, int32_t num_cus, int32_t* partitions,
                int32_t* chunk_tokens, int32_t* kernel) {
@@ -663,6 +774,6 @@ int paged_attn_combine(const pa_problem* problem, const int32_t* context_lens,
 
 const char* paged_attn_last_error(void) { return t_error.c_str(); }
 
-int paged_attn_version(void) { return 102; }
+int paged_attn_version(void) { return 103; }
 
 }  // extern "C"

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(names) == set(pa.EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert pa.paged_attn_version() == 102
+    assert pa.paged_attn_version() == 103
 
 
 def spec_problem(spec: W.Spec, max_ctx: int, **kw) -> pa.PaProblem:
@@ -155,3 +155,47 @@ def test_valid_call_without_a_gfx950_device_reports_device_error(lib):
     rc = pa.paged_attn_decode(prob, *([4096] * 7), 0.1, 4096, None, 0, None,
                               raise_on_error=False)
     assert rc == pa.PA_ERR_DEVICE
+
+
+# --------------------------------------------------------------------------
+# Dense attention entry point: argument checks run on the host before any HIP call
+# --------------------------------------------------------------------------
+def _dense_problem(**kw):
+    d = dict(batch=1, num_heads=8, num_kv_heads=2, head_dim=128, q_len=32, kv_len=40, causal=1,
+             dtype=pa.PA_F16, mask_kind=pa.PA_MASK_NONE)
+    dims = kw.pop("mask_dims", None)
+    d.update(kw)
+    p = pa.PaDenseProblem(**d)
+    if dims is not None:
+        p.mask_dims[:] = list(dims)
+    return p
+
+
+DENSE_BAD = [
+    (dict(dtype=pa.PA_F32), pa.PA_ERR_UNSUPPORTED),
+    (dict(dtype=9), pa.PA_ERR_INVALID_ARG),
+    (dict(head_dim=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(num_heads=6, num_kv_heads=4), pa.PA_ERR_INVALID_ARG),
+    (dict(num_heads=130, num_kv_heads=1), pa.PA_ERR_UNSUPPORTED),
+    (dict(q_len=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(causal=2), pa.PA_ERR_INVALID_ARG),
+    (dict(mask_kind=3), pa.PA_ERR_INVALID_ARG),
+    (dict(mask_kind=pa.PA_MASK_BOOL, mask_dims=(2, 1, 1, 40)), pa.PA_ERR_INVALID_ARG),
+    (dict(mask_kind=pa.PA_MASK_BOOL, mask_dims=(1, 3, 1, 40)), pa.PA_ERR_INVALID_ARG),
+    (dict(mask_kind=pa.PA_MASK_ADD, mask_dims=(1, 8, 32, 41)), pa.PA_ERR_INVALID_ARG),
+    (dict(mask_kind=pa.PA_MASK_ADD, mask_dims=(1, 8, 32, 0)), pa.PA_ERR_INVALID_ARG),
+    (dict(num_heads=64, num_kv_heads=1, q_len=1 << 17), pa.PA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,code", DENSE_BAD, ids=lambda x: str(x))
+def test_dense_rejects(lib, kw, code):
+    rc = pa.pa_dense_attention(_dense_problem(**kw), None, None, None, None, 0.1, None,
+                               raise_on_error=False)
+    assert rc == code, pa.paged_attn_last_error()
+    assert "verify" in pa.paged_attn_last_error() or pa.paged_attn_last_error()
+
+
+def test_dense_empty_problem_is_a_no_op(lib):
+    assert pa.pa_dense_attention(_dense_problem(batch=0), None, None, None, None, 0.1, None) == 0
+    assert pa.pa_dense_attention(_dense_problem(q_len=0), None, None, None, None, 0.1, None) == 0
