@@ -7,12 +7,12 @@
 // i only if j <= i), softmax, rows with no visible key set to zero, times V.
 // GQA: query head h = kh*G + g reads KV head kh.
 //
-// A workgroup takes (sequence b, KV head kh, a block of P = 64/G query
-// positions), so it holds R = G*P <= 64 rows: every query head of the group at
-// those positions, and each K/V tile of the KV head is read once for all of
-// them. The keys stream through a ring of kRing 16-key LDS slots as in the
-// cooperative decode kernel (two waves of two row tiles, each wave issuing its
-// share of every slot's loads, one barrier per slot); the causal limit and the
+// A workgroup takes (sequence b, KV head kh, a block of P = 16*NW*NRT/G query
+// positions), so it holds R = G*P <= 16*NW*NRT rows: every query head of the
+// group at those positions, and each K/V tile of the KV head is read once for
+// all of them. The keys stream through a ring of kRing 16-key LDS slots as in
+// the cooperative decode kernel (NW waves of NRT row tiles, the issuing waves
+// sharing every slot's loads, one barrier per slot); the causal limit and the
 // mask width shorten the stream. Mask values are read per score element from
 // global memory: waiting for them drains the wave's ring, so masked runs are
 // correct but not tuned.
@@ -40,8 +40,10 @@ struct DenseArgs {
     float qscale;      // scale * log2(e)
 };
 
-// MASK: 0 none, 1 boolean, 2 additive.
-template <typename T, int D, int NW, int NRT, int kRing, int MASK>
+// MASK: 0 none, 1 boolean, 2 additive. PAIR: workgroup w takes blocks w and
+// nblk - 1 - w of its (sequence, KV head), one after the other, so that under
+// the causal limit every workgroup has the same number of keys to attend.
+template <typename T, int D, int NW, int NRT, int kRing, int MASK, bool PAIR>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dense_mfma(DenseArgs<T> d) {
     using Lay = SlotLayout<T, D>;
@@ -57,9 +59,17 @@ void dense_mfma(DenseArgs<T> d) {
     const int lane = threadIdx.x & 63, c16 = lane & 15, g16 = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const DenseGeometry& g = d.g;
-    const int blk = blockIdx.x % g.nblk;
-    const int kh = (blockIdx.x / g.nblk) % g.HK;
-    const int b = blockIdx.x / (g.nblk * g.HK);
+    const int nw = PAIR ? (g.nblk + 1) / 2 : g.nblk;  // workgroups per (b, kh)
+    const int w = blockIdx.x % nw;
+    const int kh = (blockIdx.x / nw) % g.HK;
+    const int b = blockIdx.x / (nw * g.HK);
+    for (int half = 0; half < (PAIR ? 2 : 1); ++half) {
+    const int blk = half == 0 ? w : g.nblk - 1 - w;
+    if (half == 1) {
+        if (blk == w) break;  // odd block count: the middle block has no partner
+        asm volatile("" ::: "memory");
+        __syncthreads();      // every wave is done with the ring before it is refilled
+    }
     const int i0 = blk * g.P;                // first query position of the block
     const int R = g.G * g.P;                 // rows: r = gg*P + p -> head kh*G + gg, position i0 + p
     const int pend = min(g.P, g.SQ - i0);    // positions of the block that exist (>= 1)
@@ -166,6 +176,7 @@ void dense_mfma(DenseArgs<T> d) {
             if (r >= R || r % g.P >= pend) return -1;
             return ((int64_t)(r / g.P) * g.SQ + i0 + r % g.P) * D;
         });
+    }  // blocks of this workgroup
 }
 
 }  // namespace pa
