@@ -71,6 +71,16 @@ template <> struct Mfma<_Float16> {
         return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, phi),
                                                      __builtin_bit_cast(f16x4_t, v), acc, 0, 0, 0);
     }
+    // O += P V over two sub-pages in one 32-deep product (the same cost as one
+    // 16-deep product): lane k slots 0..3 hold the first sub-page's keys
+    // 4*g .. 4*g + 3, slots 4..7 the second's, in both operands.
+    __device__ static __forceinline__ f32x4_t pv2(u32x2_t p0, u32x2_t p1, u32x2_t v0, u32x2_t v1,
+                                                  f32x4_t acc) {
+        const u32x4_t a = u32x4_t{p0[0], p0[1], p1[0], p1[1]};
+        const u32x4_t b = u32x4_t{v0[0], v0[1], v1[0], v1[1]};
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), acc, 0, 0, 0);
+    }
 };
 
 template <> struct Mfma<bf16_t> {
@@ -445,7 +455,10 @@ struct SubPageStream {
 };
 
 // ---- online-softmax state of NRT row tiles (rows 16*(rt0 + rt) + c16) ----
-template <typename T, int D, int NRT>
+// PAIRPV (fp16 only): the PV product of a sub-page waits for the next one and
+// both go through one 32-deep product; the pending half is added on its own
+// (flush) before the accumulators are rescaled and before they are read.
+template <typename T, int D, int NRT, bool PAIRPV = false>
 struct RowTiles {
     using M = Mfma<T>;
     using Lay = SlotLayout<T, D>;
@@ -459,6 +472,9 @@ struct RowTiles {
     float m[NRT], lsum[NRT];
     f32x4_t acc[NRT][NT];
     u32x2_t phi[NRT], plo[NRT];
+    static constexpr bool kPair = PAIRPV && std::is_same<T, _Float16>::value;
+    u32x2_t pend_p[NRT], pend_v[NT];  // the sub-page whose PV waits (kPair)
+    bool pv_pending = false;
     int rmod[NRT];  // query row modulo nq: its position among the new rows
 
     __device__ __forceinline__ RowTiles(const SplitArgs<T>& args, int ln, int first_tile)
@@ -514,6 +530,7 @@ struct RowTiles {
         }
     }
     __device__ __forceinline__ void reset() {
+        pv_pending = false;
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
             m[rt] = kNegMax;
@@ -595,25 +612,37 @@ struct RowTiles {
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt)
                 sc[rt][kk % NC] = M::qk(kop[kk], qop[rt][kk], sc[rt][kk % NC]);
+        float sv[NRT][4], tms[NRT];
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
             f32x4_t s = sc[rt][0];
             if constexpr (NC == 2) s += sc[rt][1];
-            float sv[4];
             if (full) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sv[i] = s[i] * a.qscale;
+                for (int i = 0; i < 4; ++i) sv[rt][i] = s[i] * a.qscale;
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    sv[i] = 4 * g16 + i < lim[rt] ? s[i] * a.qscale : -__builtin_inff();
+                    sv[rt][i] = 4 * g16 + i < lim[rt] ? s[i] * a.qscale : -__builtin_inff();
             }
             if constexpr (BIAS) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sv[i] += bias[rt][i];
+                for (int i = 0; i < 4; ++i) sv[rt][i] += bias[rt][i];
             }
             // m[rt] is the same in the 4 lanes of a row (lanes c16 + 16*g).
-            float tm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+            tms[rt] = fmaxf(fmaxf(sv[rt][0], sv[rt][1]), fmaxf(sv[rt][2], sv[rt][3]));
+        }
+        if constexpr (kPair) {
+            // a waiting PV product is at the old references: add it before any
+            // tile's accumulators are rescaled
+            bool moves = false;
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) moves = moves || tms[rt] > m[rt] + kSlack;
+            if (__any(moves)) flush();
+        }
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            float tm = tms[rt];
             if (__any(tm > m[rt] + kSlack)) {
                 tm = fmaxf(tm, __shfl_xor(tm, 16));
                 tm = fmaxf(tm, __shfl_xor(tm, 32));  // exact max of the row's 16 keys
@@ -631,7 +660,7 @@ struct RowTiles {
             }
             float p[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - m[rt]);
+            for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[rt][i] - m[rt]);
             lsum[rt] += (p[0] + p[1]) + (p[2] + p[3]);
             M::make_p(p, phi[rt], plo[rt]);
         }
@@ -646,10 +675,40 @@ struct RowTiles {
 #pragma unroll
             for (int t = 0; t < NT; ++t) vt[t] = u32x2_t{vt[t][0] & m0, vt[t][1] & m1};
         }
+        if constexpr (kPair) {
+            if (!pv_pending) {  // wait for the next sub-page
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+                for (int rt = 0; rt < NRT; ++rt) pend_p[rt] = phi[rt];
 #pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) acc[rt][t] = M::pv(phi[rt], plo[rt], vt[t], acc[rt][t]);
+                for (int t = 0; t < NT; ++t) pend_v[t] = vt[t];
+                pv_pending = true;
+                return;
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt)
+                    acc[rt][t] = M::pv2(pend_p[rt], phi[rt], pend_v[t], vt[t], acc[rt][t]);
+            pv_pending = false;
+        } else {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt)
+                    acc[rt][t] = M::pv(phi[rt], plo[rt], vt[t], acc[rt][t]);
+        }
+    }
+    // Adds a waiting PV product on its own (kPair; nothing otherwise).
+    __device__ __forceinline__ void flush() {
+        if constexpr (kPair) {
+            if (!pv_pending) return;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt)
+                    acc[rt][t] = M::pv(pend_p[rt], pend_p[rt], pend_v[t], acc[rt][t]);
+            pv_pending = false;
+        }
     }
     // Normalised rows (all of their keys attended): output row r, held in
     // acc[rt][*][i] for r = 16*(rt0 + rt) + 4*g16 + i, goes to `base` + off(r)
@@ -885,7 +944,7 @@ void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table,
                       const int32_t* __restrict__ slots) {
     using Lay = SlotLayout<T, D>;
     using Stream = SubPageStream<T, D, BS>;
-    using Rows = RowTiles<T, D, NRT>;
+    using Rows = RowTiles<T, D, NRT, true>;
     using Cur = typename Stream::Cur;
     constexpr int KS = D / 32;
     constexpr int NWI = NW < KS ? NW : KS;  // waves that issue loads
@@ -1003,6 +1062,7 @@ void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table,
             rows.scores(kop, lim, !is_new && valid == 16);
             rows.accumulate(vt, valid);
             if (piece_ends) {
+                rows.flush();
                 rows.emit(cc.b, kh, grp, piece_from_start && seq_ends);
                 rows.reset();
             }

@@ -47,7 +47,7 @@ template <typename T, int D, int NW, int NRT, int kRing, int MASK, bool PAIR>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dense_mfma(DenseArgs<T> d) {
     using Lay = SlotLayout<T, D>;
-    using Rows = RowTiles<T, D, NRT>;
+    using Rows = RowTiles<T, D, NRT, true>;
     constexpr int KS = D / 32;
     constexpr int NWI = NW < KS ? NW : KS;  // waves that issue loads
     constexpr int IPW = KS / NWI;           // instructions per half per issuing wave
@@ -171,6 +171,7 @@ void dense_mfma(DenseArgs<T> d) {
         rows.accumulate(vt, valid);
     }
     if (q_pending) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no keys: Q was never waited for
+    rows.flush();
     if (has_rows)
         rows.emit_rows(d.out + head0 * g.SQ * D, [&](int r) -> int64_t {
             if (r >= R || r % g.P >= pend) return -1;

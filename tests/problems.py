@@ -169,3 +169,71 @@ def append_problem(w: W.Workload, *, overwrite: int = 0, duplicate: bool = False
     w2 = W.Workload(spec, w.context_lens.copy(), table, nblocks, w.q.cpu(), kp, vp,
                     w.new_k.cpu(), w.new_v.cpu(), w.scale)
     return w2, slots, reads
+
+
+# ---------------------------------------------------------------------------
+# Score staircases: inputs whose running maximum moves at chosen key positions
+# ---------------------------------------------------------------------------
+STAIR_STEP_LOG2 = 9.0  # one jump of the score, in log2 units (above a slack of 8)
+
+
+def stair_levels(n_keys: int, jumps) -> np.ndarray:
+    """Level of key j: the number of jump sub-pages J (of 16 keys) with 16*J <= j."""
+    j = np.arange(n_keys)
+    return np.array([sum(1 for J in jumps if 16 * J <= x) for x in j], dtype=np.float64)
+
+
+def stair_direction(D: int, seed: int) -> torch.Tensor:
+    g = torch.Generator().manual_seed(seed)
+    return torch.where(torch.rand(D, generator=g) < 0.5, -1.0, 1.0)
+
+
+def staircase_dense(B, HQ, HK, S, D, dtype, jumps_per_seq, seed=0):
+    """q [B, HQ, S, D] = s * u with u in {-1, 1}^D and s = 1 or 0.55 by (head,
+    16-position block) parity; k = level * step * u / sqrt(D) + 0.05 noise, so
+    with scale 1/sqrt(D) the scores of sequence b rise by step * s natural-log
+    units at every jump sub-page of jumps_per_seq[b]. v is N(0, 1). Returns
+    (q, k, v, scale) as CPU tensors of the dtype."""
+    dt = {"f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    g = torch.Generator().manual_seed(seed)
+    u = stair_direction(D, seed + 1)
+    step = STAIR_STEP_LOG2 / np.log2(np.e)
+    h = torch.arange(HQ)[:, None]
+    i = torch.arange(S)[None, :]
+    s = torch.where((h + i // 16) % 2 == 0, 1.0, 0.55)            # [HQ, S]
+    q = (s[None, :, :, None] * u).expand(B, HQ, S, D).contiguous()
+    lev = torch.stack([torch.from_numpy(stair_levels(S, jumps_per_seq[b])).float()
+                       for b in range(B)])                          # [B, S]
+    k = (lev[:, None, :, None] * (step / np.sqrt(D)) * u).expand(B, HK, S, D)
+    k = k + 0.05 * torch.randn(B, HK, S, D, generator=g)
+    v = torch.randn(B, HK, S, D, generator=g)
+    return q.to(dt), k.to(dt), v.to(dt), float(np.float32(1.0 / np.sqrt(D)))
+
+
+def staircase_decode(w: W.Workload, jumps_per_seq, seed=0) -> W.Workload:
+    """The same staircase on a paged workload: q[b, h, r] = s_h * u (s_h = 1 or
+    0.55 by head parity); the key at logical position p of sequence b gets
+    level(p) * step * u / sqrt(D) + 0.05 noise through the block table, and the
+    new rows take the level of the last cached key plus one jump. Values and the
+    layout are unchanged; the scale becomes 1/sqrt(D)."""
+    s = w.spec
+    g = torch.Generator().manual_seed(seed)
+    u = stair_direction(s.D, seed + 1)
+    step = STAIR_STEP_LOG2 / np.log2(np.e)
+    dt = w.q.dtype
+    sh = torch.where(torch.arange(s.H) % 2 == 0, 1.0, 0.55)
+    q = (sh[None, :, None, None] * u).expand(s.B, s.H, s.NQ, s.D).to(dt).contiguous()
+    kp = w.k_pool.clone()
+    nk = w.new_k.clone()
+    for b in range(s.B):
+        L = int(w.context_lens[b])
+        lev = stair_levels(L, jumps_per_seq[b])
+        for p in range(L):
+            blk = int(w.block_table[b, p // s.BS])
+            row = lev[p] * (step / np.sqrt(s.D)) * u + 0.05 * torch.randn(s.KV, s.D, generator=g)
+            kp[blk, p % s.BS] = row.to(dt)
+        top = (lev[-1] if L else 0.0) + 1.0
+        nk[b] = (top * (step / np.sqrt(s.D)) * u
+                 + 0.05 * torch.randn(s.KV, s.NQ, s.D, generator=g)).to(dt)
+    return W.Workload(s, w.context_lens, w.block_table, w.num_blocks, q, kp, w.v_pool, nk,
+                      w.new_v, float(np.float32(1.0 / np.sqrt(s.D))))

@@ -314,6 +314,36 @@ def test_dense_long_causal_rows_sampled():
 
 
 # ---------------------------------------------------------------------------
+# Score staircases: the running maximum moves mid-stream, at odd and even
+# sub-pages, and in some row tiles of a wave but not the others (fp16 sums two
+# sub-pages' PV products at once, so a move can find one of them waiting)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_dense_score_staircase(dtype, causal):
+    q, k, v, scale = P.staircase_dense(2, 8, 2, 200, 128, dtype, [(2, 5), (4, 8)], seed=5)
+    expect = oracle.dense_attention(q, k, v, scale, causal=causal)
+    print(f"[gpu] dense staircase {dtype} causal={causal}", flush=True)
+    out = pa.dense_attention(q.to(DEV), k.to(DEV), v.to(DEV), scale, causal=causal)
+    torch.cuda.synchronize()
+    check_dense(out, expect, dtype)
+
+
+@pytest.mark.parametrize("case", [
+    (3, 16, 2, 128, 16, 8, "f16", (333, 200, 517)),   # 64 rows per KV head
+    (2, 16, 2, 64, 32, 4, "f16", (260, 150)),         # 32 rows, pages of 32 keys
+    (2, 16, 2, 128, 16, 8, "bf16", (333, 200)),
+], ids=lambda c: "-".join(map(str, c[:7])))
+def test_decode_score_staircase(case):
+    B, H, KV, D, BS, NQ, dtype, lens = case
+    w = P.small(B=B, H=H, KV=KV, D=D, BS=BS, NQ=NQ, causal=True, dtype=dtype, lens=lens, seed=37)
+    w = to_device(P.staircase_decode(w, [(3, 9, 15), (2, 7), (11, 20, 26)][:B], seed=9))
+    expect = ref(w)
+    for parts in (0, 1, 3):
+        check(w, gpu_decode(w, num_partitions=parts), expect)
+
+
+# ---------------------------------------------------------------------------
 # Block-table indexing: bit-exact invariants
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
