@@ -47,6 +47,8 @@ def load_library(path: str):
     lib.oracle_kv_append.restype = i
     lib.oracle_dense_attention.argtypes = [i] * 7 + [p] * 3 + [i, p, p, i, f, p]
     lib.oracle_dense_attention.restype = i
+    lib.oracle_dense_attention_backward.argtypes = [i] * 7 + [p] * 4 + [i, p, p, i, f, p, p, p]
+    lib.oracle_dense_attention_backward.restype = i
     lib.oracle_widen.argtypes = [p, ctypes.c_int64, i]
     lib.oracle_widen.restype = ctypes.c_double
     lib.oracle_num_threads.argtypes = []
@@ -199,6 +201,47 @@ def dense_attention(q, k, v, scale: float, mask=None, causal: bool = False,
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     return out
+
+
+def _dense_mask(mask):
+    """(kind, pointer, dims, kept tensor) of a 4-D dense-attention mask or None."""
+    if mask is None:
+        return MASK_NONE, None, None, None
+    m = _host(mask)
+    assert m.dim() == 4, "mask must be 4-D [mb, mh, mq, mw]"
+    if m.dtype == torch.bool:
+        kind, keep = MASK_BOOL, m.to(torch.uint8).contiguous()
+    else:
+        kind, keep = MASK_ADD, m.to(torch.float32).contiguous()
+    dims = np.ascontiguousarray(list(m.shape), dtype=np.int32)
+    return kind, ctypes.c_void_p(keep.data_ptr()), dims, keep
+
+
+def dense_attention_backward(q, k, v, dout, scale: float, mask=None, causal: bool = False,
+                             lib=None):
+    """Dense GQA backward (C oracle_dense_attention_backward): the gradients
+    (dq [B, HQ, SQ, D], dk [B, HK, SK, D], dv [B, HK, SK, D]) in double of the
+    forward `dense_attention(q, k, v, scale, mask, causal)` for the output
+    gradient `dout` [B, HQ, SQ, D] (same dtype as q)."""
+    q, k, v, dout = _host(q), _host(k), _host(v), _host(dout)
+    B, HQ, SQ, D = q.shape
+    _, HK, SK, _ = k.shape
+    assert dout.shape == q.shape and dout.dtype == q.dtype
+    kind, mptr, dims, keep = _dense_mask(mask)
+    dq = np.zeros((B, HQ, SQ, D), dtype=np.float64)
+    dk = np.zeros((B, HK, SK, D), dtype=np.float64)
+    dv = np.zeros((B, HK, SK, D), dtype=np.float64)
+    rc = _load(lib).oracle_dense_attention_backward(
+        B, HQ, HK, SQ, SK, D, _DT[q.dtype], ctypes.c_void_p(q.data_ptr()),
+        ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+        ctypes.c_void_p(dout.data_ptr()), kind, mptr,
+        dims.ctypes.data_as(ctypes.c_void_p) if dims is not None else None, int(causal),
+        ctypes.c_float(scale), dq.ctypes.data_as(ctypes.c_void_p),
+        dk.ctypes.data_as(ctypes.c_void_p), dv.ctypes.data_as(ctypes.c_void_p))
+    del keep
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return dq, dk, dv
 
 
 # ----------------------------------------------------------------------------

@@ -325,6 +325,45 @@ int oracle_paged_decode_partitioned(int B, int H, int KV, int D, int BS, int max
  *   - causal: key j is visible to query i only if j <= i (the page compares the
  *     two aranges: top-left alignment).
  */
+/* Mask bias of score (b, h, i, j) of the dense operation: 0 or -inf for a
+ * boolean mask, the stored value for an additive one, -inf past a short mask
+ * width and, when causal, for keys after the query (top-left). */
+static double dense_bias(int b, int h, int i, int j, int mask_kind, const void* mask, int mb,
+                         int mh, int mq, int mw, int causal)
+{
+    double bias = 0.0;
+    if (mask_kind) {
+        if (mw != 1 && j >= mw) {
+            bias = -INFINITY;
+        } else {
+            const int64_t mi = (((int64_t)(mb == 1 ? 0 : b) * mh + (mh == 1 ? 0 : h)) * mq +
+                                (mq == 1 ? 0 : i)) * mw + (mw == 1 ? 0 : j);
+            if (mask_kind == 1)
+                bias = ((const uint8_t*)mask)[mi] ? 0.0 : -INFINITY;
+            else
+                bias = (double)((const float*)mask)[mi];
+        }
+    }
+    if (causal && j > i)
+        bias = -INFINITY;
+    return bias;
+}
+
+static int dense_mask_dims(int B, int HQ, int SQ, int SK, int mask_kind, const void* mask,
+                           const int32_t* mask_dims, int* mb, int* mh, int* mq, int* mw)
+{
+    *mb = *mh = *mq = *mw = 1;
+    if (!mask_kind)
+        return 0;
+    if (!mask || !mask_dims)
+        return -7;
+    *mb = mask_dims[0]; *mh = mask_dims[1]; *mq = mask_dims[2]; *mw = mask_dims[3];
+    if ((*mb != 1 && *mb != B) || (*mh != 1 && *mh != HQ) || (*mq != 1 && *mq != SQ) || *mw < 1 ||
+        *mw > (SK > 0 ? SK : 1))
+        return -8;
+    return 0;
+}
+
 int oracle_dense_attention(int B, int HQ, int HK, int SQ, int SK, int D, int dtype,
                            const void* q, const void* k, const void* v, int mask_kind,
                            const void* mask, const int32_t* mask_dims, int causal,
@@ -334,15 +373,10 @@ int oracle_dense_attention(int B, int HQ, int HK, int SQ, int SK, int D, int dty
         return -1;
     if (dtype < 0 || dtype > 2 || mask_kind < 0 || mask_kind > 2)
         return -3;
-    int mb = 1, mh = 1, mq = 1, mw = 1;
-    if (mask_kind) {
-        if (!mask || !mask_dims)
-            return -7;
-        mb = mask_dims[0]; mh = mask_dims[1]; mq = mask_dims[2]; mw = mask_dims[3];
-        if ((mb != 1 && mb != B) || (mh != 1 && mh != HQ) || (mq != 1 && mq != SQ) || mw < 1 ||
-            mw > (SK > 0 ? SK : 1))
-            return -8;
-    }
+    int mb, mh, mq, mw;
+    const int mrc = dense_mask_dims(B, HQ, SQ, SK, mask_kind, mask, mask_dims, &mb, &mh, &mq, &mw);
+    if (mrc)
+        return mrc;
     const int G = HQ / HK;
     const double sc = (double)scale;
     int failed = 0;
@@ -368,22 +402,7 @@ int oracle_dense_attention(int B, int HQ, int HK, int SQ, int SK, int D, int dty
             double dot = 0.0;
             for (int d = 0; d < D; ++d)
                 dot += qr[d] * oracle_widen(k, krow * D + d, dtype);
-            double bias = 0.0;
-            if (mask_kind) {
-                if (mw != 1 && j >= mw) {
-                    bias = -INFINITY;
-                } else {
-                    const int64_t mi = (((int64_t)(mb == 1 ? 0 : b) * mh + (mh == 1 ? 0 : h)) * mq +
-                                        (mq == 1 ? 0 : i)) * mw + (mw == 1 ? 0 : j);
-                    if (mask_kind == 1)
-                        bias = ((const uint8_t*)mask)[mi] ? 0.0 : -INFINITY;
-                    else
-                        bias = (double)((const float*)mask)[mi];
-                }
-            }
-            if (causal && j > i)
-                bias = -INFINITY;
-            s[j] = sc * dot + bias;
+            s[j] = sc * dot + dense_bias(b, h, i, j, mask_kind, mask, mb, mh, mq, mw, causal);
             if (s[j] > m)
                 m = s[j];
         }
@@ -404,6 +423,113 @@ int oracle_dense_attention(int B, int HQ, int HK, int SQ, int SK, int D, int dty
                 out[row * D + d] /= z;
         }
         free(s); free(qr);
+    }
+    return failed ? -6 : 0;
+}
+
+/*
+ * Dense GQA attention backward: the gradient part of execute() on the docs.rs
+ * page "onnxruntime-ep-mlx 0.31.1: src/ops/attention_vjp/dense.rs". The
+ * forward is recomputed exactly as oracle_dense_attention does (P, Y); then,
+ * per query row, dP_j = <dY, v_j>, delta = sum_d Y_d dY_d, dS_j = P_j (dP_j -
+ * delta), dQ = scale * sum_j dS_j k_j, and KV head kh collects over the G query
+ * heads that read it dK_j += scale * dS_j q and dV_j += P_j dY. The page scales
+ * q and k by sqrt(scale) each and multiplies the two products by sqrt(scale)
+ * once more, which gives the same scale * (...) written here. Rows with every
+ * key masked have P = 0 and contribute nothing. Work is split over (b, kh), so
+ * each dK/dV row has one writer.
+ */
+int oracle_dense_attention_backward(int B, int HQ, int HK, int SQ, int SK, int D, int dtype,
+                                    const void* q, const void* k, const void* v,
+                                    const void* dout, int mask_kind, const void* mask,
+                                    const int32_t* mask_dims, int causal, float scale,
+                                    double* dq, double* dk, double* dv)
+{
+    if (B < 0 || HQ <= 0 || HK <= 0 || SQ < 0 || SK < 0 || D <= 0 || HQ % HK != 0)
+        return -1;
+    if (dtype < 0 || dtype > 2 || mask_kind < 0 || mask_kind > 2)
+        return -3;
+    int mb, mh, mq, mw;
+    const int mrc = dense_mask_dims(B, HQ, SQ, SK, mask_kind, mask, mask_dims, &mb, &mh, &mq, &mw);
+    if (mrc)
+        return mrc;
+    const int G = HQ / HK;
+    const double sc = (double)scale;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t unit = 0; unit < (int64_t)B * HK; ++unit) {
+        const int b = (int)(unit / HK), kh = (int)(unit % HK);
+        const size_t nk = (size_t)(SK > 0 ? SK : 1);
+        double* s = (double*)malloc(sizeof(double) * nk);    /* scores, then P */
+        double* dp = (double*)malloc(sizeof(double) * nk);
+        double* qr = (double*)malloc(sizeof(double) * (size_t)D);
+        double* gy = (double*)malloc(sizeof(double) * (size_t)D);  /* dY row */
+        double* y = (double*)malloc(sizeof(double) * (size_t)D);
+        if (!s || !dp || !qr || !gy || !y) {
+#pragma omp atomic write
+            failed = 1;
+            free(s); free(dp); free(qr); free(gy); free(y);
+            continue;
+        }
+        const int64_t kv0 = ((int64_t)b * HK + kh) * SK; /* first key row of the unit */
+        for (int64_t e = kv0 * D; e < (kv0 + SK) * D; ++e)
+            dk[e] = dv[e] = 0.0;
+        for (int g = 0; g < G; ++g) {
+            const int h = g + kh * G; /* the G query heads that read KV head kh */
+            for (int i = 0; i < SQ; ++i) {
+                const int64_t row = ((int64_t)b * HQ + h) * SQ + i;
+                for (int d = 0; d < D; ++d) {
+                    qr[d] = oracle_widen(q, row * D + d, dtype);
+                    gy[d] = oracle_widen(dout, row * D + d, dtype);
+                    dq[row * D + d] = 0.0;
+                }
+                /* forward recompute: P (softmax of the scores) and Y */
+                double m = -INFINITY;
+                for (int j = 0; j < SK; ++j) {
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        dot += qr[d] * oracle_widen(k, (kv0 + j) * D + d, dtype);
+                    s[j] = sc * dot + dense_bias(b, h, i, j, mask_kind, mask, mb, mh, mq, mw, causal);
+                    if (s[j] > m)
+                        m = s[j];
+                }
+                if (m == -INFINITY)
+                    continue; /* every key masked: P = 0, no gradient */
+                double z = 0.0;
+                for (int j = 0; j < SK; ++j) {
+                    s[j] = exp(s[j] - m);
+                    z += s[j];
+                }
+                for (int d = 0; d < D; ++d)
+                    y[d] = 0.0;
+                for (int j = 0; j < SK; ++j) {
+                    s[j] /= z;
+                    for (int d = 0; d < D; ++d)
+                        y[d] += s[j] * oracle_widen(v, (kv0 + j) * D + d, dtype);
+                }
+                /* dP, delta, dS */
+                double delta = 0.0;
+                for (int d = 0; d < D; ++d)
+                    delta += y[d] * gy[d];
+                for (int j = 0; j < SK; ++j) {
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        dot += gy[d] * oracle_widen(v, (kv0 + j) * D + d, dtype);
+                    dp[j] = s[j] * (dot - delta); /* dS_j */
+                }
+                /* dQ, and this row's share of dK and dV */
+                for (int j = 0; j < SK; ++j) {
+                    if (s[j] == 0.0)
+                        continue;
+                    for (int d = 0; d < D; ++d) {
+                        dq[row * D + d] += sc * dp[j] * oracle_widen(k, (kv0 + j) * D + d, dtype);
+                        dk[(kv0 + j) * D + d] += sc * dp[j] * qr[d];
+                        dv[(kv0 + j) * D + d] += s[j] * gy[d];
+                    }
+                }
+            }
+        }
+        free(s); free(dp); free(qr); free(gy); free(y);
     }
     return failed ? -6 : 0;
 }

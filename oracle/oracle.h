@@ -84,6 +84,19 @@ int oracle_dense_attention(int B, int HQ, int HK, int SQ, int SK, int D, int dty
                            const void* mask, const int32_t* mask_dims, int causal,
                            float scale, double* out);
 
+/*
+ * Dense GQA attention backward (the same page, execute()'s gradients): given
+ * dout = dY [B, HQ, SQ, D] of the forward above (same inputs, mask and causal
+ * flag), dq [B, HQ, SQ, D], dk and dv [B, HK, SK, D] (double) receive the
+ * gradients: dS = P * (dY V^T - rowsum(Y * dY)), dQ = scale dS K, dK = scale
+ * dS^T Q and dV = P^T dY, dK and dV summed over the G query heads of a KV head.
+ */
+int oracle_dense_attention_backward(int B, int HQ, int HK, int SQ, int SK, int D, int dtype,
+                                    const void* q, const void* k, const void* v,
+                                    const void* dout, int mask_kind, const void* mask,
+                                    const int32_t* mask_dims, int causal, float scale,
+                                    double* dq, double* dk, double* dv);
+
 /* Exact widening of one stored element (exported so tests can pin it). */
 double oracle_widen(const void* base, int64_t index, int dtype);
 

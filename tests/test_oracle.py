@@ -414,6 +414,112 @@ def test_dense_additive_bias_semantics():
 
 
 # --------------------------------------------------------------------------
+# Dense GQA backward
+# --------------------------------------------------------------------------
+def _full_bias(B, HQ, SQ, SK, mask, causal):
+    """[B, HQ, SQ, SK] float64 bias of the dense problem, built independently of
+    the oracle: bool -> 0/-inf, additive as is, -inf past a short width, -inf
+    above the top-left diagonal when causal."""
+    bias = torch.zeros(B, HQ, SQ, SK, dtype=torch.float64)
+    if mask is not None:
+        mw = mask.shape[3]
+        m = mask if mask.dtype != torch.bool else torch.where(
+            mask, torch.tensor(0.0), torch.tensor(float("-inf")))
+        m = m.double()
+        if mw != 1 and mw < SK:
+            m = torch.cat([m, torch.full(m.shape[:3] + (SK - mw,), float("-inf"),
+                                         dtype=torch.float64)], dim=3)
+        bias = bias + m.expand(B, HQ, SQ, SK)
+    if causal:
+        hide = torch.arange(SK)[None, :] > torch.arange(SQ)[:, None]
+        bias = bias.masked_fill(hide, float("-inf"))
+    return bias
+
+
+def _autograd_dense(q, k, v, dout, scale, mask=None, causal=False):
+    """Gradients of sum(Y * dout) by torch float64 autograd of a separate
+    formulation: K/V repeated to every query head, scores scale * Q K^T + bias,
+    softmax with rows of no visible key set to zero, Y = P V."""
+    B, HQ, SQ, D = q.shape
+    HK, SK = k.shape[1], k.shape[2]
+    G = HQ // HK
+    bias = _full_bias(B, HQ, SQ, SK, mask, causal)
+    empty = torch.isinf(bias).all(dim=-1) & (bias.amax(dim=-1) < 0)
+    qd = q.double().requires_grad_()
+    kd = k.double().requires_grad_()
+    vd = v.double().requires_grad_()
+    s = float(np.float32(scale)) * (qd @ kd.repeat_interleave(G, dim=1).transpose(-1, -2)) + bias
+    s = s.masked_fill(empty[..., None], 0.0)
+    p = torch.softmax(s, dim=-1).masked_fill(empty[..., None], 0.0)
+    y = p @ vd.repeat_interleave(G, dim=1)
+    (y * dout.double()).sum().backward()
+    return qd.grad.numpy(), kd.grad.numpy(), vd.grad.numpy()
+
+
+def _bwd_case(case, seed=0):
+    B, HQ, HK, SQ, SK, D, dtype, kind, dims, causal = case
+    q, k, v = _dense_inputs(B, HQ, HK, SQ, SK, D, dtype, seed=SQ + SK + seed)
+    g = torch.Generator().manual_seed(100 + seed)
+    dout = torch.randn(B, HQ, SQ, D, generator=g).to(q.dtype)
+    mask = _mask(kind, dims, seed=3) if kind else None
+    return q, k, v, dout, mask, causal
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=lambda c: "-".join(map(str, c[:8])) + ("-c" if c[9] else ""))
+def test_dense_backward_matches_autograd(case):
+    q, k, v, dout, mask, causal = _bwd_case(case)
+    got = oracle.dense_attention_backward(q, k, v, dout, 0.2, mask=mask, causal=causal)
+    exp = _autograd_dense(q, k, v, dout, 0.2, mask=mask, causal=causal)
+    for a, b in zip(got, exp):
+        assert np.abs(a - b).max() < 1e-11
+
+
+def test_dense_backward_finite_differences():
+    # central differences of the forward oracle's loss sum(Y * dout), inputs in
+    # float32 moved by 2^-12 (exact in float32 for these magnitudes)
+    B, HQ, HK, SQ, SK, D = 1, 4, 2, 5, 7, 16
+    q, k, v = _dense_inputs(B, HQ, HK, SQ, SK, D, "f32", seed=9)
+    dout = torch.randn(B, HQ, SQ, D, generator=torch.Generator().manual_seed(10))
+    mask = _mask("add", (1, 1, SQ, SK), seed=11)
+    scale, h = 0.3, 2.0 ** -12
+    dq, dk, dv = oracle.dense_attention_backward(q, k, v, dout, scale, mask=mask, causal=True)
+
+    def loss(qq, kk, vv):
+        y = oracle.dense_attention(qq, kk, vv, scale, mask=mask, causal=True)
+        return float((y * dout.double().numpy()).sum())
+
+    rng = np.random.default_rng(12)
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        base = [q, k, v][which]
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, n)) for n in base.shape)
+            plus, minus = base.clone(), base.clone()
+            plus[idx] += h
+            minus[idx] -= h
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = plus, minus
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - grad[idx]) < 1e-6 * max(1.0, abs(grad[idx])), (which, idx, fd, grad[idx])
+
+
+def test_dense_backward_invariants():
+    # Every row's dS sums to 0 over its keys, so the key-gradients of a KV head
+    # sum to 0; rows of P sum to 1, so its value-gradients sum to the dout rows
+    # of its G query heads (rows that see at least one key)
+    case = (2, 6, 2, 9, 13, 32, "f32", "bool", (2, 1, 9, 13), True)
+    q, k, v, dout, mask, causal = _bwd_case(case, seed=1)
+    mask[1, 0, 4] = False  # one row of batch 1 sees nothing
+    dq, dk, dv = oracle.dense_attention_backward(q, k, v, dout, 0.25, mask=mask, causal=causal)
+    assert np.abs(dk.sum(axis=2)).max() < 1e-12
+    bias = _full_bias(2, 6, 9, 13, mask, causal)
+    seen = ~(torch.isinf(bias).all(dim=-1))  # [B, HQ, SQ]
+    want = (dout.double() * seen[..., None]).reshape(2, 2, 3, 9, 32).sum(dim=(2, 3)).numpy()
+    assert np.abs(dv.sum(axis=2) - want).max() < 1e-12
+    assert (dq[1, :, 4] == 0).all()
+
+
+# --------------------------------------------------------------------------
 # Mutation check: each planted mistake must trip at least one pin.
 # --------------------------------------------------------------------------
 def _pins(lib):
@@ -464,6 +570,14 @@ def _pins(lib):
             if np.abs(ref[~empty] - exp[~empty]).max() > 1e-12 or (ref[empty] != 0).any():
                 failed.append("dense")
                 break
+        for case in (DENSE_CASES[2], DENSE_CASES[4], DENSE_CASES[5], DENSE_CASES[6]):
+            q, k, v, dout, mask, causal = _bwd_case(case)
+            got = oracle.dense_attention_backward(q, k, v, dout, 0.2, mask=mask, causal=causal,
+                                                  lib=lib)
+            exp = _autograd_dense(q, k, v, dout, 0.2, mask=mask, causal=causal)
+            if any(np.abs(a - b).max() > 1e-11 for a, b in zip(got, exp)):
+                failed.append("dense_backward")
+                break
     except ValueError:
         failed.append("rejected")
     return failed
@@ -493,12 +607,26 @@ MUTATIONS = {
                                "for (int kh = 0; kh < 1; ++kh) {\n                const int64_t row"),
     "append_rows_of_head_0": ("const int64_t row = ((int64_t)b * KV + kh) * NQ + j;",
                               "const int64_t row = ((int64_t)b * KV) * NQ + j;"),
-    "dense_causal_bottom_right": ("if (causal && j > i)", "if (causal && j > i + SK - SQ)"),
+    "dense_causal_shifted_diagonal": ("if (causal && j > i)", "if (causal && j > i - 2)"),
     "dense_head_mapping": ("const int kh = h / G; /* query head h = kh*G + g */",
                            "const int kh = h % HK; /* query head h = kh*G + g */"),
     "dense_pad_off_by_one": ("if (mw != 1 && j >= mw) {", "if (mw != 1 && j > mw) {"),
-    "dense_mask_head_index": ("(mh == 1 ? 0 : h)) * mq", "(mh == 1 ? 0 : kh)) * mq"),
-    "dense_bias_scaled": ("s[j] = sc * dot + bias;", "s[j] = sc * (dot + bias);"),
+    "dense_mask_head_index": ("(mh == 1 ? 0 : h)) * mq", "(mh == 1 ? 0 : h / 2)) * mq"),
+    "dense_bias_scaled": ("\n            s[j] = sc * dot + dense_bias(",
+                          "\n            s[j] = sc * 2.0 * dot + dense_bias("),
+    "dense_bias_doubled": ("bias = (double)((const float*)mask)[mi];",
+                           "bias = 2.0 * (double)((const float*)mask)[mi];"),
+    "bwd_head_mapping": ("const int h = g + kh * G;", "const int h = g * HK + kh;"),
+    "bwd_drop_delta": ("dp[j] = s[j] * (dot - delta);", "dp[j] = s[j] * dot;"),
+    "bwd_dk_first_head_only": ("dk[(kv0 + j) * D + d] += sc * dp[j] * qr[d];",
+                               "if (g == 0) dk[(kv0 + j) * D + d] += sc * dp[j] * qr[d];"),
+    "bwd_dq_without_scale": ("dq[row * D + d] += sc * dp[j] *", "dq[row * D + d] += dp[j] *"),
+    "bwd_dv_from_y": ("dv[(kv0 + j) * D + d] += s[j] * gy[d];",
+                      "dv[(kv0 + j) * D + d] += s[j] * y[d];"),
+    "bwd_dp_from_keys": ("dot += gy[d] * oracle_widen(v,", "dot += gy[d] * oracle_widen(k,"),
+    "bwd_dk_from_dout": ("dk[(kv0 + j) * D + d] += sc * dp[j] * qr[d];",
+                         "dk[(kv0 + j) * D + d] += sc * dp[j] * gy[d];"),
+    "bwd_unnormalised_p": ("                    s[j] /= z;\n", "                    s[j] /= 1.0;\n"),
 }
 
 
