@@ -158,6 +158,47 @@ def dense_prefill(torch, pa, timed, warmup: int) -> dict:
     }
 
 
+def dense_backward(torch, pa, timed, warmup: int) -> dict:
+    """pa_dense_attention_backward on the same causal prefill (dq, dk, dv for a
+    synthetic output gradient): algorithmic flops 10*D per visible pair (five
+    products of 2*D: the score recompute, dP, dV, dQ and dK), against the fp16
+    matrix-core peak."""
+    B, HQ, HK, S, D = 1, 32, 8, 2048, 128
+    g = torch.Generator(device="cuda:0").manual_seed(1200)
+    q = torch.randn(B, HQ, S, D, generator=g, device="cuda:0").half()
+    k = torch.randn(B, HK, S, D, generator=g, device="cuda:0").half()
+    v = torch.randn(B, HK, S, D, generator=g, device="cuda:0").half()
+    dout = torch.randn(B, HQ, S, D, generator=g, device="cuda:0").half()
+    scale = 1.0 / D ** 0.5
+    prob = pa.make_dense_problem(q, k, causal=True)
+    _, need = pa.pa_dense_backward_workspace_size(prob)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        pa.pa_dense_attention_backward(prob, q, k, v, None, dout, scale, dq, dk, dv, ws, need,
+                                       stream)
+
+    for i in range(min(warmup, 50)):
+        call(i)
+    ms = timed(call, 50)
+    flop = 10 * D * HQ * B * S * (S + 1) // 2
+    tflops = flop / (ms / 1e3) / 1e12
+    log(f"[bench] dense causal backward {ms * 1e3:.1f} us, {tflops:.1f} TFLOP/s")
+    return {
+        "entry_point": "pa_dense_attention_backward",
+        "config": {"workload": "causal prefill backward", "batch": B, "num_heads": HQ,
+                   "num_kv_heads": HK, "q_len": S, "kv_len": S, "head_dim": D,
+                   "dtype": "f16", "causal": True, "mask": None},
+        "us_per_call": round(ms * 1e3, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                     "algorithmic_flop_per_call": flop},
+    }
+
+
 def percentile(sorted_values, q) -> float:
     """Linear-interpolation percentile of an ascending list."""
     x = (len(sorted_values) - 1) * q / 100.0
@@ -315,6 +356,7 @@ def main():
         f"plain step on the same pools {ms_plain_ext * 1e3:.2f} us/step")
 
     dense = dense_prefill(torch, pa, timed, args.warmup)
+    dense_bwd = dense_backward(torch, pa, timed, args.warmup)
 
     copy_gbps = copy_bandwidth(torch)
     log(f"[bench] device copy bandwidth {copy_gbps:.0f} GB/s (read+write)")
@@ -379,6 +421,7 @@ def main():
             "slots": "every new row into a spare slot past the cached blocks (no read patched)",
         },
         "dense_prefill": dense,
+        "dense_backward": dense_bwd,
         "device_copy_gbps": round(copy_gbps, 1),
         "cpu_baseline": cpu,
     }

@@ -254,12 +254,39 @@ int pa_dense_attention(const pa_dense_problem* problem, const void* q, const voi
                        const void* v, const void* mask, float scale, void* out,
                        pa_stream_t stream);
 
+/*
+ * Dense GQA attention backward: the gradient half of execute() on the same
+ * page ("onnxruntime-ep-mlx 0.31.1: src/ops/attention_vjp/dense.rs"). For the
+ * forward of pa_dense_attention on the same problem, inputs and mask, and the
+ * output gradient dout = dY [batch, num_heads, q_len, head_dim], it recomputes
+ * P (the softmax rows, 0 for rows with no visible key) and Y = P V, and writes
+ *   dS = P * (dY V^T - rowsum(Y * dY))      (per query row)
+ *   dq = scale * dS K                       [batch, num_heads, q_len, head_dim]
+ *   dk = scale * sum over the group dS^T Q  [batch, num_kv_heads, kv_len, head_dim]
+ *   dv = sum over the group P^T dY          [batch, num_kv_heads, kv_len, head_dim]
+ * where the group of KV head kh is the query heads kh*G .. kh*G + G - 1
+ * (G = num_heads / num_kv_heads). Products accumulate in fp32 and are rounded
+ * once to the I/O dtype. `workspace` (device, 256-byte aligned, at least
+ * pa_dense_backward_workspace_size bytes, no initial contents required) holds
+ * two fp32 values per query row between the launches; dq, dk and dv are
+ * written whole; nothing else is written. Device pointers are owned by the
+ * caller; asynchronous on `stream`. Supported shapes and errors as for
+ * pa_dense_attention, plus PA_ERR_WORKSPACE for a missing, small or
+ * misaligned workspace.
+ */
+int pa_dense_backward_workspace_size(const pa_dense_problem* problem, size_t* bytes);
+
+int pa_dense_attention_backward(const pa_dense_problem* problem, const void* q, const void* k,
+                                const void* v, const void* mask, const void* dout, float scale,
+                                void* dq, void* dk, void* dv, void* workspace,
+                                size_t workspace_bytes, pa_stream_t stream);
+
 /* Message of the last failing call on this thread ("" if none). Valid until the
  * next call on this thread. */
 const char* paged_attn_last_error(void);
 
 /* ABI version of this header (major * 100 + minor). */
-int paged_attn_version(void);  /* 103: pa_dense_attention */
+int paged_attn_version(void);  /* 104: pa_dense_attention_backward */
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,8 @@ PA_MASK_NONE, PA_MASK_BOOL, PA_MASK_ADD = 0, 1, 2
 
 EXPORTED = ("pa_plan_ex", "pa_plan", "pa_workspace_size", "pa_workspace_size_ex",
             "paged_attn_decode", "paged_attn_decode_append", "paged_attn_combine",
-            "pa_dense_attention", "paged_attn_last_error", "paged_attn_version")
+            "pa_dense_attention", "pa_dense_backward_workspace_size",
+            "pa_dense_attention_backward", "paged_attn_last_error", "paged_attn_version")
 
 
 class PaProblem(ctypes.Structure):
@@ -81,6 +82,13 @@ def library(path: Optional[str] = None):
     lib.pa_dense_attention.argtypes = [ctypes.POINTER(PaDenseProblem), vp, vp, vp, vp,
                                        ctypes.c_float, vp, vp]
     lib.pa_dense_attention.restype = ctypes.c_int
+    lib.pa_dense_backward_workspace_size.argtypes = [ctypes.POINTER(PaDenseProblem),
+                                                     ctypes.POINTER(ctypes.c_size_t)]
+    lib.pa_dense_backward_workspace_size.restype = ctypes.c_int
+    lib.pa_dense_attention_backward.argtypes = [ctypes.POINTER(PaDenseProblem), vp, vp, vp, vp,
+                                                vp, ctypes.c_float, vp, vp, vp, vp,
+                                                ctypes.c_size_t, vp]
+    lib.pa_dense_attention_backward.restype = ctypes.c_int
     lib.paged_attn_last_error.argtypes = []
     lib.paged_attn_last_error.restype = ctypes.c_char_p
     lib.paged_attn_version.argtypes = []
@@ -199,6 +207,26 @@ def pa_dense_attention(problem: PaDenseProblem, q, k, v, mask, scale: float, out
     return rc
 
 
+def pa_dense_backward_workspace_size(problem: PaDenseProblem, raise_on_error: bool = True):
+    n = ctypes.c_size_t()
+    rc = library().pa_dense_backward_workspace_size(ctypes.byref(problem), ctypes.byref(n))
+    if raise_on_error:
+        _check(rc)
+    return rc, n.value
+
+
+def pa_dense_attention_backward(problem: PaDenseProblem, q, k, v, mask, dout, scale: float, dq,
+                                dk, dv, workspace, workspace_bytes: int, stream=None,
+                                raise_on_error: bool = True) -> int:
+    rc = library().pa_dense_attention_backward(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(dout),
+        ctypes.c_float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+        ctypes.c_size_t(workspace_bytes), _stream(stream))
+    if raise_on_error:
+        _check(rc)
+    return rc
+
+
 def paged_attn_version() -> int:
     return library().paged_attn_version()
 
@@ -310,3 +338,25 @@ def dense_attention(q, k, v, scale: float, *, mask=None, causal: bool = False, o
         stream = torch.cuda.current_stream()
     pa_dense_attention(prob, q, k, v, mask, scale, out, stream)
     return out
+
+
+def dense_attention_backward(q, k, v, dout, scale: float, *, mask=None, causal: bool = False,
+                             stream=None, workspace=None):
+    """Dense GQA attention backward for the forward dense_attention(q, k, v,
+    scale, mask=mask, causal=causal) and the output gradient dout (same shape
+    and dtype as q). Returns (dq, dk, dv), with dk and dv summed over the query
+    heads of each KV head."""
+    import torch
+    if mask is not None:
+        mask = mask.to(torch.uint8) if mask.dtype == torch.bool else mask.to(torch.float32)
+        mask = mask.contiguous()
+    prob = make_dense_problem(q, k, causal=causal, mask=mask)
+    _, need = pa_dense_backward_workspace_size(prob)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    pa_dense_attention_backward(prob, q, k, v, mask, dout, scale, dq, dk, dv, workspace,
+                                workspace.numel(), stream)
+    return dq, dk, dv

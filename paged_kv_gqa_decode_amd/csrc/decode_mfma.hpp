@@ -454,6 +454,61 @@ struct SubPageStream {
     }
 };
 
+// ---- operand reads from a slot (lane = 16*g16 + c16) ----
+// Rows: the 16-byte chunks 4*kk + g16 of row c16 of the slot's first half, for
+// kk < D/32: an MFMA operand whose lane holds row c16 and elements 32*kk +
+// 8*g16 .. +7 (A of a product whose rows are the slot's rows, or B of one whose
+// columns are). Chunk 4*kk + g16 of row c16 sits at c16*R + (((g16 ^ swz(c16))
+// ^ 4*kk) << 4), so the address of step kk is one base XOR (kk << 6); the base
+// is recomputed per call (opaque to the optimizer) rather than kept as D/32
+// live registers. (LDS-space pointers: a generic pointer would become a flat
+// load, which the vector-memory counter also counts, so waiting for the
+// operand would wait for every pool load in flight.)
+template <typename T, int D>
+__device__ __forceinline__ void slot_read_rows(const char* slot, int c16, int g16,
+                                               u32x4_t (&op)[D / 32]) {
+    using Lay = SlotLayout<T, D>;
+    typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
+    uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(slot) + Lay::k_addr(c16, g16);
+    asm volatile("" : "+v"(base));
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+        op[kk] = *(lds_u32x4*)(uintptr_t)(base ^ (uint32_t)(kk << 6));
+}
+// Columns of the slot's second half for the D/16 column tiles: the B operand
+// of a 16-deep product whose contraction runs over the slot's rows, tile t =
+// X[row 4*g16 + j][col 16*t + c16], j = 0..3, read with one transposing LDS
+// read: within a 16-lane group, lane s supplies row 4*g16 + s/4, columns 16*t +
+// 4*(s%4) .. +3, and lane c16 receives column c16 of the 4 rows. (Chunk 2*t + h
+// of a row sits at ((2*t + h) ^ vswz) << 4 = base ^ (t << 5): one base per
+// call.) The reads are issued as inline assembly: the compiler treats its
+// transposing-read builtin as possibly aliasing the buffer-to-LDS loads in
+// flight and would wait for all of them first. The results are only valid
+// after slot_lds_wait(), which ties them to an LDS-counter wait.
+template <typename T, int D>
+__device__ __forceinline__ void slot_read_cols(const char* slot, int c16, int g16,
+                                               u32x2_t (&vt)[D / 16]) {
+    using Lay = SlotLayout<T, D>;
+    const int s = c16;
+    const int row = 4 * g16 + s / 4;
+    uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(slot) + Lay::kKBytes +
+                    Lay::v_addr(row, (s & 3) >> 1) + 8 * (s & 1);
+    asm volatile("" : "+v"(base));
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+        const uint32_t p = base ^ (uint32_t)(t << 5);
+        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vt[t]) : "v"(p) : "memory");
+    }
+}
+// Waits for every LDS read of this wave (and its scalar loads); values read by
+// slot_read_cols are used only through this call's outputs.
+template <int D>
+__device__ __forceinline__ void slot_lds_wait(u32x2_t (&vt)[D / 16]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) asm volatile("" : "+v"(vt[t]));
+}
+
 // ---- online-softmax state of NRT row tiles (rows 16*(rt0 + rt) + c16) ----
 // PAIRPV (fp16 only): the PV product of a sub-page waits for the next one and
 // both go through one 32-deep product; the pending half is added on its own
@@ -539,50 +594,16 @@ struct RowTiles {
             for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     }
-    // K operands of one sub-page, read from a slot (256-byte aligned). Chunk
-    // 4*kk + g16 of key c16 sits at c16*R + (((g16 ^ swz(c16)) ^ 4*kk) << 4), so
-    // the address of step kk is one base XOR (kk << 6); the base is recomputed
-    // per call (opaque to the optimizer) rather than kept as KS live registers.
-    // (LDS-space pointers: a generic pointer would become a flat load, which
-    // the vector-memory counter also counts, so waiting for the operand would
-    // wait for every pool load in flight.)
+    // K operands of one sub-page (A of S^T = K Q^T), read from a slot.
     __device__ __forceinline__ void read_k(const char* slot, u32x4_t (&kop)[KS]) const {
-        typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
-        uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(slot) + Lay::k_addr(c16, g16);
-        asm volatile("" : "+v"(base));
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-            kop[kk] = *(lds_u32x4*)(uintptr_t)(base ^ (uint32_t)(kk << 6));
+        slot_read_rows<T, D>(slot, c16, g16, kop);
     }
-    // V operands of the NT output tiles: B of O += P V for tile t is V[key
-    // 4*g16 + j][d = 16*t + c16], j = 0..3, read with one transposing LDS read:
-    // within a 16-lane group, lane s supplies row 4*g16 + s/4, columns
-    // 16*t + 4*(s%4) .. +3, and lane c16 receives column c16 of the 4 rows.
-    // (Chunk 2*t + h of a row sits at ((2*t + h) ^ vswz) << 4 = base ^ (t << 5):
-    // one base per call, recomputed per call like read_k's.)
-    // The reads are issued as inline assembly: the compiler treats its
-    // transposing-read builtin as possibly aliasing the buffer-to-LDS loads in
-    // flight and would wait for all of them first. The results are only valid
-    // after lds_wait(), which ties them to an LDS-counter wait.
+    // V operands of the NT output tiles (B of O += P V), read from a slot;
+    // valid after lds_wait().
     __device__ __forceinline__ void read_v(const char* slot, u32x2_t (&vt)[NT]) const {
-        const int s = c16;
-        const int row = 4 * g16 + s / 4;
-        uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(slot) + Lay::kKBytes +
-                        Lay::v_addr(row, (s & 3) >> 1) + 8 * (s & 1);
-        asm volatile("" : "+v"(base));
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const uint32_t p = base ^ (uint32_t)(t << 5);
-            asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vt[t]) : "v"(p) : "memory");
-        }
+        slot_read_cols<T, D>(slot, c16, g16, vt);
     }
-    // Waits for every LDS read of this wave (and its scalar loads); values read
-    // by read_v are used only through this call's outputs.
-    __device__ __forceinline__ static void lds_wait(u32x2_t (&vt)[NT]) {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-        for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(vt[t]));
-    }
+    __device__ __forceinline__ static void lds_wait(u32x2_t (&vt)[NT]) { slot_lds_wait<D>(vt); }
     // Visible-key limits of one sub-page: keys [0, valid) exist; for new rows
     // (is_new) key tau is new row t0 + tau, visible to a query row by causality.
     __device__ __forceinline__ void limits(int valid, bool is_new, int t0, int (&lim)[NRT]) const {

@@ -1,0 +1,357 @@
+// Dense (training) GQA attention backward on the matrix cores (gfx950,
+// fp16/bf16): the gradient half of execute() on the docs.rs page
+// "onnxruntime-ep-mlx 0.31.1: src/ops/attention_vjp/dense.rs". With P the
+// recomputed softmax (masks and the top-left causal limit as in the forward),
+// Y = P V and dY the output gradient:
+//   dP = dY V^T,  delta = rowsum(Y * dY),  dS = P * (dP - delta),
+//   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dY,
+// dK and dV of KV head kh summed over the G query heads h = kh*G + g.
+//
+// Three launches: the forward kernel in its statistics form (per query row the
+// base-2 log-sum-exp of the scores and delta, Y kept in fp32 and never stored),
+// then the two kernels below, which recompute P from those statistics:
+//   dense_bwd_dq   - a workgroup per (sequence, KV head, block of positions),
+//                    the forward's rows layout; K and V stream through a ring;
+//   dense_bwd_dkdv - a workgroup per (sequence, KV head, 16*NW keys), each wave
+//                    holding 16 keys; the Q/dY rows of all G heads stream
+//                    through a ring, so the group sums stay in registers (one
+//                    writer per dK/dV row, no atomics).
+// Every streamed tile of 16 rows is loaded twice into a pair of slots with the
+// roles swapped (X rows | Y columns, then Y rows | X columns), so that both
+// operand forms each product needs come from the slot reads of the decode
+// kernels.
+#pragma once
+
+#include "dense_mfma.hpp"
+
+namespace pa {
+
+template <typename T>
+struct BwdArgs {
+    const T* dout;  // dY [B, HQ, SQ, D]
+    T* dq;          // [B, HQ, SQ, D]
+    T* dk;          // [B, HK, SK, D]
+    T* dv;
+    float scale;
+};
+
+// The 16-byte chunks 32*kk + 8*g16 of one row of D elements (an operand whose
+// lane holds that row): plain global loads.
+template <typename T, int D>
+__device__ __forceinline__ void frag_load(const T* row, int g16, u32x4_t (&op)[D / 32]) {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+        const uint4 v = load16(row + 32 * kk + 8 * g16);
+        op[kk] = u32x4_t{v.x, v.y, v.z, v.w};
+    }
+}
+
+// Value j of four wave-uniform values for the lanes of group j (mask[j] all
+// ones there, zero elsewhere): bitwise, exact for every value.
+__device__ __forceinline__ float pick4(float a, float b, float c, float d,
+                                       const uint32_t (&mask)[4]) {
+    return __uint_as_float((__float_as_uint(a) & mask[0]) | (__float_as_uint(b) & mask[1]) |
+                           (__float_as_uint(c) & mask[2]) | (__float_as_uint(d) & mask[3]));
+}
+
+// dQ: rows as in dense_mfma (R = G*P rows of one (b, kh) and P positions, NRT
+// 16-row tiles per wave); per 16-key tile, S^T = K Q^T and dP^T = V dY^T give
+// this lane's row c16 against keys 4*g16 + e, then dS and dQ += dS K.
+template <typename T, int D, int NW, int NRT, int kRing, int MASK, bool PAIR>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dense_bwd_dq(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
+                  const float* __restrict__ delta) {
+    using Lay = SlotLayout<T, D>;
+    using M = Mfma<T>;
+    constexpr int KS = D / 32, NT = D / 16;
+    constexpr int NWI = NW < KS ? NW : KS;  // waves that issue loads
+    constexpr int IPW = KS / NWI;           // instructions per half per issuing wave
+    constexpr int OPS = 4 * IPW;            // per key tile: two slots of two halves
+    constexpr int TB = 2 * Lay::kBytes;     // bytes of one key tile
+    static_assert(D % 32 == 0 && Lay::kOps == KS && KS % NWI == 0, "shape");
+    static_assert(kRing >= 3 && OPS * (kRing - 2) <= 63, "ring");
+
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const int lane = threadIdx.x & 63, c16 = lane & 15, g16 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const DenseGeometry& g = d.g;
+    const int nw = PAIR ? (g.nblk + 1) / 2 : g.nblk;  // workgroups per (b, kh)
+    const int wg = blockIdx.x % nw;
+    const int kh = (blockIdx.x / nw) % g.HK;
+    const int b = blockIdx.x / (nw * g.HK);
+    const int64_t kv0 = ((int64_t)b * g.HK + kh) * g.SK * D;
+    const T* const kb = d.k + kv0;
+    const T* const vb = d.v + kv0;
+    const int64_t head0 = (int64_t)b * g.HQ + (int64_t)kh * g.G;  // first query head of the group
+    const bool issues = wave < NWI;
+
+    for (int half = 0; half < (PAIR ? 2 : 1); ++half) {
+    const int blk = half == 0 ? wg : g.nblk - 1 - wg;
+    if (half == 1) {
+        if (blk == wg) break;  // odd block count: the middle block has no partner
+        asm volatile("" ::: "memory");
+        __syncthreads();      // every wave is done with the ring before it is refilled
+    }
+    const int i0 = blk * g.P;
+    const int R = g.G * g.P;
+    const int pend = min(g.P, g.SQ - i0);
+    int kend = g.SK;
+    if (g.causal) kend = min(kend, i0 + pend);
+    if (MASK && d.mw != 1 && d.mw < g.SK) kend = min(kend, d.mw);
+    const int n_sub = (kend + 15) / 16;
+    const bool has_rows = 16 * NRT * wave < R;
+
+    // this lane's row of tile rt (row c16), clamped to a real one
+    int srow_p[NRT], srow_h[NRT];
+    u32x4_t qop[NRT][KS], gop[NRT][KS];
+    float lse_r[NRT], dl_r[NRT];
+    f32x4_t acc[NRT][NT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+        const int r = min(16 * (wave * NRT + rt) + c16, R - 1);
+        srow_p[rt] = min(r % g.P, pend - 1);
+        srow_h[rt] = kh * g.G + r / g.P;
+        const int64_t row = ((int64_t)b * g.HQ + srow_h[rt]) * g.SQ + i0 + srow_p[rt];
+        frag_load<T, D>(d.q + row * D, g16, qop[rt]);
+        frag_load<T, D>(w.dout + row * D, g16, gop[rt]);
+        lse_r[rt] = lse[row];
+        dl_r[rt] = delta[row];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[rt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the row operands, before the ring's loads
+
+    // key tile s: slot A = K rows (| V columns, unused), slot B = V rows | K columns
+    auto fetch_tile = [&](int s) {
+        const int64_t o = (int64_t)16 * s * D;
+        const int rmax = min(15, g.SK - 1 - 16 * s);
+        char* sl = smem + (s % kRing) * TB;
+        fetch_rows<T, D, IPW>(kb + o, vb + o, rmax, sl, lane, wave, NWI);
+        fetch_rows<T, D, IPW>(vb + o, kb + o, rmax, sl + Lay::kBytes, lane, wave, NWI);
+    };
+    for (int s = 0; s < kRing - 1 && s < n_sub; ++s)
+        if (issues) fetch_tile(s);
+    for (int i = 0; i < n_sub; ++i) {
+        const int ahead = min(kRing - 2, n_sub - 1 - i);  // tiles fetched after i
+        if (issues) wait_ahead<OPS, kRing - 2>(ahead);
+        else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        // every wave's part of tile i is in; slot pair i - 1 is read out
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const int nxt = i + kRing - 1;
+        if (nxt < n_sub && issues) fetch_tile(nxt);
+        if (!has_rows) continue;
+        const char* sa = smem + (i % kRing) * TB;
+        const char* sb = sa + Lay::kBytes;
+        u32x4_t kop[KS], vop[KS];
+        u32x2_t kt[NT];
+        slot_read_rows<T, D>(sa, c16, g16, kop);
+        slot_read_rows<T, D>(sb, c16, g16, vop);
+        slot_read_cols<T, D>(sb, c16, g16, kt);
+        slot_lds_wait<D>(kt);
+        const int key0 = 16 * i;
+        const int valid = min(16, kend - key0);
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            f32x4_t st = f32x4_t{0.f, 0.f, 0.f, 0.f}, dpt = st;
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                st = M::qk(kop[kk], qop[rt][kk], st);
+                dpt = M::qk(vop[kk], gop[rt][kk], dpt);
+            }
+            const int lim = g.causal ? max(0, min(valid, i0 + srow_p[rt] - key0 + 1)) : valid;
+            float ds[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * g16 + e;
+                float x = st[e] * d.qscale;
+                if constexpr (MASK != 0)
+                    x += mask_bias2<MASK>(d, b, srow_h[rt], i0 + srow_p[rt],
+                                          min(key0 + j, d.mw - 1));
+                const float p = j < lim ? fast_exp2(x - lse_r[rt]) : 0.f;
+                ds[e] = p * (dpt[e] - dl_r[rt]);
+            }
+            u32x2_t phi, plo;
+            M::make_p(ds, phi, plo);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[rt][t] = M::pv(phi, plo, kt[t], acc[rt][t]);
+        }
+    }
+    if (has_rows) {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * (wave * NRT + rt) + 4 * g16 + i;
+                if (r >= R || r % g.P >= pend) continue;
+                T* dst = w.dq + ((head0 + r / g.P) * g.SQ + i0 + r % g.P) * D + c16;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) Elem<T>::store(dst + 16 * t, acc[rt][t][i] * w.scale);
+            }
+    }
+    }  // blocks of this workgroup
+}
+
+// dK, dV: wave `wave` of a workgroup holds keys kw0 .. kw0 + 15 of (b, kh) as
+// operands (K, V rows) and two accumulators; the Q/dY rows of the G query
+// heads stream through the ring in 16-row tiles (head-major). Per tile, S = Q
+// K^T and dP = dY V^T give query rows 4*g16 + e against this lane's key c16,
+// then dV += P^T dY and dK += dS^T Q. The tile's 16 log-sum-exps and deltas
+// are read with scalar loads (lse and delta are read-only here), which the
+// vector-memory counter of the ring does not see; the statistics arrays hold
+// 16 entries of padding past the last row.
+template <typename T, int D, int NW, int kRing, int MASK>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dense_bwd_dkdv(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
+                    const float* __restrict__ delta) {
+    using Lay = SlotLayout<T, D>;
+    using M = Mfma<T>;
+    constexpr int KS = D / 32, NT = D / 16;
+    constexpr int NWI = NW < KS ? NW : KS;
+    constexpr int IPW = KS / NWI;
+    constexpr int OPS = 4 * IPW;
+    constexpr int TB = 2 * Lay::kBytes;
+    static_assert(D % 32 == 0 && Lay::kOps == KS && KS % NWI == 0, "shape");
+    static_assert(kRing >= 3 && OPS * (kRing - 2) <= 63, "ring");
+
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const int lane = threadIdx.x & 63, c16 = lane & 15, g16 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const DenseGeometry& g = d.g;
+    const int nkb = (g.SK + 16 * NW - 1) / (16 * NW);  // key blocks per (b, kh)
+    const int kblk = blockIdx.x % nkb;
+    const int kh = (blockIdx.x / nkb) % g.HK;
+    const int b = blockIdx.x / (nkb * g.HK);
+    const int kw0 = kblk * 16 * NW + 16 * wave;  // this wave's first key
+    const int64_t kv0 = ((int64_t)b * g.HK + kh) * g.SK;
+    const int64_t head0 = (int64_t)b * g.HQ + (int64_t)kh * g.G;
+    const bool issues = wave < NWI;
+    const bool has_keys = kw0 < g.SK;
+    // all-ones for the lane's 16-lane group g16, zero for the others (opaque to
+    // the optimizer, which would otherwise turn the pick into an indexed
+    // private array)
+    uint32_t gmask[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        gmask[j] = g16 == j ? 0xffffffffu : 0u;
+        asm volatile("" : "+v"(gmask[j]));
+    }
+
+    u32x4_t kfr[KS], vfr[KS];
+    {
+        const int64_t kr = kv0 + min(kw0 + c16, g.SK - 1);
+        frag_load<T, D>(d.k + kr * D, g16, kfr);
+        frag_load<T, D>(d.v + kr * D, g16, vfr);
+    }
+    f32x4_t dk[NT], dv[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) dk[t] = dv[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+    // query tiles: head gg of the group, positions 16*it .. +15; under the
+    // causal limit positions before the block's first key see none of its keys
+    const int ntile = (g.SQ + 15) / 16;
+    const int it0 = g.causal ? min(ntile, kblk * NW) : 0;
+    const int nit = ntile - it0;
+    const int n_t = g.G * nit;
+    auto tile_row0 = [&](int t) -> int64_t {  // row index of the tile's first row
+        return (head0 + t / nit) * g.SQ + 16 * (it0 + t % nit);
+    };
+    auto fetch_tile = [&](int t) {
+        const int64_t r0 = tile_row0(t);
+        const int rmax = min(15, g.SQ - 1 - 16 * (it0 + t % nit));
+        char* sl = smem + (t % kRing) * TB;
+        const T* qr = d.q + r0 * D;
+        const T* gr = w.dout + r0 * D;
+        fetch_rows<T, D, IPW>(qr, gr, rmax, sl, lane, wave, NWI);                  // Q rows | dY cols
+        fetch_rows<T, D, IPW>(gr, qr, rmax, sl + Lay::kBytes, lane, wave, NWI);  // dY rows | Q cols
+    };
+    for (int s = 0; s < kRing - 1 && s < n_t; ++s)
+        if (issues) fetch_tile(s);
+    const float* const lse0 = lse + head0 * g.SQ;  // statistics of the group's first row
+    const float* const dl0 = delta + head0 * g.SQ;
+    for (int t = 0; t < n_t; ++t) {
+        const int gg = t / nit;                   // head of the group
+        const int q0 = 16 * (it0 + t - gg * nit);  // first query position of the tile
+        const int hq = kh * g.G + gg;
+        const int sr = __builtin_amdgcn_readfirstlane(gg * g.SQ + q0);  // < 2^31 (checked)
+        const float* ls = lse0 + sr;
+        const float* dl = dl0 + sr;
+        float lv[16], dv16[16];  // uniform loads of all 16 rows, then a per-lane pick
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            lv[j] = ls[j];
+            dv16[j] = dl[j];
+        }
+        float lr[4], dr[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {  // row 4*g16 + e of the tile
+            lr[e] = pick4(lv[e], lv[4 + e], lv[8 + e], lv[12 + e], gmask);
+            dr[e] = pick4(dv16[e], dv16[4 + e], dv16[8 + e], dv16[12 + e], gmask);
+        }
+        const int ahead = min(kRing - 2, n_t - 1 - t);
+        if (issues) wait_ahead<OPS, kRing - 2>(ahead);
+        else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const int nxt = t + kRing - 1;
+        if (nxt < n_t && issues) fetch_tile(nxt);
+        if (!has_keys || (g.causal && kw0 > q0 + 15)) continue;  // no visible pair in this tile
+        const char* sa = smem + (t % kRing) * TB;
+        const char* sb = sa + Lay::kBytes;
+        u32x4_t qa[KS], ga[KS];
+        u32x2_t gt[NT], qt[NT];
+        slot_read_rows<T, D>(sa, c16, g16, qa);
+        slot_read_rows<T, D>(sb, c16, g16, ga);
+        slot_read_cols<T, D>(sa, c16, g16, gt);
+        slot_read_cols<T, D>(sb, c16, g16, qt);
+        slot_lds_wait<D>(gt);
+        slot_lds_wait<D>(qt);
+        f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f}, dp = s;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            s = M::qk(qa[kk], kfr[kk], s);
+            dp = M::qk(ga[kk], vfr[kk], dp);
+        }
+        const int kj = kw0 + c16;
+        float p[4], ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int qi = q0 + 4 * g16 + e;
+            bool vis = kj < g.SK && qi < g.SQ && (!g.causal || kj <= qi);
+            float x = s[e] * d.qscale;
+            if constexpr (MASK != 0) {
+                vis = vis && (d.mw == 1 || kj < d.mw);
+                x += mask_bias2<MASK>(d, b, hq, min(qi, g.SQ - 1), min(kj, d.mw - 1));
+            }
+            p[e] = vis ? fast_exp2(x - lr[e]) : 0.f;
+            ds[e] = p[e] * (dp[e] - dr[e]);
+        }
+        u32x2_t phi, plo, dhi, dlo;
+        M::make_p(p, phi, plo);
+        M::make_p(ds, dhi, dlo);
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            dv[u] = M::pv(phi, plo, gt[u], dv[u]);
+            dk[u] = M::pv(dhi, dlo, qt[u], dk[u]);
+        }
+    }
+    if (has_keys) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = kw0 + 4 * g16 + i;
+            if (key >= g.SK) continue;
+            T* kd = w.dk + (kv0 + key) * D + c16;
+            T* vd = w.dv + (kv0 + key) * D + c16;
+#pragma unroll
+            for (int u = 0; u < NT; ++u) {
+                Elem<T>::store(kd + 16 * u, dk[u][i] * w.scale);
+                Elem<T>::store(vd + 16 * u, dv[u][i]);
+            }
+        }
+    }
+}
+
+}  // namespace pa

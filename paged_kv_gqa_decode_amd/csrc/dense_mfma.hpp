@@ -38,12 +38,74 @@ struct DenseArgs {
     int mb, mh, mq, mw;
     DenseGeometry g;
     float qscale;      // scale * log2(e)
+    // statistics pass of the backward (STATS): out is not written; per query
+    // row (index (b*HQ + h)*SQ + i) lse = log2 of sum_j 2^(s_j * log2 e) (+inf
+    // for a row with no visible key) and delta = sum_d Y_d * dout_d, Y in fp32
+    const T* dout;
+    float* lse;
+    float* delta;
 };
+
+// Mask bias of score (b, h, qi, kj) in base-2 units (0 or -inf for a boolean
+// mask, value * log2(e) for an additive one); indices already inside the
+// mask's broadcast shape (kj < mw unless mw == 1).
+template <int MASK, typename T>
+__device__ __forceinline__ float mask_bias2(const DenseArgs<T>& d, int b, int h, int qi, int kj) {
+    const int64_t mi = (((int64_t)(d.mb == 1 ? 0 : b) * d.mh + (d.mh == 1 ? 0 : h)) * d.mq +
+                        (d.mq == 1 ? 0 : qi)) * d.mw + (d.mw == 1 ? 0 : kj);
+    if constexpr (MASK == 1)
+        return static_cast<const uint8_t*>(d.mask)[mi] ? 0.f : -__builtin_inff();
+    else
+        return static_cast<const float*>(d.mask)[mi] * 1.4426950408889634f;
+}
+
+// Backward statistics of the finished rows of a RowTiles (rows 16*(rt0 + rt)
+// + 4*g16 + i held in acc[rt][*][i]): lse = m + log2(l) per row (+inf when l =
+// 0, so that every recomputed probability of the row is 0) and delta = sum_d
+// (acc / l)_d * dout_d, reduced over the 16 lanes of a row group. off(r) is the
+// element offset of row r from row index `first` * D (-1: no such row).
+template <int D, typename Rows, typename T, typename F>
+__device__ __forceinline__ void dense_row_stats(const Rows& rows, const DenseArgs<T>& d,
+                                                int64_t first, F&& off) {
+    constexpr int NT = D / 16;
+    const int c16 = rows.c16, g16 = rows.g16;
+#pragma unroll
+    for (int rt = 0; rt < (int)(sizeof(rows.m) / sizeof(rows.m[0])); ++rt) {
+        float lrow = rows.lsum[rt];
+        lrow += __shfl_xor(lrow, 16);
+        lrow += __shfl_xor(lrow, 32);  // l of row 16*(rt0+rt) + c16
+        const int rc = 16 * (rows.rt0 + rt) + c16;
+        const int64_t oc = off(rc);
+        if (g16 == 0 && oc >= 0)
+            d.lse[first + oc / D] = lrow > 0.f ? rows.m[rt] + __builtin_log2f(lrow)
+                                               : __builtin_inff();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * (rows.rt0 + rt) + 4 * g16 + i;
+            const float l_r = __shfl(lrow, 4 * g16 + i);
+            const int64_t o = off(r);  // the same in the 16 lanes of the group
+            float part = 0.f;
+            if (o >= 0) {
+                const T* gy = d.dout + first * D + o + c16;
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    part = fmaf(rows.acc[rt][t][i], Elem<T>::load(gy + 16 * t), part);
+            }
+            part += __shfl_xor(part, 1);
+            part += __shfl_xor(part, 2);
+            part += __shfl_xor(part, 4);
+            part += __shfl_xor(part, 8);
+            if (o >= 0 && c16 == 0) d.delta[first + o / D] = l_r > 0.f ? part / l_r : 0.f;
+        }
+    }
+}
 
 // MASK: 0 none, 1 boolean, 2 additive. PAIR: workgroup w takes blocks w and
 // nblk - 1 - w of its (sequence, KV head), one after the other, so that under
 // the causal limit every workgroup has the same number of keys to attend.
-template <typename T, int D, int NW, int NRT, int kRing, int MASK, bool PAIR>
+// STATS: write the backward's row statistics (DenseArgs::lse, ::delta) instead
+// of the output.
+template <typename T, int D, int NW, int NRT, int kRing, int MASK, bool PAIR, bool STATS = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dense_mfma(DenseArgs<T> d) {
     using Lay = SlotLayout<T, D>;
@@ -53,7 +115,6 @@ void dense_mfma(DenseArgs<T> d) {
     constexpr int IPW = KS / NWI;           // instructions per half per issuing wave
     static_assert(D % 32 == 0 && Lay::kOps == KS && KS % NWI == 0, "shape");
     static_assert(kRing >= 3 && 2 * IPW * (kRing - 2) <= 63, "ring");
-    constexpr float kLog2e = 1.4426950408889634f;
 
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const int lane = threadIdx.x & 63, c16 = lane & 15, g16 = lane >> 4;
@@ -147,20 +208,11 @@ void dense_mfma(DenseArgs<T> d) {
         if constexpr (MASK != 0) {
             float bias[NRT][4];
 #pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) {
-                const int64_t mrow = (((int64_t)(d.mb == 1 ? 0 : b) * d.mh +
-                                       (d.mh == 1 ? 0 : srow_h[rt])) * d.mq +
-                                      (d.mq == 1 ? 0 : i0 + srow_p[rt])) * d.mw;
+            for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = d.mw == 1 ? 0 : min(key0 + 4 * g16 + e, d.mw - 1);
-                    if constexpr (MASK == 1)
-                        bias[rt][e] = static_cast<const uint8_t*>(d.mask)[mrow + j]
-                                          ? 0.f : -__builtin_inff();
-                    else
-                        bias[rt][e] = static_cast<const float*>(d.mask)[mrow + j] * kLog2e;
-                }
-            }
+                for (int e = 0; e < 4; ++e)
+                    bias[rt][e] = mask_bias2<MASK>(d, b, srow_h[rt], i0 + srow_p[rt],
+                                                   min(key0 + 4 * g16 + e, d.mw - 1));
             rows.template scores<true>(kop, lim, false, bias);
         } else {
             // every key visible to every row: whole sub-page, and causally
@@ -172,11 +224,16 @@ void dense_mfma(DenseArgs<T> d) {
     }
     if (q_pending) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no keys: Q was never waited for
     rows.flush();
-    if (has_rows)
-        rows.emit_rows(d.out + head0 * g.SQ * D, [&](int r) -> int64_t {
-            if (r >= R || r % g.P >= pend) return -1;
-            return ((int64_t)(r / g.P) * g.SQ + i0 + r % g.P) * D;
-        });
+    auto row_off = [&](int r) -> int64_t {  // element offset of row r from head0's first row
+        if (r >= R || r % g.P >= pend) return -1;
+        return ((int64_t)(r / g.P) * g.SQ + i0 + r % g.P) * D;
+    };
+    if (has_rows) {
+        if constexpr (STATS)
+            dense_row_stats<D>(rows, d, head0 * g.SQ, row_off);
+        else
+            rows.emit_rows(d.out + head0 * g.SQ * D, row_off);
+    }
     }  // blocks of this workgroup
 }
 

@@ -40,6 +40,7 @@ template <> struct Elem<float> {
         f[3] = __uint_as_float(r.w);
     }
     __device__ static __forceinline__ void store(float* p, float v) { *p = v; }
+    __device__ static __forceinline__ float load(const float* p) { return *p; }
 };
 
 template <> struct Elem<_Float16> {
@@ -55,6 +56,7 @@ template <> struct Elem<_Float16> {
         unpack_word(r.w, f + 6);
     }
     __device__ static __forceinline__ void store(_Float16* p, float v) { *p = (_Float16)v; }
+    __device__ static __forceinline__ float load(const _Float16* p) { return (float)*p; }
 };
 
 template <> struct Elem<bf16_t> {
@@ -71,6 +73,9 @@ template <> struct Elem<bf16_t> {
     }
     __device__ static __forceinline__ void store(bf16_t* p, float v) {
         p->bits = f32_to_bf16_rne(v);
+    }
+    __device__ static __forceinline__ float load(const bf16_t* p) {
+        return __uint_as_float((uint32_t)p->bits << 16);
     }
 };
 

@@ -18,7 +18,7 @@
 #include "combine.hpp"
 #include "decode_mfma.hpp"
 #include "decode_valu.hpp"
-#include "dense_mfma.hpp"
+#include "dense_bwd.hpp"
 
 namespace {
 
@@ -630,14 +630,15 @@ void launch_dense_k(const pa::DenseArgs<T>& a, unsigned grid, hipStream_t s) {
                            dim3(64 * kDenseWaves), lds, s, a);
 }
 
+// Kernel arguments of a dense problem (forward geometry; out, dout and the
+// statistics pointers left empty).
 template <typename T>
-int run_dense(const pa_dense_problem* p, const void* q, const void* k, const void* v,
-              const void* mask, float scale, void* out, hipStream_t s) {
-    pa::DenseArgs<T> a;
+pa::DenseArgs<T> dense_args(const pa_dense_problem* p, const void* q, const void* k,
+                            const void* v, const void* mask, float scale) {
+    pa::DenseArgs<T> a{};
     a.q = static_cast<const T*>(q);
     a.k = static_cast<const T*>(k);
     a.v = static_cast<const T*>(v);
-    a.out = static_cast<T*>(out);
     a.mask = mask;
     a.mb = p->mask_dims[0];
     a.mh = p->mask_dims[1];
@@ -653,8 +654,21 @@ int run_dense(const pa_dense_problem* p, const void* q, const void* k, const voi
     a.g.nblk = (int)ceil_div(p->q_len, a.g.P);
     a.g.causal = p->causal;
     a.qscale = (float)((double)scale * 1.4426950408889634);
-    const int64_t per_kv = p->causal ? (a.g.nblk + 1) / 2 : a.g.nblk;  // paired blocks
-    const int64_t grid = (int64_t)p->batch * p->num_kv_heads * per_kv;
+    return a;
+}
+
+// Workgroups of the forward's row blocks (paired under the causal limit).
+int64_t dense_row_grid(const pa_dense_problem* p, const pa::DenseGeometry& g) {
+    const int64_t per_kv = p->causal ? (g.nblk + 1) / 2 : g.nblk;
+    return (int64_t)p->batch * p->num_kv_heads * per_kv;
+}
+
+template <typename T>
+int run_dense(const pa_dense_problem* p, const void* q, const void* k, const void* v,
+              const void* mask, float scale, void* out, hipStream_t s) {
+    pa::DenseArgs<T> a = dense_args<T>(p, q, k, v, mask, scale);
+    a.out = static_cast<T*>(out);
+    const int64_t grid = dense_row_grid(p, a.g);
     if (grid >= (1LL << 31))
         return fail(PA_ERR_UNSUPPORTED, "too many workgroups (%lld) for one call",
                     (long long)grid);
@@ -671,6 +685,83 @@ int run_dense(const pa_dense_problem* p, const void* q, const void* k, const voi
     if (hipError_t e = hipGetLastError(); e != hipSuccess)
         return fail(PA_ERR_LAUNCH, "dense attention launch failed: %s; verify the device state",
                     hipGetErrorString(e));
+    return succeed();
+}
+
+// ---------------------------------------------------------------------------
+// Dense GQA attention backward
+// ---------------------------------------------------------------------------
+// dK/dV: 16 keys per wave, four waves (64 keys) per workgroup.
+constexpr int kBwdKeyWaves = 4;
+
+// Bytes of one statistics array (lse or delta): a float per query row plus 16
+// floats of padding (the dK/dV kernel reads whole 16-row tiles), rounded up to
+// 256 bytes.
+size_t dense_stats_bytes(const pa_dense_problem* p) {
+    const int64_t rows = (int64_t)p->batch * p->num_heads * p->q_len;
+    return (size_t)(((rows + 16) * 4 + 255) / 256 * 256);
+}
+
+template <typename T, int D, int MASK>
+void launch_dense_bwd_k(const pa::DenseArgs<T>& a, const pa::BwdArgs<T>& w, unsigned grid_rows,
+                        unsigned grid_keys, hipStream_t s) {
+    constexpr int kRing = D == 128 ? 4 : 8;
+    const size_t lds_fwd = (size_t)kRing * pa::SlotLayout<T, D>::kBytes;
+    const size_t lds_bwd = 2 * lds_fwd;  // a pair of slots per tile: 64 KiB
+    const float* lse = a.lse;
+    const float* dl = a.delta;
+    if (grid_rows) {
+        if (a.g.causal) {
+            hipLaunchKernelGGL((pa::dense_mfma<T, D, kDenseWaves, 1, kRing, MASK, true, true>),
+                               dim3(grid_rows), dim3(64 * kDenseWaves), lds_fwd, s, a);
+            hipLaunchKernelGGL((pa::dense_bwd_dq<T, D, kDenseWaves, 1, kRing, MASK, true>),
+                               dim3(grid_rows), dim3(64 * kDenseWaves), lds_bwd, s, a, w, lse, dl);
+        } else {
+            hipLaunchKernelGGL((pa::dense_mfma<T, D, kDenseWaves, 2, kRing, MASK, false, true>),
+                               dim3(grid_rows), dim3(64 * kDenseWaves), lds_fwd, s, a);
+            hipLaunchKernelGGL((pa::dense_bwd_dq<T, D, kDenseWaves, 2, kRing, MASK, false>),
+                               dim3(grid_rows), dim3(64 * kDenseWaves), lds_bwd, s, a, w, lse, dl);
+        }
+    }
+    if (grid_keys)
+        hipLaunchKernelGGL((pa::dense_bwd_dkdv<T, D, kBwdKeyWaves, kRing, MASK>), dim3(grid_keys),
+                           dim3(64 * kBwdKeyWaves), lds_bwd, s, a, w, lse, dl);
+}
+
+template <typename T>
+int run_dense_bwd(const pa_dense_problem* p, const void* q, const void* k, const void* v,
+                  const void* mask, const void* dout, float scale, void* dq, void* dk, void* dv,
+                  void* workspace, hipStream_t s) {
+    pa::DenseArgs<T> a = dense_args<T>(p, q, k, v, mask, scale);
+    a.dout = static_cast<const T*>(dout);
+    a.lse = static_cast<float*>(workspace);
+    a.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + dense_stats_bytes(p));
+    pa::BwdArgs<T> w;
+    w.dout = a.dout;
+    w.dq = static_cast<T*>(dq);
+    w.dk = static_cast<T*>(dk);
+    w.dv = static_cast<T*>(dv);
+    w.scale = scale;
+    const int64_t grid_rows = p->q_len > 0 ? dense_row_grid(p, a.g) : 0;
+    const int64_t grid_keys = (int64_t)p->batch * p->num_kv_heads *
+                              ceil_div(p->kv_len, 16 * kBwdKeyWaves);
+    if (grid_rows >= (1LL << 31) || grid_keys >= (1LL << 31))
+        return fail(PA_ERR_UNSUPPORTED, "too many workgroups (%lld, %lld) for one call",
+                    (long long)grid_rows, (long long)grid_keys);
+    const unsigned gr = (unsigned)grid_rows, gk = (unsigned)grid_keys;
+    const int mk = p->mask_kind;
+    if (p->head_dim == 64) {
+        if (mk == PA_MASK_BOOL) launch_dense_bwd_k<T, 64, 1>(a, w, gr, gk, s);
+        else if (mk == PA_MASK_ADD) launch_dense_bwd_k<T, 64, 2>(a, w, gr, gk, s);
+        else launch_dense_bwd_k<T, 64, 0>(a, w, gr, gk, s);
+    } else {
+        if (mk == PA_MASK_BOOL) launch_dense_bwd_k<T, 128, 1>(a, w, gr, gk, s);
+        else if (mk == PA_MASK_ADD) launch_dense_bwd_k<T, 128, 2>(a, w, gr, gk, s);
+        else launch_dense_bwd_k<T, 128, 0>(a, w, gr, gk, s);
+    }
+    if (hipError_t e = hipGetLastError(); e != hipSuccess)
+        return fail(PA_ERR_LAUNCH, "dense attention backward launch failed: %s; verify the "
+                    "device state", hipGetErrorString(e));
     return succeed();
 }
 
@@ -699,6 +790,43 @@ int pa_dense_attention(const pa_dense_problem* problem, const void* q, const voi
     return run_dense<pa::bf16_t>(p, q, k, v, mask, scale, out, s);
 }
 
+
+int pa_dense_backward_workspace_size(const pa_dense_problem* problem, size_t* bytes) {
+    if (!bytes) return fail(PA_ERR_INVALID_ARG, "bytes is NULL");
+    if (int rc = validate_dense(problem)) return rc;
+    *bytes = 2 * dense_stats_bytes(problem);
+    return succeed();
+}
+
+int pa_dense_attention_backward(const pa_dense_problem* problem, const void* q, const void* k,
+                                const void* v, const void* mask, const void* dout, float scale,
+                                void* dq, void* dk, void* dv, void* workspace,
+                                size_t workspace_bytes, pa_stream_t stream) {
+    if (int rc = validate_dense(problem)) return rc;
+    const pa_dense_problem* p = problem;
+    if (p->batch == 0 || (p->q_len == 0 && p->kv_len == 0)) return succeed();
+    const bool rows = p->q_len > 0, keys = p->kv_len > 0;
+    if ((rows && (!q || !dout || !dq)) || (keys && (!k || !v || !dk || !dv)) ||
+        (rows && keys && (!q || !k)))
+        return fail(PA_ERR_INVALID_ARG, "a tensor pointer is NULL (q %p, k %p, v %p, dout %p, "
+                    "dq %p, dk %p, dv %p)", q, k, v, dout, dq, dk, dv);
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(dout, 16) ||
+        misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16))
+        return fail(PA_ERR_INVALID_ARG, "q, k, v, dout, dq, dk and dv must be 16-byte aligned");
+    if (p->mask_kind != PA_MASK_NONE &&
+        (!mask || (p->mask_kind == PA_MASK_ADD && misaligned(mask, 4))))
+        return fail(PA_ERR_INVALID_ARG, "mask is NULL or (additive) not 4-byte aligned");
+    const size_t need = 2 * dense_stats_bytes(p);
+    if (!workspace || workspace_bytes < need || misaligned(workspace, 256))
+        return fail(PA_ERR_WORKSPACE, "workspace %p of %zu bytes: need %zu bytes, 256-byte "
+                    "aligned (pa_dense_backward_workspace_size)", workspace, workspace_bytes, need);
+    int cus = 0;
+    if (int rc = current_device_cus(&cus)) return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (p->dtype == PA_F16)
+        return run_dense_bwd<_Float16>(p, q, k, v, mask, dout, scale, dq, dk, dv, workspace, s);
+    return run_dense_bwd<pa::bf16_t>(p, q, k, v, mask, dout, scale, dq, dk, dv, workspace, s);
+}
 
 int pa_plan_ex(const pa_problem* problem, int32_t num_cus, int32_t* partitions,
                int32_t* chunk_tokens, int32_t* kernel) {
@@ -792,6 +920,6 @@ int paged_attn_combine(const pa_problem* problem, const int32_t* context_lens,
 
 const char* paged_attn_last_error(void) { return t_error.c_str(); }
 
-int paged_attn_version(void) { return 103; }
+int paged_attn_version(void) { return 104; }
 
 }  // extern "C"

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(names) == set(pa.EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert pa.paged_attn_version() == 103
+    assert pa.paged_attn_version() == 104
 
 
 def spec_problem(spec: W.Spec, max_ctx: int, **kw) -> pa.PaProblem:
@@ -199,3 +199,50 @@ def test_dense_rejects(lib, kw, code):
 def test_dense_empty_problem_is_a_no_op(lib):
     assert pa.pa_dense_attention(_dense_problem(batch=0), None, None, None, None, 0.1, None) == 0
     assert pa.pa_dense_attention(_dense_problem(q_len=0), None, None, None, None, 0.1, None) == 0
+
+
+# --------------------------------------------------------------------------
+# Dense backward entry points: host-side checks
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("kw,code", DENSE_BAD, ids=lambda x: str(x))
+def test_dense_backward_rejects(lib, kw, code):
+    prob = _dense_problem(**kw)
+    rc, _ = pa.pa_dense_backward_workspace_size(prob, raise_on_error=False)
+    assert rc == code, pa.paged_attn_last_error()
+    rc = pa.pa_dense_attention_backward(prob, None, None, None, None, None, 0.1, None, None,
+                                        None, None, 0, raise_on_error=False)
+    assert rc == code, pa.paged_attn_last_error()
+
+
+def test_dense_backward_workspace_size(lib):
+    # two fp32 arrays (log-sum-exp, delta) of one value per query row plus 16
+    # of padding, each rounded up to 256 bytes
+    for B, HQ, SQ in ((1, 8, 32), (3, 12, 7), (2, 32, 2048)):
+        _, n = pa.pa_dense_backward_workspace_size(
+            _dense_problem(batch=B, num_heads=HQ, num_kv_heads=HQ // 4, q_len=SQ))
+        assert n == 2 * (((B * HQ * SQ + 16) * 4 + 255) // 256 * 256)
+
+
+def test_dense_backward_checks_pointers_and_workspace(lib):
+    prob = _dense_problem()
+    _, need = pa.pa_dense_backward_workspace_size(prob)
+    fake = 1 << 20  # aligned, never dereferenced: every check below fails before any HIP call
+    args = [fake] * 5
+    rc = pa.pa_dense_attention_backward(prob, *args, 0.1, fake, fake, fake, fake, need - 4,
+                                        raise_on_error=False)
+    assert rc == pa.PA_ERR_WORKSPACE, pa.paged_attn_last_error()
+    rc = pa.pa_dense_attention_backward(prob, *args, 0.1, fake, fake, fake, fake + 16, need,
+                                        raise_on_error=False)
+    assert rc == pa.PA_ERR_WORKSPACE  # not 256-byte aligned
+    rc = pa.pa_dense_attention_backward(prob, fake, fake, fake, None, None, 0.1, fake, fake,
+                                        fake, fake, need, raise_on_error=False)
+    assert rc == pa.PA_ERR_INVALID_ARG  # no dout
+    rc = pa.pa_dense_attention_backward(prob, *args, 0.1, fake + 2, fake, fake, fake, need,
+                                        raise_on_error=False)
+    assert rc == pa.PA_ERR_INVALID_ARG  # misaligned dq
+
+
+def test_dense_backward_empty_problem_is_a_no_op(lib):
+    for kw in (dict(batch=0), dict(q_len=0, kv_len=0)):
+        assert pa.pa_dense_attention_backward(_dense_problem(**kw), None, None, None, None, None,
+                                              0.1, None, None, None, None, 0) == 0

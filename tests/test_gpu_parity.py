@@ -314,6 +314,83 @@ def test_dense_long_causal_rows_sampled():
 
 
 # ---------------------------------------------------------------------------
+# Dense GQA attention backward (pa_dense_attention_backward) against the oracle
+# ---------------------------------------------------------------------------
+DENSE_BWD_GPU = DENSE_GPU + [
+    (1, 8, 2, 24, 80, 128, "bf16", None, None, True),              # SK > SQ: keys no query sees
+    (1, 8, 2, 130, 150, 128, "f16", None, None, False),            # several key blocks and tiles
+    (2, 8, 1, 70, 90, 64, "bf16", "bool", (2, 8, 70, 90), True),   # G = 8, D = 64, masked
+]
+
+
+def _bwd_inputs(case, seed=61):
+    q, k, v, mask, causal, dtype = _dense_case_inputs(case, seed)
+    g = torch.Generator().manual_seed(seed + 7)
+    dout = torch.randn(q.shape, generator=g).to(q.dtype)
+    return q, k, v, dout, mask, causal, dtype
+
+
+def check_grad(name, got, expect, dtype):
+    got = got.detach().cpu().double().numpy()
+    assert np.isfinite(got).all(), name
+    err = np.abs(got - expect)
+    bar = allowed(expect, dtype)
+    worst = np.unravel_index(np.argmax(err - bar), err.shape) if err.size else None
+    print(f"[gpu]   {name}: max err {err.max() if err.size else 0:.3e}, max |ref| "
+          f"{np.abs(expect).max() if err.size else 0:.3e}", flush=True)
+    assert (err <= bar).all(), f"{name}: error {err[worst]} > {bar[worst]} at {worst}"
+
+
+@pytest.mark.parametrize("case", DENSE_BWD_GPU,
+                         ids=lambda c: "-".join(map(str, c[:8])) + ("-c" if c[9] else ""))
+def test_dense_backward_matches_the_oracle(case):
+    q, k, v, dout, mask, causal, dtype = _bwd_inputs(case)
+    edq, edk, edv = oracle.dense_attention_backward(q, k, v, dout, 0.09, mask=mask, causal=causal)
+    print(f"[gpu] dense backward {case[:8]} causal={causal}", flush=True)
+    dq, dk, dv = pa.dense_attention_backward(
+        q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV), 0.09,
+        mask=mask.to(DEV) if mask is not None else None, causal=causal)
+    torch.cuda.synchronize()
+    check_grad("dq", dq, edq, dtype)
+    check_grad("dk", dk, edk, dtype)
+    check_grad("dv", dv, edv, dtype)
+
+
+def test_dense_backward_prefill_sampled():
+    # 1 x 32 query heads over 8 KV heads, 2048 positions, causal, fp16 (the
+    # prefill the bench times): dq of three blocks of rows against the oracle on
+    # those rows (their keys, the causal limit as a mask); dk and dv through the
+    # sums that hold at any size (keys: 0; values: the dout rows of the group)
+    B, HQ, HK, S, D = 1, 32, 8, 2048, 128
+    g = torch.Generator().manual_seed(73)
+    q = torch.randn(B, HQ, S, D, generator=g).half()
+    k = torch.randn(B, HK, S, D, generator=g).half()
+    v = torch.randn(B, HK, S, D, generator=g).half()
+    dout = torch.randn(B, HQ, S, D, generator=g).half()
+    scale = 0.088
+    print("[gpu] dense backward prefill", flush=True)
+    dq, dk, dv = pa.dense_attention_backward(q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV),
+                                             scale, causal=True)
+    dq, dk, dv = dq.cpu(), dk.cpu().double(), dv.cpu().double()
+    for a, n in ((0, 24), (1000, 24), (S - 24, 24)):
+        vis = (torch.arange(a + n)[None, :] <= torch.arange(a, a + n)[:, None])[None, None]
+        edq, _, _ = oracle.dense_attention_backward(
+            q[:, :, a:a + n], k[:, :, :a + n], v[:, :, :a + n], dout[:, :, a:a + n], scale,
+            mask=vis, causal=False)
+        check_grad(f"dq rows {a}..{a + n - 1}", dq[:, :, a:a + n], edq, "f16")
+    G = HQ // HK
+    ksum = dk.sum(dim=2).numpy()
+    kbar = 2.0 ** -9 * dk.abs().sum(dim=2).numpy() + 1e-2
+    assert (np.abs(ksum) <= kbar).all(), np.abs(ksum).max()
+    want = dout.double().reshape(B, HK, G, S, D).sum(dim=(2, 3)).numpy()
+    vsum = dv.sum(dim=2).numpy()
+    vbar = 2.0 ** -9 * dv.abs().sum(dim=2).numpy() + 1e-2
+    print(f"[gpu]   sum dk max {np.abs(ksum).max():.3e}, sum dv err "
+          f"{np.abs(vsum - want).max():.3e}", flush=True)
+    assert (np.abs(vsum - want) <= vbar).all(), np.abs(vsum - want).max()
+
+
+# ---------------------------------------------------------------------------
 # Score staircases: the running maximum moves mid-stream, at odd and even
 # sub-pages, and in some row tiles of a wave but not the others (fp16 sums two
 # sub-pages' PV products at once, so a move can find one of them waiting)
