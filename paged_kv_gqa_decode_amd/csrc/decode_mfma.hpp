@@ -202,7 +202,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 // instructions i = i0, i0 + istep, ... (COUNT of each half); 16 bytes per lane
 // per instruction. All offsets are in voffset, so the descriptors cover exactly
 // rmax + 1 rows.
-template <typename T, int D, int COUNT>
+// VV: the first half also in the second half's layout (rows read with
+// slot_read_rows_v, columns with slot_read_cols_at).
+template <typename T, int D, int COUNT, bool VV = false>
 __device__ __forceinline__ void fetch_rows(const T* k, const T* v, int rmax, char* slot, int lane,
                                            int i0 = 0, int istep = 1) {
     using Lay = SlotLayout<T, D>;
@@ -218,7 +220,8 @@ __device__ __forceinline__ void fetch_rows(const T* k, const T* v, int rmax, cha
         const int i = i0 + istep * t;
         const int row = Lay::kKeysPerOp * i + ln / Lay::kChunks;
         const int rc = min(row, rmax);
-        const int koff = rc * kStride + (((ln % Lay::kChunks) ^ Lay::swz(row)) << 4);
+        const int koff = rc * kStride +
+                         (((ln % Lay::kChunks) ^ (VV ? Lay::vswz(row) : Lay::swz(row))) << 4);
         const int voff = rc * kStride + (((ln % Lay::kChunks) ^ Lay::vswz(row)) << 4);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(k_lds + i * 1024), 16, koff, 0,
                                                  0, 0);
@@ -486,12 +489,12 @@ __device__ __forceinline__ void slot_read_rows(const char* slot, int c16, int g1
 // flight and would wait for all of them first. The results are only valid
 // after slot_lds_wait(), which ties them to an LDS-counter wait.
 template <typename T, int D>
-__device__ __forceinline__ void slot_read_cols(const char* slot, int c16, int g16,
-                                               u32x2_t (&vt)[D / 16]) {
+__device__ __forceinline__ void slot_read_cols_at(const char* half, int c16, int g16,
+                                                  u32x2_t (&vt)[D / 16]) {
     using Lay = SlotLayout<T, D>;
     const int s = c16;
     const int row = 4 * g16 + s / 4;
-    uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(slot) + Lay::kKBytes +
+    uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(half) +
                     Lay::v_addr(row, (s & 3) >> 1) + 8 * (s & 1);
     asm volatile("" : "+v"(base));
 #pragma unroll
@@ -499,6 +502,25 @@ __device__ __forceinline__ void slot_read_cols(const char* slot, int c16, int g1
         const uint32_t p = base ^ (uint32_t)(t << 5);
         asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vt[t]) : "v"(p) : "memory");
     }
+}
+template <typename T, int D>
+__device__ __forceinline__ void slot_read_cols(const char* slot, int c16, int g16,
+                                               u32x2_t (&vt)[D / 16]) {
+    slot_read_cols_at<T, D>(slot + SlotLayout<T, D>::kKBytes, c16, g16, vt);
+}
+// Rows, as slot_read_rows, of a half in the second half's layout (`half` is
+// its first byte): chunk 4*kk + g16 of row c16 sits at c16*R + (((g16 ^
+// vswz(c16)) ^ 4*kk) << 4), again one base XOR (kk << 6).
+template <typename T, int D>
+__device__ __forceinline__ void slot_read_rows_v(const char* half, int c16, int g16,
+                                                 u32x4_t (&op)[D / 32]) {
+    using Lay = SlotLayout<T, D>;
+    typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
+    uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(half) + Lay::v_addr(c16, g16);
+    asm volatile("" : "+v"(base));
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+        op[kk] = *(lds_u32x4*)(uintptr_t)(base ^ (uint32_t)(kk << 6));
 }
 // Waits for every LDS read of this wave (and its scalar loads); values read by
 // slot_read_cols are used only through this call's outputs.

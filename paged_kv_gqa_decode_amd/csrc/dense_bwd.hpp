@@ -16,10 +16,10 @@
 //                    holding 16 keys; the Q/dY rows of all G heads stream
 //                    through a ring, so the group sums stay in registers (one
 //                    writer per dK/dV row, no atomics).
-// Every streamed tile of 16 rows is loaded twice into a pair of slots with the
-// roles swapped (X rows | Y columns, then Y rows | X columns), so that both
-// operand forms each product needs come from the slot reads of the decode
-// kernels.
+// Every streamed tile of 16 rows (K and V, or Q and dY) is loaded once into a
+// slot whose two halves both use the layout the transposing LDS read needs;
+// rows are read from the same layout (slot_read_rows_v), so each half serves
+// both operand forms its products take.
 #pragma once
 
 #include "dense_mfma.hpp"
@@ -66,8 +66,8 @@ void dense_bwd_dq(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
     constexpr int KS = D / 32, NT = D / 16;
     constexpr int NWI = NW < KS ? NW : KS;  // waves that issue loads
     constexpr int IPW = KS / NWI;           // instructions per half per issuing wave
-    constexpr int OPS = 4 * IPW;            // per key tile: two slots of two halves
-    constexpr int TB = 2 * Lay::kBytes;     // bytes of one key tile
+    constexpr int OPS = 2 * IPW;            // per key tile: two halves
+    constexpr int TB = Lay::kBytes;         // bytes of one key tile
     static_assert(D % 32 == 0 && Lay::kOps == KS && KS % NWI == 0, "shape");
     static_assert(kRing >= 3 && OPS * (kRing - 2) <= 63, "ring");
 
@@ -121,13 +121,12 @@ void dense_bwd_dq(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
     }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the row operands, before the ring's loads
 
-    // key tile s: slot A = K rows (| V columns, unused), slot B = V rows | K columns
+    // key tile s: K | V, both halves in the transposable layout
     auto fetch_tile = [&](int s) {
         const int64_t o = (int64_t)16 * s * D;
         const int rmax = min(15, g.SK - 1 - 16 * s);
-        char* sl = smem + (s % kRing) * TB;
-        fetch_rows<T, D, IPW>(kb + o, vb + o, rmax, sl, lane, wave, NWI);
-        fetch_rows<T, D, IPW>(vb + o, kb + o, rmax, sl + Lay::kBytes, lane, wave, NWI);
+        fetch_rows<T, D, IPW, true>(kb + o, vb + o, rmax, smem + (s % kRing) * TB, lane, wave,
+                                    NWI);
     };
     for (int s = 0; s < kRing - 1 && s < n_sub; ++s)
         if (issues) fetch_tile(s);
@@ -143,12 +142,11 @@ void dense_bwd_dq(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
         if (nxt < n_sub && issues) fetch_tile(nxt);
         if (!has_rows) continue;
         const char* sa = smem + (i % kRing) * TB;
-        const char* sb = sa + Lay::kBytes;
         u32x4_t kop[KS], vop[KS];
         u32x2_t kt[NT];
-        slot_read_rows<T, D>(sa, c16, g16, kop);
-        slot_read_rows<T, D>(sb, c16, g16, vop);
-        slot_read_cols<T, D>(sb, c16, g16, kt);
+        slot_read_rows_v<T, D>(sa, c16, g16, kop);
+        slot_read_rows_v<T, D>(sa + Lay::kKBytes, c16, g16, vop);
+        slot_read_cols_at<T, D>(sa, c16, g16, kt);
         slot_lds_wait<D>(kt);
         const int key0 = 16 * i;
         const int valid = min(16, kend - key0);
@@ -193,40 +191,49 @@ void dense_bwd_dq(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
     }  // blocks of this workgroup
 }
 
-// dK, dV: wave `wave` of a workgroup holds keys kw0 .. kw0 + 15 of (b, kh) as
-// operands (K, V rows) and two accumulators; the Q/dY rows of the G query
-// heads stream through the ring in 16-row tiles (head-major). Per tile, S = Q
-// K^T and dP = dY V^T give query rows 4*g16 + e against this lane's key c16,
-// then dV += P^T dY and dK += dS^T Q. The tile's 16 log-sum-exps and deltas
-// are read with scalar loads (lse and delta are read-only here), which the
-// vector-memory counter of the ring does not see; the statistics arrays hold
-// 16 entries of padding past the last row.
+// dK, dV: key wave kw (0..NW-1) of a workgroup holds keys kw0 .. kw0 + 15 of
+// (b, kh) as operands (K, V rows); two sets of NW waves hold the same keys and
+// take alternate tiles of the Q/dY rows of the G query heads (head-major, 16
+// rows a tile), so two waves share each SIMD. Per tile, S = Q K^T and dP = dY
+// V^T give query rows 4*g16 + e against this lane's key c16, then dV += P^T dY
+// and dK += dS^T Q. At the end the second set hands its accumulators to the
+// first through LDS. The tile's 16 log-sum-exps and deltas are read with
+// scalar loads (lse and delta are read-only here), which the vector-memory
+// counter of the ring does not see; the statistics arrays hold 16 entries of
+// padding past the last row.
+// Tiles run position-major from the last position tile down, heads inside, so
+// that the workgroups of every key block of (b, kh) start on the same tile and
+// read the same rows at about the same time (under the causal limit each stops
+// at its own first tile).
 template <typename T, int D, int NW, int kRing, int MASK>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dense_bwd_dkdv(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
                     const float* __restrict__ delta) {
     using Lay = SlotLayout<T, D>;
     using M = Mfma<T>;
+    constexpr int NSET = 2;                 // wave sets (alternate query tiles)
     constexpr int KS = D / 32, NT = D / 16;
-    constexpr int NWI = NW < KS ? NW : KS;
+    constexpr int NWI = NW < KS ? NW : KS;  // waves of a set that issue its loads
     constexpr int IPW = KS / NWI;
-    constexpr int OPS = 4 * IPW;
-    constexpr int TB = 2 * Lay::kBytes;
+    constexpr int OPS = 2 * IPW;            // per tile: two halves
+    constexpr int TB = Lay::kBytes;         // bytes of one tile
     static_assert(D % 32 == 0 && Lay::kOps == KS && KS % NWI == 0, "shape");
     static_assert(kRing >= 3 && OPS * (kRing - 2) <= 63, "ring");
+    static_assert(NW * 2 * NT * 4 * 64 * 4 <= kRing * NSET * TB, "hand-off fits the ring");
 
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const int lane = threadIdx.x & 63, c16 = lane & 15, g16 = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int set = wave / NW, kw = wave % NW;
     const DenseGeometry& g = d.g;
     const int nkb = (g.SK + 16 * NW - 1) / (16 * NW);  // key blocks per (b, kh)
     const int kblk = blockIdx.x % nkb;
     const int kh = (blockIdx.x / nkb) % g.HK;
     const int b = blockIdx.x / (nkb * g.HK);
-    const int kw0 = kblk * 16 * NW + 16 * wave;  // this wave's first key
+    const int kw0 = kblk * 16 * NW + 16 * kw;  // this wave's first key
     const int64_t kv0 = ((int64_t)b * g.HK + kh) * g.SK;
     const int64_t head0 = (int64_t)b * g.HQ + (int64_t)kh * g.G;
-    const bool issues = wave < NWI;
+    const bool issues = kw < NWI;
     const bool has_keys = kw0 < g.SK;
     // all-ones for the lane's 16-lane group g16, zero for the others (opaque to
     // the optimizer, which would otherwise turn the pick into an indexed
@@ -250,30 +257,34 @@ void dense_bwd_dkdv(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
     // query tiles: head gg of the group, positions 16*it .. +15; under the
-    // causal limit positions before the block's first key see none of its keys
+    // causal limit positions before the block's first key see none of its keys.
+    // Tile t: position tile ntile - 1 - t / G, head t % G. Iteration u holds
+    // tiles 2u (set 0) and 2u + 1 (set 1).
     const int ntile = (g.SQ + 15) / 16;
     const int it0 = g.causal ? min(ntile, kblk * NW) : 0;
     const int nit = ntile - it0;
     const int n_t = g.G * nit;
-    auto tile_row0 = [&](int t) -> int64_t {  // row index of the tile's first row
-        return (head0 + t / nit) * g.SQ + 16 * (it0 + t % nit);
+    const int n_u = (n_t + 1) / 2;
+    // a set past the last tile loads the last one again, so every issuing wave
+    // has the same loads in flight per iteration
+    auto fetch = [&](int u) {
+        const int t = min(2 * u + set, n_t - 1);
+        const int tp = t / g.G;
+        const int gg = t - tp * g.G, q0 = 16 * (ntile - 1 - tp);
+        const int64_t r0 = (head0 + gg) * g.SQ + q0;
+        fetch_rows<T, D, IPW, true>(d.q + r0 * D, w.dout + r0 * D, min(15, g.SQ - 1 - q0),
+                                    smem + ((u % kRing) * NSET + set) * TB, lane, kw, NWI);
     };
-    auto fetch_tile = [&](int t) {
-        const int64_t r0 = tile_row0(t);
-        const int rmax = min(15, g.SQ - 1 - 16 * (it0 + t % nit));
-        char* sl = smem + (t % kRing) * TB;
-        const T* qr = d.q + r0 * D;
-        const T* gr = w.dout + r0 * D;
-        fetch_rows<T, D, IPW>(qr, gr, rmax, sl, lane, wave, NWI);                  // Q rows | dY cols
-        fetch_rows<T, D, IPW>(gr, qr, rmax, sl + Lay::kBytes, lane, wave, NWI);  // dY rows | Q cols
-    };
-    for (int s = 0; s < kRing - 1 && s < n_t; ++s)
-        if (issues) fetch_tile(s);
+    for (int u = 0; u < kRing - 1 && u < n_u; ++u)
+        if (issues) fetch(u);
     const float* const lse0 = lse + head0 * g.SQ;  // statistics of the group's first row
     const float* const dl0 = delta + head0 * g.SQ;
-    for (int t = 0; t < n_t; ++t) {
-        const int gg = t / nit;                   // head of the group
-        const int q0 = 16 * (it0 + t - gg * nit);  // first query position of the tile
+    for (int u = 0; u < n_u; ++u) {
+        const int t = 2 * u + set;
+        const int tc = min(t, n_t - 1);
+        const int tp = tc / g.G;
+        const int gg = tc - tp * g.G;          // head of the group
+        const int q0 = 16 * (ntile - 1 - tp);  // first query position of the tile
         const int hq = kh * g.G + gg;
         const int sr = __builtin_amdgcn_readfirstlane(gg * g.SQ + q0);  // < 2^31 (checked)
         const float* ls = lse0 + sr;
@@ -290,23 +301,22 @@ void dense_bwd_dkdv(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
             lr[e] = pick4(lv[e], lv[4 + e], lv[8 + e], lv[12 + e], gmask);
             dr[e] = pick4(dv16[e], dv16[4 + e], dv16[8 + e], dv16[12 + e], gmask);
         }
-        const int ahead = min(kRing - 2, n_t - 1 - t);
+        const int ahead = min(kRing - 2, n_u - 1 - u);
         if (issues) wait_ahead<OPS, kRing - 2>(ahead);
         else __builtin_amdgcn_s_waitcnt(kWaitVm0);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        const int nxt = t + kRing - 1;
-        if (nxt < n_t && issues) fetch_tile(nxt);
-        if (!has_keys || (g.causal && kw0 > q0 + 15)) continue;  // no visible pair in this tile
-        const char* sa = smem + (t % kRing) * TB;
-        const char* sb = sa + Lay::kBytes;
+        const int nxt = u + kRing - 1;
+        if (nxt < n_u && issues) fetch(nxt);
+        if (t >= n_t || !has_keys || (g.causal && kw0 > q0 + 15)) continue;  // nothing visible
+        const char* sl = smem + ((u % kRing) * NSET + set) * TB;
         u32x4_t qa[KS], ga[KS];
         u32x2_t gt[NT], qt[NT];
-        slot_read_rows<T, D>(sa, c16, g16, qa);
-        slot_read_rows<T, D>(sb, c16, g16, ga);
-        slot_read_cols<T, D>(sa, c16, g16, gt);
-        slot_read_cols<T, D>(sb, c16, g16, qt);
+        slot_read_rows_v<T, D>(sl, c16, g16, qa);
+        slot_read_rows_v<T, D>(sl + Lay::kKBytes, c16, g16, ga);
+        slot_read_cols_at<T, D>(sl, c16, g16, qt);
+        slot_read_cols_at<T, D>(sl + Lay::kKBytes, c16, g16, gt);
         slot_lds_wait<D>(gt);
         slot_lds_wait<D>(qt);
         f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f}, dp = s;
@@ -333,22 +343,37 @@ void dense_bwd_dkdv(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
         M::make_p(p, phi, plo);
         M::make_p(ds, dhi, dlo);
 #pragma unroll
-        for (int u = 0; u < NT; ++u) {
-            dv[u] = M::pv(phi, plo, gt[u], dv[u]);
-            dk[u] = M::pv(dhi, dlo, qt[u], dk[u]);
+        for (int v = 0; v < NT; ++v) {
+            dv[v] = M::pv(phi, plo, gt[v], dv[v]);
+            dk[v] = M::pv(dhi, dlo, qt[v], dk[v]);
         }
     }
-    if (has_keys) {
+    // the second set's sums go to the first through the (now idle) ring
+    asm volatile("" ::: "memory");
+    __syncthreads();
+    float* const red = reinterpret_cast<float*>(smem) + (size_t)kw * 2 * NT * 4 * 64;
+    if (set == 1 && has_keys) {
+#pragma unroll
+        for (int v = 0; v < NT; ++v)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                red[(v * 4 + i) * 64 + lane] = dk[v][i];
+                red[((NT + v) * 4 + i) * 64 + lane] = dv[v][i];
+            }
+    }
+    __syncthreads();
+    if (set == 0 && has_keys) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int key = kw0 + 4 * g16 + i;
             if (key >= g.SK) continue;
-            T* kd = w.dk + (kv0 + key) * D + c16;
-            T* vd = w.dv + (kv0 + key) * D + c16;
+            const int64_t o = (kv0 + key) * D + c16;
 #pragma unroll
-            for (int u = 0; u < NT; ++u) {
-                Elem<T>::store(kd + 16 * u, dk[u][i] * w.scale);
-                Elem<T>::store(vd + 16 * u, dv[u][i]);
+            for (int v = 0; v < NT; ++v) {
+                const float ks = dk[v][i] + red[(v * 4 + i) * 64 + lane];
+                const float vs = dv[v][i] + red[((NT + v) * 4 + i) * 64 + lane];
+                Elem<T>::store(w.dk + o + 16 * v, ks * w.scale);
+                Elem<T>::store(w.dv + o + 16 * v, vs);
             }
         }
     }

@@ -691,7 +691,8 @@ int run_dense(const pa_dense_problem* p, const void* q, const void* k, const voi
 // ---------------------------------------------------------------------------
 // Dense GQA attention backward
 // ---------------------------------------------------------------------------
-// dK/dV: 16 keys per wave, four waves (64 keys) per workgroup.
+// dK/dV: 16 keys per wave, four key waves (64 keys) per workgroup, in two sets
+// that split the query tiles (eight waves).
 constexpr int kBwdKeyWaves = 4;
 
 // Bytes of one statistics array (lse or delta): a float per query row plus 16
@@ -702,30 +703,38 @@ size_t dense_stats_bytes(const pa_dense_problem* p) {
     return (size_t)(((rows + 16) * 4 + 255) / 256 * 256);
 }
 
+size_t dense_bwd_bytes(const pa_dense_problem* p) { return 2 * dense_stats_bytes(p); }
+
+// Rings: the statistics pass uses the forward's; a backward tile is one slot
+// (two halves of 16 rows), 64 KiB of them per workgroup (the dK/dV kernel's
+// slots are shared by its two wave sets).
 template <typename T, int D, int MASK>
 void launch_dense_bwd_k(const pa::DenseArgs<T>& a, const pa::BwdArgs<T>& w, unsigned grid_rows,
                         unsigned grid_keys, hipStream_t s) {
-    constexpr int kRing = D == 128 ? 4 : 8;
-    const size_t lds_fwd = (size_t)kRing * pa::SlotLayout<T, D>::kBytes;
-    const size_t lds_bwd = 2 * lds_fwd;  // a pair of slots per tile: 64 KiB
+    constexpr int kSlot = pa::SlotLayout<T, D>::kBytes;
+    constexpr int kRing = D == 128 ? 4 : 8;  // forward ring
+    constexpr int kRingDq = 65536 / kSlot;
+    constexpr int kRingKv = 65536 / (2 * kSlot);
+    const size_t lds_fwd = (size_t)kRing * kSlot;
+    const size_t lds_bwd = 65536;
     const float* lse = a.lse;
     const float* dl = a.delta;
     if (grid_rows) {
         if (a.g.causal) {
             hipLaunchKernelGGL((pa::dense_mfma<T, D, kDenseWaves, 1, kRing, MASK, true, true>),
                                dim3(grid_rows), dim3(64 * kDenseWaves), lds_fwd, s, a);
-            hipLaunchKernelGGL((pa::dense_bwd_dq<T, D, kDenseWaves, 1, kRing, MASK, true>),
+            hipLaunchKernelGGL((pa::dense_bwd_dq<T, D, kDenseWaves, 1, kRingDq, MASK, true>),
                                dim3(grid_rows), dim3(64 * kDenseWaves), lds_bwd, s, a, w, lse, dl);
         } else {
             hipLaunchKernelGGL((pa::dense_mfma<T, D, kDenseWaves, 2, kRing, MASK, false, true>),
                                dim3(grid_rows), dim3(64 * kDenseWaves), lds_fwd, s, a);
-            hipLaunchKernelGGL((pa::dense_bwd_dq<T, D, kDenseWaves, 2, kRing, MASK, false>),
+            hipLaunchKernelGGL((pa::dense_bwd_dq<T, D, kDenseWaves, 2, kRingDq, MASK, false>),
                                dim3(grid_rows), dim3(64 * kDenseWaves), lds_bwd, s, a, w, lse, dl);
         }
     }
     if (grid_keys)
-        hipLaunchKernelGGL((pa::dense_bwd_dkdv<T, D, kBwdKeyWaves, kRing, MASK>), dim3(grid_keys),
-                           dim3(64 * kBwdKeyWaves), lds_bwd, s, a, w, lse, dl);
+        hipLaunchKernelGGL((pa::dense_bwd_dkdv<T, D, kBwdKeyWaves, kRingKv, MASK>),
+                           dim3(grid_keys), dim3(128 * kBwdKeyWaves), lds_bwd, s, a, w, lse, dl);
 }
 
 template <typename T>
@@ -736,7 +745,7 @@ int run_dense_bwd(const pa_dense_problem* p, const void* q, const void* k, const
     a.dout = static_cast<const T*>(dout);
     a.lse = static_cast<float*>(workspace);
     a.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + dense_stats_bytes(p));
-    pa::BwdArgs<T> w;
+    pa::BwdArgs<T> w{};
     w.dout = a.dout;
     w.dq = static_cast<T*>(dq);
     w.dk = static_cast<T*>(dk);
@@ -794,7 +803,7 @@ int pa_dense_attention(const pa_dense_problem* problem, const void* q, const voi
 int pa_dense_backward_workspace_size(const pa_dense_problem* problem, size_t* bytes) {
     if (!bytes) return fail(PA_ERR_INVALID_ARG, "bytes is NULL");
     if (int rc = validate_dense(problem)) return rc;
-    *bytes = 2 * dense_stats_bytes(problem);
+    *bytes = dense_bwd_bytes(problem);
     return succeed();
 }
 
@@ -816,7 +825,7 @@ int pa_dense_attention_backward(const pa_dense_problem* problem, const void* q, 
     if (p->mask_kind != PA_MASK_NONE &&
         (!mask || (p->mask_kind == PA_MASK_ADD && misaligned(mask, 4))))
         return fail(PA_ERR_INVALID_ARG, "mask is NULL or (additive) not 4-byte aligned");
-    const size_t need = 2 * dense_stats_bytes(p);
+    const size_t need = dense_bwd_bytes(p);
     if (!workspace || workspace_bytes < need || misaligned(workspace, 256))
         return fail(PA_ERR_WORKSPACE, "workspace %p of %zu bytes: need %zu bytes, 256-byte "
                     "aligned (pa_dense_backward_workspace_size)", workspace, workspace_bytes, need);

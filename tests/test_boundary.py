@@ -218,9 +218,11 @@ def test_dense_backward_workspace_size(lib):
     # two fp32 arrays (log-sum-exp, delta) of one value per query row plus 16
     # of padding, each rounded up to 256 bytes
     for B, HQ, SQ in ((1, 8, 32), (3, 12, 7), (2, 32, 2048)):
-        _, n = pa.pa_dense_backward_workspace_size(
-            _dense_problem(batch=B, num_heads=HQ, num_kv_heads=HQ // 4, q_len=SQ))
-        assert n == 2 * (((B * HQ * SQ + 16) * 4 + 255) // 256 * 256)
+        for causal in (0, 1):
+            _, n = pa.pa_dense_backward_workspace_size(
+                _dense_problem(batch=B, num_heads=HQ, num_kv_heads=HQ // 4, q_len=SQ,
+                               causal=causal))
+            assert n == 2 * (((B * HQ * SQ + 16) * 4 + 255) // 256 * 256)
 
 
 def test_dense_backward_checks_pointers_and_workspace(lib):
