@@ -268,7 +268,10 @@ int pa_dense_attention(const pa_dense_problem* problem, const void* q, const voi
  * (G = num_heads / num_kv_heads). Products accumulate in fp32 and are rounded
  * once to the I/O dtype. `workspace` (device, 256-byte aligned, at least
  * pa_dense_backward_workspace_size bytes, no initial contents required) holds
- * two fp32 values per query row between the launches; dq, dk
+ * two fp32 values per query row between the launches and, for causal problems
+ * with num_heads / num_kv_heads >= 2, two fp32 halves of dk and of dv (each
+ * workgroup takes half the query heads of two key blocks of complementary
+ * weight; the halves are added in a fixed order); dq, dk
  * and dv are written whole; nothing else is written. Device pointers are owned by the
  * caller; asynchronous on `stream`. Supported shapes and errors as for
  * pa_dense_attention, plus PA_ERR_WORKSPACE for a missing, small or

@@ -33,6 +33,11 @@ struct BwdArgs {
     T* dk;          // [B, HK, SK, D]
     T* dv;
     float scale;
+    // causal, G >= 2 (SPLIT): fp32 sums of the two head halves, [2][B*HK*SK*D]
+    // each for dK (already scaled) and dV; dense_bwd_sum_halves adds them
+    float* part_dk;
+    float* part_dv;
+    int64_t part_n;  // B*HK*SK*D
 };
 
 // The 16-byte chunks 32*kk + 8*g16 of one row of D elements (an operand whose
@@ -205,7 +210,11 @@ void dense_bwd_dq(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
 // that the workgroups of every key block of (b, kh) start on the same tile and
 // read the same rows at about the same time (under the causal limit each stops
 // at its own first tile).
-template <typename T, int D, int NW, int kRing, int MASK>
+// SPLIT (causal, G >= 2): under the causal limit key block kb has tiles in
+// proportion to nkb - kb, so workgroup pair (2*w, 2*w + 1) takes the query heads
+// [0, G/2) and [G/2, G) of key block w and then of key block nkb - 1 - w: every
+// workgroup has the same work. Sums go to BwdArgs::part_* (fp32).
+template <typename T, int D, int NW, int kRing, int MASK, bool SPLIT>
 __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dense_bwd_dkdv(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
                     const float* __restrict__ delta) {
@@ -227,14 +236,17 @@ void dense_bwd_dkdv(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
     const int set = wave / NW, kw = wave % NW;
     const DenseGeometry& g = d.g;
     const int nkb = (g.SK + 16 * NW - 1) / (16 * NW);  // key blocks per (b, kh)
-    const int kblk = blockIdx.x % nkb;
-    const int kh = (blockIdx.x / nkb) % g.HK;
-    const int b = blockIdx.x / (nkb * g.HK);
-    const int kw0 = kblk * 16 * NW + 16 * kw;  // this wave's first key
+    const int npair = SPLIT ? (nkb + 1) / 2 : nkb;      // workgroup (pairs) per (b, kh)
+    const int part = SPLIT ? (int)(blockIdx.x & 1) : 0;
+    const int wgi = SPLIT ? (int)(blockIdx.x >> 1) : (int)blockIdx.x;
+    const int wblk = wgi % npair;
+    const int kh = (wgi / npair) % g.HK;
+    const int b = wgi / (npair * g.HK);
     const int64_t kv0 = ((int64_t)b * g.HK + kh) * g.SK;
     const int64_t head0 = (int64_t)b * g.HQ + (int64_t)kh * g.G;
     const bool issues = kw < NWI;
-    const bool has_keys = kw0 < g.SK;
+    const int g_lo = SPLIT ? part * (g.G / 2) : 0;  // the heads [g_lo, g_lo + GH) of the group
+    const int GH = SPLIT ? (part == 0 ? g.G / 2 : g.G - g.G / 2) : g.G;
     // all-ones for the lane's 16-lane group g16, zero for the others (opaque to
     // the optimizer, which would otherwise turn the pick into an indexed
     // private array)
@@ -245,6 +257,15 @@ void dense_bwd_dkdv(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
         asm volatile("" : "+v"(gmask[j]));
     }
 
+    for (int half = 0; half < (SPLIT ? 2 : 1); ++half) {
+    const int kblk = half == 0 ? wblk : nkb - 1 - wblk;
+    if (half == 1) {
+        if (kblk == wblk) break;  // odd block count: the middle block has no partner
+        asm volatile("" ::: "memory");
+        __syncthreads();          // the first block's hand-off is read out
+    }
+    const int kw0 = kblk * 16 * NW + 16 * kw;  // this wave's first key
+    const bool has_keys = kw0 < g.SK;
     u32x4_t kfr[KS], vfr[KS];
     {
         const int64_t kr = kv0 + min(kw0 + c16, g.SK - 1);
@@ -258,19 +279,19 @@ void dense_bwd_dkdv(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
 
     // query tiles: head gg of the group, positions 16*it .. +15; under the
     // causal limit positions before the block's first key see none of its keys.
-    // Tile t: position tile ntile - 1 - t / G, head t % G. Iteration u holds
-    // tiles 2u (set 0) and 2u + 1 (set 1).
+    // Tile t: position tile ntile - 1 - t / GH, head g_lo + t % GH. Iteration u
+    // holds tiles 2u (set 0) and 2u + 1 (set 1).
     const int ntile = (g.SQ + 15) / 16;
     const int it0 = g.causal ? min(ntile, kblk * NW) : 0;
     const int nit = ntile - it0;
-    const int n_t = g.G * nit;
+    const int n_t = GH * nit;
     const int n_u = (n_t + 1) / 2;
     // a set past the last tile loads the last one again, so every issuing wave
     // has the same loads in flight per iteration
     auto fetch = [&](int u) {
         const int t = min(2 * u + set, n_t - 1);
-        const int tp = t / g.G;
-        const int gg = t - tp * g.G, q0 = 16 * (ntile - 1 - tp);
+        const int tp = t / GH;
+        const int gg = g_lo + t - tp * GH, q0 = 16 * (ntile - 1 - tp);
         const int64_t r0 = (head0 + gg) * g.SQ + q0;
         fetch_rows<T, D, IPW, true>(d.q + r0 * D, w.dout + r0 * D, min(15, g.SQ - 1 - q0),
                                     smem + ((u % kRing) * NSET + set) * TB, lane, kw, NWI);
@@ -282,8 +303,8 @@ void dense_bwd_dkdv(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
     for (int u = 0; u < n_u; ++u) {
         const int t = 2 * u + set;
         const int tc = min(t, n_t - 1);
-        const int tp = tc / g.G;
-        const int gg = tc - tp * g.G;          // head of the group
+        const int tp = tc / GH;
+        const int gg = g_lo + tc - tp * GH;    // head of the group
         const int q0 = 16 * (ntile - 1 - tp);  // first query position of the tile
         const int hq = kh * g.G + gg;
         const int sr = __builtin_amdgcn_readfirstlane(gg * g.SQ + q0);  // < 2^31 (checked)
@@ -370,13 +391,37 @@ void dense_bwd_dkdv(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
             const int64_t o = (kv0 + key) * D + c16;
 #pragma unroll
             for (int v = 0; v < NT; ++v) {
-                const float ks = dk[v][i] + red[(v * 4 + i) * 64 + lane];
+                const float ks = (dk[v][i] + red[(v * 4 + i) * 64 + lane]) * w.scale;
                 const float vs = dv[v][i] + red[((NT + v) * 4 + i) * 64 + lane];
-                Elem<T>::store(w.dk + o + 16 * v, ks * w.scale);
-                Elem<T>::store(w.dv + o + 16 * v, vs);
+                if constexpr (SPLIT) {
+                    w.part_dk[part * w.part_n + o + 16 * v] = ks;
+                    w.part_dv[part * w.part_n + o + 16 * v] = vs;
+                } else {
+                    Elem<T>::store(w.dk + o + 16 * v, ks);
+                    Elem<T>::store(w.dv + o + 16 * v, vs);
+                }
             }
         }
     }
+    }  // key blocks of this workgroup
+}
+
+// dK = part_dk[0] + part_dk[1], dV likewise, rounded once to the I/O dtype;
+// four elements per thread (part_n is a multiple of 64).
+template <typename T>
+__global__ __launch_bounds__(256) void dense_bwd_sum_halves(BwdArgs<T> w) {
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= 2 * w.part_n) return;
+    const bool is_v = e >= w.part_n;
+    const int64_t o = is_v ? e - w.part_n : e;
+    const float* p = is_v ? w.part_dv : w.part_dk;
+    const float4 a = *reinterpret_cast<const float4*>(p + o);
+    const float4 c = *reinterpret_cast<const float4*>(p + w.part_n + o);
+    T* dst = (is_v ? w.dv : w.dk) + o;
+    Elem<T>::store(dst + 0, a.x + c.x);
+    Elem<T>::store(dst + 1, a.y + c.y);
+    Elem<T>::store(dst + 2, a.z + c.z);
+    Elem<T>::store(dst + 3, a.w + c.w);
 }
 
 }  // namespace pa

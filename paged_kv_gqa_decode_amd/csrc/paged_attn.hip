@@ -703,7 +703,22 @@ size_t dense_stats_bytes(const pa_dense_problem* p) {
     return (size_t)(((rows + 16) * 4 + 255) / 256 * 256);
 }
 
-size_t dense_bwd_bytes(const pa_dense_problem* p) { return 2 * dense_stats_bytes(p); }
+// Elements of dK (and of dV): batch * num_kv_heads * kv_len * head_dim.
+int64_t dense_kv_elems(const pa_dense_problem* p) {
+    return (int64_t)p->batch * p->num_kv_heads * p->kv_len * p->head_dim;
+}
+
+// Causal calls with G >= 2 give each dK/dV workgroup half the query heads of two
+// key blocks of complementary weight; their fp32 sums (two halves of dK and of
+// dV) follow the statistics in the workspace.
+bool dense_bwd_split(const pa_dense_problem* p) {
+    return p->causal && p->num_heads / p->num_kv_heads >= 2;
+}
+size_t dense_bwd_bytes(const pa_dense_problem* p) {
+    size_t n = 2 * dense_stats_bytes(p);
+    if (dense_bwd_split(p)) n += (size_t)(4 * dense_kv_elems(p)) * sizeof(float);
+    return n;
+}
 
 // Rings: the statistics pass uses the forward's; a backward tile is one slot
 // (two halves of 16 rows), 64 KiB of them per workgroup (the dK/dV kernel's
@@ -732,9 +747,15 @@ void launch_dense_bwd_k(const pa::DenseArgs<T>& a, const pa::BwdArgs<T>& w, unsi
                                dim3(grid_rows), dim3(64 * kDenseWaves), lds_bwd, s, a, w, lse, dl);
         }
     }
-    if (grid_keys)
-        hipLaunchKernelGGL((pa::dense_bwd_dkdv<T, D, kBwdKeyWaves, kRingKv, MASK>),
+    if (grid_keys && w.part_dk) {  // grid_keys = workgroups: pairs of key blocks, two head halves
+        hipLaunchKernelGGL((pa::dense_bwd_dkdv<T, D, kBwdKeyWaves, kRingKv, MASK, true>),
                            dim3(grid_keys), dim3(128 * kBwdKeyWaves), lds_bwd, s, a, w, lse, dl);
+        hipLaunchKernelGGL((pa::dense_bwd_sum_halves<T>),
+                           dim3((unsigned)ceil_div(2 * w.part_n, 4 * 256)), dim3(256), 0, s, w);
+    } else if (grid_keys) {
+        hipLaunchKernelGGL((pa::dense_bwd_dkdv<T, D, kBwdKeyWaves, kRingKv, MASK, false>),
+                           dim3(grid_keys), dim3(128 * kBwdKeyWaves), lds_bwd, s, a, w, lse, dl);
+    }
 }
 
 template <typename T>
@@ -751,10 +772,18 @@ int run_dense_bwd(const pa_dense_problem* p, const void* q, const void* k, const
     w.dk = static_cast<T*>(dk);
     w.dv = static_cast<T*>(dv);
     w.scale = scale;
+    w.part_n = dense_kv_elems(p);
+    if (dense_bwd_split(p)) {
+        w.part_dk = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             2 * dense_stats_bytes(p));
+        w.part_dv = w.part_dk + 2 * w.part_n;
+    }
     const int64_t grid_rows = p->q_len > 0 ? dense_row_grid(p, a.g) : 0;
+    const int64_t nkb = ceil_div(p->kv_len, 16 * kBwdKeyWaves);  // key blocks per (b, kh)
     const int64_t grid_keys = (int64_t)p->batch * p->num_kv_heads *
-                              ceil_div(p->kv_len, 16 * kBwdKeyWaves);
-    if (grid_rows >= (1LL << 31) || grid_keys >= (1LL << 31))
+                              (dense_bwd_split(p) ? 2 * ((nkb + 1) / 2) : nkb);
+    if (grid_rows >= (1LL << 31) || grid_keys >= (1LL << 31) ||
+        ceil_div(2 * w.part_n, 4 * 256) >= (1LL << 31))
         return fail(PA_ERR_UNSUPPORTED, "too many workgroups (%lld, %lld) for one call",
                     (long long)grid_rows, (long long)grid_keys);
     const unsigned gr = (unsigned)grid_rows, gk = (unsigned)grid_keys;

@@ -216,13 +216,17 @@ def test_dense_backward_rejects(lib, kw, code):
 
 def test_dense_backward_workspace_size(lib):
     # two fp32 arrays (log-sum-exp, delta) of one value per query row plus 16
-    # of padding, each rounded up to 256 bytes
-    for B, HQ, SQ in ((1, 8, 32), (3, 12, 7), (2, 32, 2048)):
+    # of padding, each rounded up to 256 bytes; causal with G >= 2: two fp32
+    # halves of dk and of dv follow
+    for B, HQ, SQ, SK in ((1, 8, 32, 40), (3, 12, 7, 9), (2, 32, 2048, 2048)):
         for causal in (0, 1):
             _, n = pa.pa_dense_backward_workspace_size(
-                _dense_problem(batch=B, num_heads=HQ, num_kv_heads=HQ // 4, q_len=SQ,
+                _dense_problem(batch=B, num_heads=HQ, num_kv_heads=HQ // 4, q_len=SQ, kv_len=SK,
                                causal=causal))
-            assert n == 2 * (((B * HQ * SQ + 16) * 4 + 255) // 256 * 256)
+            stats = 2 * (((B * HQ * SQ + 16) * 4 + 255) // 256 * 256)
+            assert n == stats + causal * 4 * 4 * (B * (HQ // 4) * SK * 128)
+    _, n = pa.pa_dense_backward_workspace_size(_dense_problem(num_heads=2, num_kv_heads=2))
+    assert n == 2 * (((1 * 2 * 32 + 16) * 4 + 255) // 256 * 256)  # G = 1: no halves
 
 
 def test_dense_backward_checks_pointers_and_workspace(lib):
