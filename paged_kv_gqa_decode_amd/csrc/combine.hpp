@@ -102,12 +102,30 @@ namespace pa {
 // the metadata.
 template <typename T>
 struct SplitCombineArgs {
-    const float* ws_o;     // [slots][R][D]
+    const typename Partial<T>::type* ws_o;  // [slots][R][D] (Partial<T>)
     const float* ws_ml;    // [slots][R][2]
     const int32_t* meta;   // [B][2]     first and last group of each sequence
     T* out;
     int KV, H, NQ, R;
 };
+
+// The PER fp16 partial-output elements of a lane, read as one 32-bit word or as
+// zero-extended 16-bit words, so that no load writes half a register and has to
+// wait for the one before it.
+template <int PER>
+__device__ __forceinline__ void load_partial(const _Float16* src, float (&o)[PER]) {
+    if constexpr (PER == 2) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(src);
+        o[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+        o[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    } else {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const uint32_t w = *reinterpret_cast<const uint16_t*>(src + e);
+            o[e] = (float)__builtin_bit_cast(_Float16, (uint16_t)w);
+        }
+    }
+}
 
 template <typename T, int D, int WPR>
 __global__ __launch_bounds__(256) void combine_split(SplitCombineArgs<T> a) {
@@ -132,7 +150,7 @@ __global__ __launch_bounds__(256) void combine_split(SplitCombineArgs<T> a) {
     const int p0 = WPR == 1 ? 0 : min(n, wave * per_w), p1 = WPR == 1 ? n : min(n, p0 + per_w);
     const int64_t first = (b + s0) * a.KV + (u - b * a.KV);  // slot of piece g0
     const float* ml = a.ws_ml + (first * R + rho) * 2;
-    const float* po = a.ws_o + (first * R + rho) * D + lane * PER;
+    const auto* po = a.ws_o + (first * R + rho) * D + lane * PER;
     // consecutive groups of one (sequence, head) are KV slots apart
     const int64_t mstride = (int64_t)a.KV * R * 2, ostride = (int64_t)a.KV * R * D;
 
@@ -145,11 +163,16 @@ __global__ __launch_bounds__(256) void combine_split(SplitCombineArgs<T> a) {
             const int cn = min(64, p1 - c0);
             // partial outputs of the first batch, issued before the (m, l) are used
             float ov[kBatch][PER];
+            // (fp16: pieces past the run read the last one again, with weight 0)
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j)
+            for (int j = 0; j < kBatch; ++j) {
+                if constexpr (Partial<T>::kNorm)
+                    load_partial<PER>(po + (c0 + min(j, cn - 1)) * ostride, ov[j]);
+                else
 #pragma unroll
-                for (int e = 0; e < PER; ++e)
-                    ov[j][e] = j < cn ? po[(c0 + j) * ostride + e] : 0.f;
+                    for (int e = 0; e < PER; ++e)
+                        ov[j][e] = j < cn ? po[(c0 + j) * ostride + e] : 0.f;
+            }
             const bool mine = lane < cn;
             const float mp = mine ? ml[(c0 + lane) * mstride] : kNegMax;
             const float lp = mine ? ml[(c0 + lane) * mstride + 1] : 0.f;
@@ -162,19 +185,24 @@ __global__ __launch_bounds__(256) void combine_split(SplitCombineArgs<T> a) {
             M = Mn;
             const float wp = mine ? fast_exp2(mp - M) : 0.f;
             Lw += wave_sum(wp * lp);
+            const float wo = Partial<T>::kNorm ? wp * lp : wp;  // weight of the stored o
             for (int j0 = 0; j0 < cn; j0 += kBatch) {
                 if (j0 > 0) {
 #pragma unroll
-                    for (int j = 0; j < kBatch; ++j)
+                    for (int j = 0; j < kBatch; ++j) {
+                        if constexpr (Partial<T>::kNorm)
+                            load_partial<PER>(po + (c0 + min(j0 + j, cn - 1)) * ostride, ov[j]);
+                        else
 #pragma unroll
-                        for (int e = 0; e < PER; ++e)
-                            ov[j][e] = j0 + j < cn ? po[(c0 + j0 + j) * ostride + e] : 0.f;
+                            for (int e = 0; e < PER; ++e)
+                                ov[j][e] = j0 + j < cn ? po[(c0 + j0 + j) * ostride + e] : 0.f;
+                    }
                 }
 #pragma unroll
                 for (int j = 0; j < kBatch; ++j) {
                     // weight of piece j0 + j (lane j0 + j; 0 past the run's end)
                     const float w = __builtin_bit_cast(
-                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wp), (j0 + j) & 63));
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wo), (j0 + j) & 63));
 #pragma unroll
                     for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, ov[j][e], acc[e]);
                 }

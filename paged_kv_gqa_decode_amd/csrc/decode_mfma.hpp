@@ -141,7 +141,7 @@ struct SplitArgs {
     const T* new_k;
     const T* new_v;
     T* out;
-    float* ws_o;   // [slots][R][D]  unnormalised partial outputs
+    typename Partial<T>::type* ws_o;  // [slots][R][D]  partial outputs (Partial<T>)
     float* ws_ml;  // [slots][R][2]  (max, sum) in base-2 units
     int32_t* meta; // [B][2]         first and last group overlapping each sequence
     SplitGeometry g;
@@ -797,8 +797,14 @@ struct RowTiles {
                     T* dst = a.out + (g0 + r) * D + c16;
 #pragma unroll
                     for (int t = 0; t < NT; ++t) Elem<T>::store(dst + 16 * t, acc[rt][t][i] * inv);
+                } else if constexpr (Partial<T>::kNorm) {
+                    const float inv = l_r != 0.f ? 1.f / l_r : 0.f;
+                    auto* dst = a.ws_o + (slot * R + r) * D + c16;
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+                        dst[16 * t] = (typename Partial<T>::type)(acc[rt][t][i] * inv);
                 } else {
-                    float* dst = a.ws_o + (slot * R + r) * D + c16;
+                    auto* dst = a.ws_o + (slot * R + r) * D + c16;
 #pragma unroll
                     for (int t = 0; t < NT; ++t) dst[16 * t] = acc[rt][t][i];
                 }

@@ -79,6 +79,19 @@ template <> struct Elem<bf16_t> {
     }
 };
 
+// Partial outputs of the matrix-core family's split pieces. fp16 I/O: o / l
+// stored as fp16 (|o / l| <= max |v|, which fp16 holds; 2^-12 relative), half
+// the bytes of the workspace round trip; the merge weighs piece p by 2^(m_p -
+// M) * l_p. Other types: the unnormalised fp32 o, weighed by 2^(m_p - M).
+template <typename T> struct Partial {
+    using type = float;
+    static constexpr bool kNorm = false;
+};
+template <> struct Partial<_Float16> {
+    using type = _Float16;
+    static constexpr bool kNorm = true;
+};
+
 __device__ __forceinline__ uint4 load16(const void* p) {
     return *reinterpret_cast<const uint4*>(p);
 }

@@ -256,10 +256,19 @@ size_t state_floats(const pa_problem* p, const Plan& pl) {
     return (size_t)p->batch * p->num_heads * p->nq * (size_t)pl.parts;
 }
 
+// Bytes of one partial-output element: fp16 I/O on the matrix-core family keeps
+// them as fp16 (Partial<T>), everything else as fp32.
+size_t partial_bytes(const pa_problem* p, const Plan& pl) {
+    return pl.kernel == PA_KERNEL_MFMA && p->dtype == PA_F16 ? 2 : 4;
+}
+// Byte offset of the (max, sum) pairs: after the partial outputs.
+size_t ml_offset(const pa_problem* p, const Plan& pl) {
+    return state_floats(p, pl) * (size_t)p->head_dim * partial_bytes(p, pl);
+}
 // Matrix-core family: after the states, two int32 per sequence: the first and
 // last group that overlap it (written by pass 1).
 size_t meta_offset(const pa_problem* p, const Plan& pl) {
-    return state_floats(p, pl) * (size_t)(p->head_dim + 2) * sizeof(float);
+    return ml_offset(p, pl) + state_floats(p, pl) * 2 * sizeof(float);
 }
 
 size_t workspace_bytes_for(const pa_problem* p, const Plan& pl) {
@@ -396,12 +405,10 @@ void launch_pass1_mfma(const pa_problem* p, const Plan& pl, hipStream_t s,
     a.new_k = d.new_k;
     a.new_v = d.new_v;
     a.out = d.out;
-    const size_t sf = state_floats(p, pl);
-    a.ws_o = d.ws_o;
-    a.ws_ml = d.ws_o ? d.ws_o + sf * p->head_dim : nullptr;
-    a.meta = d.ws_o ? reinterpret_cast<int32_t*>(reinterpret_cast<char*>(d.ws_o) +
-                                                 meta_offset(p, pl))
-                    : nullptr;
+    char* const ws = reinterpret_cast<char*>(d.ws_o);
+    a.ws_o = reinterpret_cast<typename pa::Partial<T>::type*>(ws);
+    a.ws_ml = ws ? reinterpret_cast<float*>(ws + ml_offset(p, pl)) : nullptr;
+    a.meta = ws ? reinterpret_cast<int32_t*>(ws + meta_offset(p, pl)) : nullptr;
     a.g = split_geometry(p, pl);
     a.H = p->num_heads;
     a.causal = p->causal;
@@ -443,9 +450,9 @@ void launch_combine(const pa_problem* p, const Plan& pl, hipStream_t s, const fl
     const int64_t rows = (int64_t)p->batch * p->num_heads * p->nq;
     if (pl.kernel == PA_KERNEL_MFMA) {
         pa::SplitCombineArgs<T> c;
-        const size_t sf = state_floats(p, pl);
-        c.ws_o = ws;
-        c.ws_ml = ws + sf * p->head_dim;
+        const char* const wb = reinterpret_cast<const char*>(ws);
+        c.ws_o = reinterpret_cast<const typename pa::Partial<T>::type*>(wb);
+        c.ws_ml = reinterpret_cast<const float*>(wb + ml_offset(p, pl));
         c.meta = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(ws) +
                                                   meta_offset(p, pl));
         c.out = static_cast<T*>(out);

@@ -79,8 +79,9 @@ def test_forced_partitions_cover_the_context(lib, forced):
 def test_workspace_size(lib):
     prob = spec_problem(W.CONFIGS[1], 4096)
     _, nbytes = pa.pa_workspace_size_ex(prob, 256)
-    # slots = (B + groups)*KV, each R = 4 rows of D + 2 floats; then 2 int32 per sequence
-    assert nbytes == (32 + 256) * 8 * 4 * (128 + 2) * 4 + 32 * 2 * 4
+    # slots = (B + groups)*KV, each R = 4 rows of D fp16 partial outputs (fp16 I/O)
+    # and 2 floats; then 2 int32 per sequence
+    assert nbytes == (32 + 256) * 8 * 4 * (128 * 2 + 2 * 4) + 32 * 2 * 4
     prob = spec_problem(W.CONFIGS[1], 4096, kernel=pa.PA_KERNEL_VALU)
     _, nbytes = pa.pa_workspace_size_ex(prob, 256)
     _, p, _, _ = pa.pa_plan_ex(prob, 256)
