@@ -134,16 +134,18 @@ int pa_plan(const pa_problem* problem, int32_t* partitions, int32_t* chunk_token
 /*
  * Workspace bytes paged_attn_decode needs on the current device: 0 for a plan
  * that needs no merge. No initial contents are required. The workspace holds
- * fp32 online-softmax states (the page's VECTOR_PARTIALS state, in base-2
- * units): o = sum_i 2^(t_i - m) v_i (unnormalised), m = max_i t_i and
- * l = sum_i 2^(t_i - m), with t_i = s_i * log2(e) over some keys of a row.
+ * online-softmax states (the page's VECTOR_PARTIALS state, in base-2 units):
+ * o = sum_i 2^(t_i - m) v_i (unnormalised), m = max_i t_i and
+ * l = sum_i 2^(t_i - m), with t_i = s_i * log2(e) over some keys of a row;
+ * m and l are fp32, o is fp32 except as noted below.
  *   PA_KERNEL_MFMA (balanced split): the sequences laid end to end in
  *   positions of 16 keys (ceil(L_b/16) cached, then ceil(nq/16) new) are cut
  *   into `partitions` groups of equal length (+-1); the piece of sequence b in
  *   group g, for KV head kh, is slot (b + g)*num_kv_heads + kh. Layout:
- *   o[slots][R][head_dim], ml[slots][R][2], then int32 [B][2] = first and last
- *   group of each sequence (written by pass 1); slots = (B + partitions) *
- *   num_kv_heads, R = (H/KV)*nq (rows of one KV head, r_local = (h % G)*nq + r).
+ *   o[slots][R][head_dim] (for PA_F16 stored as o / l in fp16), ml[slots][R][2],
+ *   then int32 [B][2] = first and last group of each sequence (written by pass
+ *   1); slots = (B + partitions) * num_kv_heads, R = (H/KV)*nq (rows of one KV
+ *   head, r_local = (h % G)*nq + r).
  *   PA_KERNEL_VALU (chunks of chunk_tokens cached keys per sequence):
  *   o[rows][P][head_dim], ml[rows][P][2] with rows = B*H*nq, row = (b*H + h)*nq + r.
  * States that are not needed (a unit or sequence done in one piece) are not
