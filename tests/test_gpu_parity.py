@@ -320,6 +320,8 @@ DENSE_BWD_GPU = DENSE_GPU + [
     (1, 8, 2, 24, 80, 128, "bf16", None, None, True),              # SK > SQ: keys no query sees
     (1, 8, 2, 130, 150, 128, "f16", None, None, False),            # several key blocks and tiles
     (2, 8, 1, 70, 90, 64, "bf16", "bool", (2, 8, 70, 90), True),   # G = 8, D = 64, masked
+    (1, 8, 2, 150, 150, 128, "f16", None, None, True),             # 3 key blocks: the middle alone
+    (1, 6, 2, 40, 200, 64, "f16", "add", (1, 6, 40, 200), True),   # G = 3 halves, 4 key blocks
 ]
 
 
@@ -354,6 +356,25 @@ def test_dense_backward_matches_the_oracle(case):
     check_grad("dq", dq, edq, dtype)
     check_grad("dk", dk, edk, dtype)
     check_grad("dv", dv, edv, dtype)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_backward_empty_sides(causal):
+    # no queries: dk and dv are written as zeros; no keys: dq is
+    g = torch.Generator().manual_seed(81)
+    k = torch.randn(1, 2, 50, 64, generator=g).half().to(DEV)
+    v = torch.randn(1, 2, 50, 64, generator=g).half().to(DEV)
+    q0 = torch.empty(1, 8, 0, 64, dtype=torch.float16, device=DEV)
+    print(f"[gpu] dense backward without queries causal={causal}", flush=True)
+    _, dk, dv = pa.dense_attention_backward(q0, k, v, q0, 0.1, causal=causal)
+    torch.cuda.synchronize()
+    assert (dk == 0).all() and (dv == 0).all()
+    q = torch.randn(1, 8, 20, 64, generator=g).half().to(DEV)
+    k0 = torch.empty(1, 2, 0, 64, dtype=torch.float16, device=DEV)
+    print(f"[gpu] dense backward without keys causal={causal}", flush=True)
+    dq, _, _ = pa.dense_attention_backward(q, k0, k0, q, 0.1, causal=causal)
+    torch.cuda.synchronize()
+    assert (dq == 0).all()
 
 
 def test_dense_backward_prefill_sampled():
