@@ -7,7 +7,7 @@
 //   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dY,
 // dK and dV of KV head kh summed over the G query heads h = kh*G + g.
 //
-// Three launches: the forward kernel in its statistics form (per query row the
+// Launches: the forward kernel in its statistics form (per query row the
 // base-2 log-sum-exp of the scores and delta, Y kept in fp32 and never stored),
 // then the two kernels below, which recompute P from those statistics:
 //   dense_bwd_dq   - a workgroup per (sequence, KV head, block of positions),
@@ -15,7 +15,9 @@
 //   dense_bwd_dkdv - a workgroup per (sequence, KV head, 16*NW keys), each wave
 //                    holding 16 keys; the Q/dY rows of all G heads stream
 //                    through a ring, so the group sums stay in registers (one
-//                    writer per dK/dV row, no atomics).
+//                    writer per dK/dV row, no atomics); under the causal limit
+//                    (G >= 2) each workgroup takes half the heads of two key
+//                    blocks and dense_bwd_sum_halves adds the two halves.
 // Every streamed tile of 16 rows (K and V, or Q and dY) is loaded once into a
 // slot whose two halves both use the layout the transposing LDS read needs;
 // rows are read from the same layout (slot_read_rows_v), so each half serves
@@ -139,7 +141,7 @@ void dense_bwd_dq(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
         const int ahead = min(kRing - 2, n_sub - 1 - i);  // tiles fetched after i
         if (issues) wait_ahead<OPS, kRing - 2>(ahead);
         else __builtin_amdgcn_s_waitcnt(kWaitVm0);
-        // every wave's part of tile i is in; slot pair i - 1 is read out
+        // every wave's part of tile i is in; slot i - 1 is read out
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
@@ -198,8 +200,8 @@ void dense_bwd_dq(DenseArgs<T> d, BwdArgs<T> w, const float* __restrict__ lse,
 
 // dK, dV: key wave kw (0..NW-1) of a workgroup holds keys kw0 .. kw0 + 15 of
 // (b, kh) as operands (K, V rows); two sets of NW waves hold the same keys and
-// take alternate tiles of the Q/dY rows of the G query heads (head-major, 16
-// rows a tile), so two waves share each SIMD. Per tile, S = Q K^T and dP = dY
+// take alternate tiles of the Q/dY rows of the G query heads (16 rows a tile),
+// so two waves share each SIMD. Per tile, S = Q K^T and dP = dY
 // V^T give query rows 4*g16 + e against this lane's key c16, then dV += P^T dY
 // and dK += dS^T Q. At the end the second set hands its accumulators to the
 // first through LDS. The tile's 16 log-sum-exps and deltas are read with

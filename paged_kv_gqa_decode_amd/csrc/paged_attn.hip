@@ -851,8 +851,7 @@ int pa_dense_attention_backward(const pa_dense_problem* problem, const void* q, 
     const pa_dense_problem* p = problem;
     if (p->batch == 0 || (p->q_len == 0 && p->kv_len == 0)) return succeed();
     const bool rows = p->q_len > 0, keys = p->kv_len > 0;
-    if ((rows && (!q || !dout || !dq)) || (keys && (!k || !v || !dk || !dv)) ||
-        (rows && keys && (!q || !k)))
+    if ((rows && (!q || !dout || !dq)) || (keys && (!k || !v || !dk || !dv)))
         return fail(PA_ERR_INVALID_ARG, "a tensor pointer is NULL (q %p, k %p, v %p, dout %p, "
                     "dq %p, dk %p, dv %p)", q, k, v, dout, dq, dk, dv);
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(dout, 16) ||
