@@ -586,9 +586,11 @@ def test_plan_on_device_matches_pure_host_plan():
     assert pa.pa_plan(prob)[1:] == pa.pa_plan_ex(prob, cus)[1:]
 
 
+@pytest.mark.parametrize("spec", [SMALL[1], SMALL[0]], ids=["bf16", "f16"])
 @pytest.mark.parametrize("kernel", [pa.PA_KERNEL_MFMA, pa.PA_KERNEL_VALU])
-def test_deferred_combine_matches_one_call(kernel):
-    w = to_device(W.make_workload(SMALL[1], device="cpu"))
+def test_deferred_combine_matches_one_call(kernel, spec):
+    # fp16 on the matrix-core family keeps its partial outputs as fp16 o / l
+    w = to_device(W.make_workload(spec, device="cpu"))
     table = torch.from_numpy(w.block_table).to(DEV)
     lens = torch.from_numpy(w.context_lens).to(DEV)
     args = (w.q, w.k_pool, w.v_pool, table, lens, w.new_k, w.new_v, w.scale)
