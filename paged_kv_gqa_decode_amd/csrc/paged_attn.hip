@@ -138,17 +138,14 @@ struct Plan {
 // Matrix-core family launch shapes, by 16-row tiles per KV head (Plan::rt):
 //   rt = 1: decode_mfma, one wave per (group, head) with one row tile;
 //   rt = 2: decode_mfma with two row tiles per wave;
-//   rt = 4: decode_mfma_coop, four waves of one row tile per (group, head)
-//           sharing a ring of four slots, 3 waves per SIMD (3 workgroups per
-//           CU: a one-tile wave needs ~137 VGPRs);
-// rt = 1, 2 at 2 waves per SIMD, each keeping about 128 KiB of sub-pages in
-// flight per CU (slots double for D = 64, whose slots are half as large).
-// Measured on the Llama-3-8B-shaped and ragged-serving workloads: 2 waves per
-// SIMD with 2 slots each beat 4 waves with 1 slot (oldest waves hog the memory
-// path, the last quarter of the kernel runs thin) and 1 wave with 4 slots; for
-// 64 rows (multi-row causal), 4 waves x 1 tile at 3 waves per SIMD (96 groups)
-// beat 2 waves x 2 tiles at 2 per SIMD (128 groups) by 4 %, 4 x 1 at 2 per SIMD
-// by 14 %, and a 6-slot ring by 5 %.
+//   rt = 4: decode_mfma_coop, two waves of two row tiles per (group, head)
+//           sharing a ring of four slots;
+// all at 2 waves per SIMD, each keeping about 128 KiB of sub-pages in flight
+// per CU (slots double for D = 64, whose slots are half as large). Measured
+// on the Llama-3-8B-shaped and ragged-serving workloads: 2 waves per SIMD with
+// 2 slots each beat 4 waves with 1 slot (oldest waves hog the memory path,
+// the last quarter of the kernel runs thin) and 1 wave with 4 slots; for 64
+// rows, 2 waves x 2 tiles beat 4 waves x 1 tile and 1 wave x 4 tiles.
 struct MfmaShape {
     int nw;     // waves per (group, head): 1, or the cooperative workgroup
     int nrt;    // row tiles per wave
@@ -159,7 +156,7 @@ MfmaShape mfma_shape(int rt, int head_dim) {
     const int s1 = head_dim == 128 ? 1 : 2;  // a D = 64 slot is half as large
     if (rt == 1) return {1, 1, 2 * s1, 2};
     if (rt == 2) return {1, 2, 2 * s1, 2};
-    return {4, 1, 4 * s1, 3};
+    return {2, 2, 4 * s1, 2};
 }
 int mfma_slot_bytes(int head_dim) {
     return head_dim == 64 ? pa::SlotLayout<_Float16, 64>::kBytes
@@ -371,8 +368,8 @@ void launch_mfma_k(const pa_problem* p, const Plan& pl, size_t lds, hipStream_t 
         hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 2, 2 * S1, 2, APPEND>), grid, dim3(256), lds,
                            s, a, table, a.ap.slots);
     } else {
-        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 4, 1, 4 * S1, 3, APPEND>),
-                           dim3((unsigned)streams), dim3(256), lds, s, a, table, a.ap.slots);
+        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2, 2, 4 * S1, 2, APPEND>),
+                           dim3((unsigned)streams), dim3(128), lds, s, a, table, a.ap.slots);
     }
 }
 

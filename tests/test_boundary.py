@@ -53,7 +53,7 @@ PLAN_TABLE = [
     (0, 100, pa.PA_KERNEL_VALU, 1, 112),
     (1, 4096, pa.PA_KERNEL_MFMA, 256, 48),
     (2, 131072, pa.PA_KERNEL_MFMA, 256, 48),
-    (3, 8192, pa.PA_KERNEL_MFMA, 96, 16 * 33),   # 3 four-wave workgroups per CU / 8 heads
+    (3, 8192, pa.PA_KERNEL_MFMA, 128, 16 * 33),
     (4, 16384, pa.PA_KERNEL_MFMA, 256, 80),
 ]
 
