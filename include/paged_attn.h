@@ -203,6 +203,28 @@ int paged_attn_decode_append(const pa_problem* problem, const void* q, void* k_p
                              void* workspace, size_t workspace_bytes, pa_stream_t stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * paged_attn_decode with the split's partial states kept in a workspace the
+ * library owns, a static device array of PA_STATIC_WORKSPACE_BYTES that each
+ * device holds from the library's load until the process ends. Nothing is
+ * allocated or freed. Arguments, effects and errors as paged_attn_decode
+ * (both kernels always run: PA_FLAG_DEFER_COMBINE is rejected with
+ * PA_ERR_INVALID_ARG), plus PA_ERR_WORKSPACE when the plan needs more than
+ * PA_STATIC_WORKSPACE_BYTES (pa_workspace_size reports what it needs; a
+ * smaller num_partitions or batch lowers it). No initial contents are needed.
+ * Every call on one device shares that device's array: calls that can overlap
+ * on one device (different streams, or different host threads without
+ * ordering) race on it and must not be issued.
+ */
+#define PA_STATIC_WORKSPACE_BYTES ((size_t)32 << 20)
+
+int paged_attn_decode_static(const pa_problem* problem, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* block_table,
+                             const int32_t* context_lens, const void* new_k, const void* new_v,
+                             float scale, void* out, pa_stream_t stream);
+
+/*
  * Merge step alone (page: PARTIALS_REDUCE), as its own kernel. Reads the
  * partial states a partitioned paged_attn_decode left in `workspace` for the
  * same problem and
@@ -291,7 +313,7 @@ int pa_dense_attention_backward(const pa_dense_problem* problem, const void* q, 
 const char* paged_attn_last_error(void);
 
 /* ABI version of this header (major * 100 + minor). */
-int paged_attn_version(void);  /* 104: pa_dense_attention_backward */
+int paged_attn_version(void);  /* 105: paged_attn_decode_static */
 
 #ifdef __cplusplus
 }

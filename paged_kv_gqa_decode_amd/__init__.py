@@ -23,8 +23,11 @@ PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
 PA_FLAG_DEFER_COMBINE = 1
 PA_MASK_NONE, PA_MASK_BOOL, PA_MASK_ADD = 0, 1, 2
 
+PA_STATIC_WORKSPACE_BYTES = 32 << 20
+
 EXPORTED = ("pa_plan_ex", "pa_plan", "pa_workspace_size", "pa_workspace_size_ex",
-            "paged_attn_decode", "paged_attn_decode_append", "paged_attn_combine",
+            "paged_attn_decode", "paged_attn_decode_append", "paged_attn_decode_static",
+            "paged_attn_combine",
             "pa_dense_attention", "pa_dense_backward_workspace_size",
             "pa_dense_attention_backward", "paged_attn_last_error", "paged_attn_version")
 
@@ -78,6 +81,9 @@ def library(path: Optional[str] = None):
     lib.paged_attn_decode_append.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
                                              vp, vp, ctypes.c_size_t, vp]
     lib.paged_attn_decode_append.restype = ctypes.c_int
+    lib.paged_attn_decode_static.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
+                                             vp, vp]
+    lib.paged_attn_decode_static.restype = ctypes.c_int
     lib.paged_attn_combine.argtypes = [P, vp, vp, ctypes.c_size_t, vp, vp]
     lib.pa_dense_attention.argtypes = [ctypes.POINTER(PaDenseProblem), vp, vp, vp, vp,
                                        ctypes.c_float, vp, vp]
@@ -182,6 +188,18 @@ def paged_attn_decode_append(problem: PaProblem, q, k_pool, v_pool, block_table,
         ctypes.byref(problem), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
         _ptr(context_lens), _ptr(new_k), _ptr(new_v), _ptr(slot_mapping), ctypes.c_float(scale),
         _ptr(out), _ptr(workspace), ctypes.c_size_t(workspace_bytes), _stream(stream))
+    if raise_on_error:
+        _check(rc)
+    return rc
+
+
+def paged_attn_decode_static(problem: PaProblem, q, k_pool, v_pool, block_table, context_lens,
+                             new_k, new_v, scale: float, out, stream=None,
+                             raise_on_error: bool = True) -> int:
+    rc = library().paged_attn_decode_static(
+        ctypes.byref(problem), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+        _ptr(context_lens), _ptr(new_k), _ptr(new_v), ctypes.c_float(scale), _ptr(out),
+        _stream(stream))
     if raise_on_error:
         _check(rc)
     return rc

@@ -20,6 +20,13 @@
 #include "decode_valu.hpp"
 #include "dense_bwd.hpp"
 
+// Workspace of paged_attn_decode_static, for callers that cannot allocate:
+// every device the library runs on holds its own copy of this array until the
+// process ends. In host code the name denotes a host-side stand-in, not device
+// memory: the device address comes from hipGetSymbolAddress (scratch_address),
+// and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[PA_STATIC_WORKSPACE_BYTES];
+
 namespace {
 
 thread_local std::string t_error;
@@ -278,12 +285,14 @@ size_t workspace_bytes_for(const pa_problem* p, const Plan& pl) {
     return bytes;
 }
 
-// Per-device property cache (compute units, gfx950 or not), filled once.
+// Per-device property cache (compute units, gfx950 or not), filled once, and
+// the device address of that device's static workspace (set on first use).
 struct DeviceInfo {
     bool known = false;
     bool gfx950 = false;
     int cus = 0;
     char arch[64] = {0};
+    void* scratch = nullptr;
 };
 std::mutex g_device_mutex;
 DeviceInfo g_devices[64];
@@ -310,6 +319,27 @@ int current_device_cus(int* cus) {
         return fail(PA_ERR_DEVICE, "device %d is %s, not gfx950 (MI355X); verify the selected "
                     "device", dev, info.arch);
     *cus = info.cus;
+    return PA_OK;
+}
+
+// Device address of the current device's copy of `scratch`, looked up once per
+// device with that device current (each device holds the array at its own
+// address). Call after current_device_cus has accepted the device.
+int scratch_address(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return fail(PA_ERR_DEVICE, "no usable HIP device for the static workspace");
+    std::lock_guard<std::mutex> lock(g_device_mutex);
+    DeviceInfo& info = g_devices[dev];
+    if (!info.scratch) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(PA_ERR_DEVICE, "cannot locate the static workspace on device %d: %s; "
+                        "verify the HIP runtime", dev, hipGetErrorString(e));
+        info.scratch = p;
+    }
+    *ptr = info.scratch;
     return PA_OK;
 }
 
@@ -930,6 +960,34 @@ int paged_attn_decode_append(const pa_problem* problem, const void* q, void* k_p
                         slot_mapping, scale, out, workspace, workspace_bytes, stream);
 }
 
+int paged_attn_decode_static(const pa_problem* problem, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* block_table,
+                             const int32_t* context_lens, const void* new_k, const void* new_v,
+                             float scale, void* out, pa_stream_t stream) {
+    if (int rc = validate_problem(problem)) return rc;
+    if (problem->flags & PA_FLAG_DEFER_COMBINE)
+        return fail(PA_ERR_INVALID_ARG, "PA_FLAG_DEFER_COMBINE is not accepted by "
+                    "paged_attn_decode_static (its partial states stay in the library's static "
+                    "workspace, which paged_attn_combine cannot be given); verify pa_problem.flags");
+    if (problem->batch == 0) return succeed();
+    int cus = 0;
+    if (int rc = current_device_cus(&cus)) return rc;
+    Plan pl;
+    if (int rc = plan_impl(problem, cus, &pl)) return rc;
+    const size_t need = workspace_bytes_for(problem, pl);
+    if (need > (size_t)PA_STATIC_WORKSPACE_BYTES)
+        return fail(PA_ERR_WORKSPACE, "this plan (%d partitions) needs %zu bytes of workspace, "
+                    "more than the %zu-byte static workspace; call paged_attn_decode with a "
+                    "workspace of pa_workspace_size bytes, or lower num_partitions or the batch",
+                    pl.parts, need, (size_t)PA_STATIC_WORKSPACE_BYTES);
+    void* ws = nullptr;
+    if (need > 0)
+        if (int rc = scratch_address(&ws)) return rc;
+    return decode_entry(problem, q, k_pool, v_pool, block_table, context_lens, new_k, new_v,
+                        nullptr, scale, out, ws, need > 0 ? (size_t)PA_STATIC_WORKSPACE_BYTES : 0,
+                        stream);
+}
+
 int paged_attn_combine(const pa_problem* problem, const int32_t* context_lens,
                        const void* workspace, size_t workspace_bytes, void* out,
                        pa_stream_t stream) {
@@ -964,6 +1022,6 @@ int paged_attn_combine(const pa_problem* problem, const int32_t* context_lens,
 
 const char* paged_attn_last_error(void) { return t_error.c_str(); }
 
-int paged_attn_version(void) { return 104; }
+int paged_attn_version(void) { return 105; }
 
 }  // extern "C"

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(names) == set(pa.EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert pa.paged_attn_version() == 104
+    assert pa.paged_attn_version() == 105
 
 
 def spec_problem(spec: W.Spec, max_ctx: int, **kw) -> pa.PaProblem:
