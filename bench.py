@@ -1,25 +1,30 @@
 #!/usr/bin/env python3
 """Decode-attention benchmark on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config I] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--configs 1,2,3,4] [--headline 4] [--gpus 1]
 
-Workload (default): the Llama-3-8B shaped decode batch (B=32, H=32, KV=8, D=128,
-BLOCK=16, fp16 pools, context lengths uniform in 512..4096, NQ=1), seeded
-synthetic data generated on the GPU. `--config` selects another workload of
-paged_kv_gqa_decode_amd.workloads.CONFIGS (0..4).
+Workloads: the decode configurations of paged_kv_gqa_decode_amd.workloads.CONFIGS
+that the 70 %-of-HBM target covers (1: Llama-3-8B shaped batch, 2: long-context
+split, 3: multi-row causal, 4: ragged serving), seeded synthetic data generated
+on the GPU; the headline is the ragged-serving batch (B=256, H=64, KV=8, D=128,
+BLOCK=32, bf16, lognormal context lengths), the largest of them.
 
-One step = one paged_attn_decode call (every kernel the step needs). W untimed
-steps, then K timed steps back to back, bracketed by torch.cuda.synchronize()
-and by two HIP events on the launch stream. Pools are rotated over `--replicas`
-copies so the working set exceeds the 256 MB Infinity Cache. The dominant
-kernel (pass 1) is then timed alone: K pass-1 launches back to back between
-two HIP events on the same stream (an event between two kernels would add its
-own drain), and the combine the same way.
+One step = one paged_attn_decode call (pass 1 and, for split plans, the
+combine). Per workload: W untimed steps, then `--repeats` regions of K steps
+back to back, each bracketed by torch.cuda.synchronize() and two HIP events on
+the launch stream; the reported time per step is the median over the regions
+(p10 / p90 beside it). Pools are rotated over `--replicas` copies so the
+working set exceeds the 256 MB Infinity Cache. The dominant kernel (pass 1) is
+then timed alone: K pass-1 launches back to back between two HIP events on the
+same stream (an event between two kernels would add its own drain), and the
+combine the same way.
 
 Prints ONE JSON line (stdout):
-  value  = KV GB/s over the timed region, KV bytes = sum_b (L_b + NQ)*KV*D*2*s
+  value  = KV GB/s of the headline workload, KV bytes = sum_b (L_b + NQ)*KV*D*2*s
   roofline.achieved = KV bytes per pass-1 launch / mean pass-1 launch duration
-  cpu_baseline = the oracle (plain C, fp64) on this host's cores, same workload
+  configs = the same figures for every workload measured
+  cpu_baseline = the oracle (plain C, fp64) on this host's cores, a bounded
+                 sample of the headline workload
 """
 import argparse
 import hashlib
@@ -223,20 +228,174 @@ def copy_bandwidth(torch, nbytes=1 << 30, reps=10) -> float:
     return 2 * nbytes / sec / 1e9
 
 
+def measure_workload(torch, pa, W, spec, args, stream, timed):
+    """Every figure of one workload: the step (median of regions), pass 1 and
+    the combine alone, and the slot-patched step against the plain one."""
+    dev = "cuda:0"
+    log(f"[bench] generating {spec.name} on {dev}")
+    w = W.make_workload(spec, device=dev)
+    table = torch.from_numpy(w.block_table).to(dev)
+    lens = torch.from_numpy(w.context_lens).to(dev)
+    kpools = [w.k_pool] + [w.k_pool.clone() for _ in range(args.replicas - 1)]
+    vpools = [w.v_pool] + [w.v_pool.clone() for _ in range(args.replicas - 1)]
+    # the step users make: one paged_attn_decode call (merge included)
+    dec = pa.Decoder(w.q, w.k_pool, table, max_context_len=w.max_context_len, causal=spec.causal,
+                     num_partitions=args.partitions, kernel=args.kernel)
+    # the same plan with the merge left to the caller, to time the two kernels apart
+    dec_d = pa.Decoder(w.q, w.k_pool, table, max_context_len=w.max_context_len,
+                       causal=spec.causal, num_partitions=args.partitions, kernel=args.kernel,
+                       flags=pa.PA_FLAG_DEFER_COMBINE)
+    kvb = W.kv_bytes(w)
+    two = dec.partitions > 1
+    kname = KERNEL_NAMES.get(dec.kernel, dec.kernel)
+    log(f"[bench] {spec.name}: kv bytes/step {kvb}, partitions {dec.partitions}, chunk "
+        f"{dec.chunk_tokens}, kernel {kname}, workspace {dec.workspace_bytes} B")
+
+    def step(i):
+        r = i % len(kpools)
+        dec(w.q, kpools[r], vpools[r], table, lens, w.new_k, w.new_v, w.scale, stream=stream,
+            check=False)
+
+    def pass1(i):
+        r = i % len(kpools)
+        dec_d(w.q, kpools[r], vpools[r], table, lens, w.new_k, w.new_v, w.scale, stream=stream,
+              check=False)
+
+    def combine(i):
+        pa.paged_attn_combine(dec_d.problem, lens, dec_d.workspace, dec_d.workspace_bytes,
+                              dec_d.out, stream=stream)
+
+    # the tensors are checked once here; the timed loops call with check=False
+    for r in range(len(kpools)):
+        pa.check_decode_args(w.q, kpools[r], vpools[r], table, lens, w.new_k, w.new_v, dec.out)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    regions = [timed(step, K) * 1e3 for _ in range(max(1, args.repeats))]
+    wall = time.perf_counter() - t0
+    srt = sorted(regions)
+    us = statistics.median(regions)
+    mean_pass1 = timed(pass1, K) * 1e3
+    mean_comb = timed(combine, K) * 1e3 if two else 0.0
+    gbps = kvb / (us / 1e6) / 1e9
+    achieved = kvb / (mean_pass1 / 1e6) / 1e9
+    log(f"[bench] {spec.name}: {us:.2f} us/step (median of {len(regions)} regions of {K}), "
+        f"{gbps:.1f} GB/s ({gbps / HBM_PEAK_GBPS:.1%}); pass 1 {mean_pass1:.2f} us "
+        f"({achieved / HBM_PEAK_GBPS:.1%}), combine {mean_comb:.2f} us; wall "
+        f"{wall / K / len(regions) * 1e6:.2f} us/step")
+    res = {
+        "us_per_step": round(us, 2),
+        "p10_us_per_step": round(percentile(srt, 10), 2),
+        "p90_us_per_step": round(percentile(srt, 90), 2),
+        "region_us_per_step": [round(x, 2) for x in regions],
+        "kv_bytes_per_step": kvb,
+        "kv_gbps": round(gbps, 2),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "config": {
+            "workload": spec.name,
+            "batch": spec.B, "num_heads": spec.H, "num_kv_heads": spec.KV, "head_dim": spec.D,
+            "block_size": spec.BS, "nq": spec.NQ, "causal": spec.causal, "io_dtype": spec.dtype,
+            "context_lens": list(spec.lengths), "kv_bytes_per_step": kvb, "accumulate": "f32",
+            "partitions": dec.partitions, "chunk_tokens": dec.chunk_tokens, "kernel": kname,
+            "pool_replicas": len(kpools), "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(spec.name, kvb),
+            "kernel": f"pass 1 ({kname} decode kernel), timed alone: {K} launches back to back "
+                      f"between two HIP events",
+            "mean_launch_us": round(mean_pass1, 3),
+            "algorithmic_bytes_per_launch": kvb,
+            "combine_mean_us": round(mean_comb, 3),
+        },
+    }
+    if not args.lean:
+        res["append_step"] = append_step(torch, pa, spec, w, table, lens, kpools, vpools, args,
+                                         stream, timed, step, kvb)
+    del kpools, vpools, dec, dec_d, w
+    torch.cuda.empty_cache()
+    return res
+
+
+def append_step(torch, pa, spec, w, table, lens, kpools, vpools, args, stream, timed, step, kvb):
+    """The slot-patched step (paged_attn_decode_append): the same step also
+    storing every new row into a spare slot past the cached blocks (the pools
+    get ceil(B*NQ/BS) extra blocks; nothing cached is overwritten, so no read
+    is patched): what the store and the per-sub-page slot checks cost, against
+    the plain step on the same extended pools."""
+    dev = "cuda:0"
+    spare = -(-(spec.B * spec.NQ) // spec.BS)
+    nb = kpools[0].shape[0]
+    kx = [torch.cat([p, p.new_zeros((spare,) + tuple(p.shape[1:]))]) for p in kpools]
+    vx = [torch.cat([p, p.new_zeros((spare,) + tuple(p.shape[1:]))]) for p in vpools]
+    flat = torch.arange(spec.B * spec.NQ, device=dev, dtype=torch.int64)
+    slots = ((nb + flat // spec.BS) * spec.BS + flat % spec.BS).to(torch.int32).view(spec.B, spec.NQ)
+    dec_a = pa.Decoder(w.q, kx[0], table, max_context_len=w.max_context_len, causal=spec.causal,
+                       num_partitions=args.partitions, kernel=args.kernel)
+
+    def step_append(i):
+        r = i % len(kx)
+        dec_a(w.q, kx[r], vx[r], table, lens, w.new_k, w.new_v, w.scale, stream=stream,
+              slot_mapping=slots, check=False)
+
+    def step_plain(i):
+        r = i % len(kx)
+        dec_a(w.q, kx[r], vx[r], table, lens, w.new_k, w.new_v, w.scale, stream=stream,
+              check=False)
+
+    for r in range(len(kx)):
+        pa.check_decode_args(w.q, kx[r], vx[r], table, lens, w.new_k, w.new_v, dec_a.out, slots)
+    for i in range(args.warmup):
+        step_append(i)
+    K = args.steps
+    app, plain = [], []
+    for _ in range(3):  # interleaved, so that clock drift hits both alike
+        app.append(timed(step_append, K) * 1e3)
+        plain.append(timed(step_plain, K) * 1e3)
+    ua, up = statistics.median(app), statistics.median(plain)
+    elem = 4 if spec.dtype == "f32" else 2
+    stored = spec.B * spec.NQ * spec.KV * spec.D * 2 * elem
+    log(f"[bench] {spec.name}: slot-patched step {ua:.2f} us/step, plain step on the same pools "
+        f"{up:.2f} us/step ({(ua / up - 1):+.1%})")
+    del kx, vx, dec_a
+    return {
+        "entry_point": "paged_attn_decode_append",
+        "us_per_step": round(ua, 2),
+        "plain_step_same_pools_us": round(up, 2),
+        "overhead_frac": round(ua / up - 1, 4),
+        "kv_gbps": round(kvb / (ua / 1e6) / 1e9, 2),
+        "stored_bytes_per_step": stored,
+        "slots": "every new row into a spare slot past the cached blocks (no read patched)",
+        "timing": "median of 3 regions of K steps each, interleaved with the plain step",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--repeats", type=int, default=5,
-                    help="extra timed regions of K steps after the headline one, for the "
-                         "median / p10 / p90 of the per-step time")
-    ap.add_argument("--config", type=int, default=1)
+                    help="timed regions of K steps per workload; the reported time per step is "
+                         "their median")
+    ap.add_argument("--configs", default="1,2,3,4",
+                    help="comma-separated workload indices of CONFIGS, measured in this order")
+    ap.add_argument("--headline", type=int, default=4,
+                    help="workload whose figures are the line's value / roofline")
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 valu, 2 mfma")
     ap.add_argument("--partitions", type=int, default=0, help="0 = launch heuristic")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lean", action="store_true",
+                    help="decode steps, pass 1 and the combine only (for profiler runs): no "
+                         "slot-patched step, dense legs, copy bandwidth or CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run device-to-device copies of a known size (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters of a profiler run)")
@@ -264,38 +423,11 @@ def main():
     import paged_kv_gqa_decode_amd as pa
     from paged_kv_gqa_decode_amd import workloads as W
 
-    spec = W.CONFIGS[args.config]
-    dev = "cuda:0"
+    order = [int(x) for x in args.configs.split(",") if x.strip()]
+    if args.headline not in order:
+        order.append(args.headline)
     torch.cuda.set_device(0)
-    log(f"[bench] generating {spec.name} on {dev}")
-    w = W.make_workload(spec, device=dev)
-    table = torch.from_numpy(w.block_table).to(dev)
-    lens = torch.from_numpy(w.context_lens).to(dev)
-    kpools = [w.k_pool] + [w.k_pool.clone() for _ in range(args.replicas - 1)]
-    vpools = [w.v_pool] + [w.v_pool.clone() for _ in range(args.replicas - 1)]
-    # The combine is enqueued by the bench itself (PA_FLAG_DEFER_COMBINE) so that
-    # HIP events can bracket pass 1 and the combine separately; the step is the same.
-    dec = pa.Decoder(w.q, w.k_pool, table, max_context_len=w.max_context_len, causal=spec.causal,
-                     num_partitions=args.partitions, kernel=args.kernel,
-                     flags=pa.PA_FLAG_DEFER_COMBINE)
     stream = torch.cuda.current_stream()
-    kvb = W.kv_bytes(w)
-    two = dec.partitions > 1
-    log(f"[bench] kv bytes/step {kvb}, partitions {dec.partitions}, chunk {dec.chunk_tokens}, "
-        f"kernel {KERNEL_NAMES.get(dec.kernel, dec.kernel)}, workspace {dec.workspace_bytes} B")
-
-    def pass1(i):
-        r = i % len(kpools)
-        dec(w.q, kpools[r], vpools[r], table, lens, w.new_k, w.new_v, w.scale, stream=stream)
-
-    def combine():
-        pa.paged_attn_combine(dec.problem, lens, dec.workspace, dec.workspace_bytes, dec.out,
-                              stream=stream)
-
-    def step(i):
-        pass1(i)
-        if two:
-            combine()
 
     def timed(fn, count):
         """Mean ms per call of `count` calls of fn issued back to back between two
@@ -309,121 +441,59 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / count
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    K = args.steps
-    # Timed region: K steps back to back, HIP events only at its two ends.
-    t0 = time.perf_counter()
-    ms_per_step = timed(step, K)
-    wall = time.perf_counter() - t0
-    # Spread: further regions of K steps, each between its own two events.
-    reps = sorted(timed(step, K) * 1e3 for _ in range(args.repeats))
-    # The dominant kernel alone, then the combine alone (same stream, same inputs).
-    mean_pass1 = timed(pass1, K)
-    mean_comb = timed(lambda i: combine(), K) if two else 0.0
-    value = kvb / (ms_per_step / 1e3) / 1e9
-    achieved = kvb / (mean_pass1 / 1e3) / 1e9
-    log(f"[bench] {ms_per_step * 1e3:.2f} us/step (region), pass 1 {mean_pass1 * 1e3:.2f} us, "
-        f"combine {mean_comb * 1e3:.2f} us, wall {wall / K * 1e6:.2f} us/step, {value:.1f} GB/s")
+    results = {}
+    for c in order:
+        results[W.CONFIGS[c].name] = measure_workload(torch, pa, W, W.CONFIGS[c], args, stream,
+                                                      timed)
+    spec = W.CONFIGS[args.headline]
+    head = results[spec.name]
 
-    # The slot-patched step (paged_attn_decode_append): the same step also
-    # storing every new row into a spare slot past the cached blocks (the pools
-    # get ceil(B*NQ/BS) extra blocks; nothing cached is overwritten, so no read
-    # is patched): what the store and the per-sub-page slot checks cost.
-    spare = -(-(spec.B * spec.NQ) // spec.BS)
-    nb = kpools[0].shape[0]
-    kpools = [torch.cat([p, p.new_zeros((spare,) + tuple(p.shape[1:]))]) for p in kpools]
-    vpools = [torch.cat([p, p.new_zeros((spare,) + tuple(p.shape[1:]))]) for p in vpools]
-    flat = torch.arange(spec.B * spec.NQ, device=dev, dtype=torch.int64)
-    slots = ((nb + flat // spec.BS) * spec.BS + flat % spec.BS).to(torch.int32).view(spec.B, spec.NQ)
-    dec_a = pa.Decoder(w.q, kpools[0], table, max_context_len=w.max_context_len,
-                       causal=spec.causal, num_partitions=args.partitions, kernel=args.kernel)
-
-    def step_append(i):
-        r = i % len(kpools)
-        dec_a(w.q, kpools[r], vpools[r], table, lens, w.new_k, w.new_v, w.scale, stream=stream,
-              slot_mapping=slots)
-
-    for i in range(args.warmup):
-        step_append(i)
-    ms_append = timed(step_append, K)
-    ms_plain_ext = timed(step, K)  # the plain step on the same (extended) pools
-    elem = 4 if spec.dtype == "f32" else 2
-    stored = spec.B * spec.NQ * spec.KV * spec.D * 2 * elem
-    log(f"[bench] slot-patched step {ms_append * 1e3:.2f} us/step "
-        f"({kvb / (ms_append / 1e3) / 1e9:.1f} GB/s of KV reads, {stored} B stored); "
-        f"plain step on the same pools {ms_plain_ext * 1e3:.2f} us/step")
-
-    dense = dense_prefill(torch, pa, timed, args.warmup)
-    dense_bwd = dense_backward(torch, pa, timed, args.warmup)
-
-    copy_gbps = copy_bandwidth(torch)
-    log(f"[bench] device copy bandwidth {copy_gbps:.0f} GB/s (read+write)")
-    traffic = measured_traffic(spec.name, kvb)
+    extra = {}
+    if not args.lean:
+        extra["dense_prefill"] = dense_prefill(torch, pa, timed, args.warmup)
+        extra["dense_backward"] = dense_backward(torch, pa, timed, args.warmup)
+        copy_gbps = copy_bandwidth(torch)
+        log(f"[bench] device copy bandwidth {copy_gbps:.0f} GB/s (read+write)")
+        extra["device_copy_gbps"] = round(copy_gbps, 1)
 
     cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] timing the oracle on the host")
+    if not args.no_cpu_baseline and not args.lean:
+        log(f"[bench] timing the oracle on the host ({spec.name})")
+        w = W.make_workload(spec, device="cuda:0")
         cpu = cpu_baseline(w, args.cpu_seconds)
+        del w
         log(f"[bench] oracle {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
 
     result = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["kv_gbps"],
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "us_per_step": round(ms_per_step * 1e3, 2),
-        "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
+        "ms_per_step": round(head["us_per_step"] / 1e3, 5),
+        "us_per_step": head["us_per_step"],
+        "hbm_frac": head["hbm_frac"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": spec.dtype,
         "data": "synthetic",
-        "config": {
-            "workload": spec.name,
-            "batch": spec.B, "num_heads": spec.H, "num_kv_heads": spec.KV, "head_dim": spec.D,
-            "block_size": spec.BS, "nq": spec.NQ, "causal": spec.causal, "io_dtype": spec.dtype,
-            "context_lens": list(spec.lengths), "kv_bytes_per_step": kvb,
-            "accumulate": "f32",
-            "partitions": dec.partitions, "chunk_tokens": dec.chunk_tokens,
-            "kernel": KERNEL_NAMES.get(dec.kernel, dec.kernel), "pool_replicas": len(kpools),
-            "parallelism": "single GPU",
+        "config": head["config"],
+        "timing": {
+            "statistic": f"median over {len(head['region_us_per_step'])} timed regions of "
+                         f"{args.steps} steps each (one paged_attn_decode call per step)",
+            "p10_us_per_step": head["p10_us_per_step"],
+            "p90_us_per_step": head["p90_us_per_step"],
+            "region_us_per_step": head["region_us_per_step"],
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "kernel": f"pass 1 ({KERNEL_NAMES.get(dec.kernel, dec.kernel)} decode kernel), timed "
-                      f"alone: {K} launches back to back between two HIP events",
-            "mean_launch_us": round(mean_pass1 * 1e3, 3),
-            "algorithmic_bytes_per_launch": kvb,
-            "combine_mean_us": round(mean_comb * 1e3, 3) if two else 0.0,
-        },
-        "step_repeats": {
-            "regions": len(reps), "steps_each": K,
-            "median_us_per_step": round(statistics.median(reps), 2) if reps else None,
-            "p10_us_per_step": round(percentile(reps, 10), 2) if reps else None,
-            "p90_us_per_step": round(percentile(reps, 90), 2) if reps else None,
-        },
-        "append_step": {
-            "entry_point": "paged_attn_decode_append",
-            "us_per_step": round(ms_append * 1e3, 2),
-            "plain_step_same_pools_us": round(ms_plain_ext * 1e3, 2),
-            "kv_gbps": round(kvb / (ms_append / 1e3) / 1e9, 2),
-            "stored_bytes_per_step": stored,
-            "slots": "every new row into a spare slot past the cached blocks (no read patched)",
-        },
-        "dense_prefill": dense,
-        "dense_backward": dense_bwd,
-        "device_copy_gbps": round(copy_gbps, 1),
+        "roofline": head["roofline"],
         "cpu_baseline": cpu,
+        "configs": {
+            name: {k: v for k, v in r.items() if k not in ("region_us_per_step",)}
+            for name, r in results.items()
+        },
+        **extra,
     }
     print(json.dumps(result), flush=True)
 

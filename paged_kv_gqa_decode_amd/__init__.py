@@ -255,18 +255,74 @@ def paged_attn_version() -> int:
 # ---------------------------------------------------------------------------
 def _dtype_code(t) -> int:
     import torch
-    return {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}[t.dtype]
+    code = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}.get(t.dtype)
+    if code is None:
+        raise TypeError(f"dtype {t.dtype} is not supported (float32, float16 or bfloat16)")
+    return code
+
+
+def _expect(t, name: str, shape, dtype, device):
+    """Raise unless t is a contiguous tensor of that shape, dtype and device (the
+    C ABI reads raw pointers, so a wrong dtype, a strided view or a host tensor
+    would be read as something else without any error)."""
+    if t is None:
+        raise ValueError(f"{name} is missing")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device} (the other tensors' device)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} is not contiguous (strides {t.stride()}); pass .contiguous()")
+
+
+def check_decode_args(q, k_pool, v_pool, block_table, context_lens, new_k, new_v, out=None,
+                      slot_mapping=None):
+    """Shapes, dtypes, devices and contiguity of one decode step's tensors:
+    q, out [B, H, NQ, D]; k_pool, v_pool [num_blocks, BS, KV, D] (q's dtype);
+    block_table int32 [B, max_blocks_per_seq]; context_lens int32 [B]; new_k,
+    new_v [B, KV, NQ, D]; slot_mapping int32 [B, NQ]; all on q's device."""
+    import torch
+    if q is None or q.dim() != 4:
+        raise ValueError("q must be a 4-D tensor [B, H, NQ, D]")
+    if k_pool is None or k_pool.dim() != 4:
+        raise ValueError("k_pool must be a 4-D tensor [num_blocks, BS, KV, D]")
+    B, H, NQ, D = q.shape
+    dt, dev = q.dtype, q.device
+    _dtype_code(q)
+    KV = k_pool.shape[2]
+    _expect(q, "q", (B, H, NQ, D), dt, dev)
+    _expect(k_pool, "k_pool", (k_pool.shape[0], k_pool.shape[1], KV, D), dt, dev)
+    _expect(v_pool, "v_pool", tuple(k_pool.shape), dt, dev)
+    if block_table is None or block_table.dim() != 2:
+        raise ValueError("block_table must be a 2-D int32 tensor [B, max_blocks_per_seq]")
+    _expect(block_table, "block_table", (B, block_table.shape[1]), torch.int32, dev)
+    _expect(context_lens, "context_lens", (B,), torch.int32, dev)
+    _expect(new_k, "new_k", (B, KV, NQ, D), dt, dev)
+    _expect(new_v, "new_v", (B, KV, NQ, D), dt, dev)
+    if out is not None:
+        _expect(out, "out", (B, H, NQ, D), dt, dev)
+    if slot_mapping is not None:
+        _expect(slot_mapping, "slot_mapping", (B, NQ), torch.int32, dev)
 
 
 def make_problem(q, k_pool, block_table, *, max_context_len: int, causal: bool = True,
                  num_partitions: int = 0, kernel: int = PA_KERNEL_AUTO,
                  flags: int = 0) -> PaProblem:
+    if q.dim() != 4 or k_pool.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("q [B, H, NQ, D], k_pool [num_blocks, BS, KV, D] and block_table "
+                         "[B, max_blocks_per_seq] must be 4-, 4- and 2-D")
     B, H, NQ, D = q.shape
     NB, BS, KV, D2 = k_pool.shape
-    assert D == D2, "head_dim of q and the pools differ"
+    if D != D2 or k_pool.dtype != q.dtype:
+        raise ValueError(f"q ({q.dtype}, head_dim {D}) and k_pool ({k_pool.dtype}, head_dim "
+                         f"{D2}) differ")
+    if block_table.shape[0] != B:
+        raise ValueError(f"block_table has {block_table.shape[0]} rows for a batch of {B}")
     return PaProblem(batch=B, num_heads=H, num_kv_heads=KV, head_dim=D, block_size=BS,
-                     num_blocks=NB, max_blocks_per_seq=block_table.shape[1] if block_table.dim() == 2 else 0,
-                     nq=NQ, causal=int(causal), dtype=_dtype_code(q),
+                     num_blocks=NB, max_blocks_per_seq=block_table.shape[1], nq=NQ,
+                     causal=int(causal), dtype=_dtype_code(q),
                      max_context_len=int(max_context_len), num_partitions=int(num_partitions),
                      kernel=int(kernel), flags=int(flags))
 
@@ -288,20 +344,30 @@ class Decoder:
                           if self.workspace_bytes else None)
         self.out = torch.empty_like(q)
 
+    def _check_problem(self, q, k_pool, block_table):
+        p = self.problem
+        if (tuple(q.shape) != (p.batch, p.num_heads, p.nq, p.head_dim)
+                or tuple(k_pool.shape) != (p.num_blocks, p.block_size, p.num_kv_heads, p.head_dim)
+                or tuple(block_table.shape) != (p.batch, p.max_blocks_per_seq)):
+            raise ValueError("the tensors' shapes differ from the ones this Decoder was built for")
+
     def __call__(self, q, k_pool, v_pool, block_table, context_lens, new_k, new_v, scale,
-                 out=None, stream=None, slot_mapping=None):
+                 out=None, stream=None, slot_mapping=None, check: bool = True):
         """One step; with slot_mapping (int32 [B, NQ]) the slot-patched step that
-        also stores the new rows into the pools."""
+        also stores the new rows into the pools. check=False skips the tensor
+        checks (for a loop over tensors already checked once)."""
         import torch
         out = self.out if out is None else out
+        if check:
+            check_decode_args(q, k_pool, v_pool, block_table, context_lens, new_k, new_v, out,
+                              slot_mapping)
+            self._check_problem(q, k_pool, block_table)
         if stream is None:
             stream = torch.cuda.current_stream()
         if slot_mapping is None:
             paged_attn_decode(self.problem, q, k_pool, v_pool, block_table, context_lens, new_k,
                               new_v, scale, out, self.workspace, self.workspace_bytes, stream)
         else:
-            assert slot_mapping.dtype == torch.int32 and slot_mapping.is_contiguous()
-            assert tuple(slot_mapping.shape) == (q.shape[0], q.shape[2])
             paged_attn_decode_append(self.problem, q, k_pool, v_pool, block_table, context_lens,
                                      new_k, new_v, slot_mapping, scale, out, self.workspace,
                                      self.workspace_bytes, stream)
@@ -312,20 +378,51 @@ def decode(q, k_pool, v_pool, block_table, context_lens, new_k, new_v, scale: fl
            max_context_len: int, causal: bool = True, num_partitions: int = 0,
            kernel: int = PA_KERNEL_AUTO, out=None, stream=None):
     """One decode-attention step; returns out [B, H, NQ, D] in q's dtype."""
+    check_decode_args(q, k_pool, v_pool, block_table, context_lens, new_k, new_v, out)
     dec = Decoder(q, k_pool, block_table, max_context_len=max_context_len, causal=causal,
                   num_partitions=num_partitions, kernel=kernel)
     return dec(q, k_pool, v_pool, block_table, context_lens, new_k, new_v, scale, out=out,
-               stream=stream)
+               stream=stream, check=False)
 
 
 def decode_append(q, k_pool, v_pool, block_table, context_lens, new_k, new_v, slot_mapping,
                   scale: float, *, max_context_len: int, causal: bool = True,
                   num_partitions: int = 0, kernel: int = PA_KERNEL_AUTO, out=None, stream=None):
     """The slot-patched step: returns out and stores the new rows into k_pool/v_pool."""
+    check_decode_args(q, k_pool, v_pool, block_table, context_lens, new_k, new_v, out,
+                      slot_mapping)
     dec = Decoder(q, k_pool, block_table, max_context_len=max_context_len, causal=causal,
                   num_partitions=num_partitions, kernel=kernel)
     return dec(q, k_pool, v_pool, block_table, context_lens, new_k, new_v, scale, out=out,
-               stream=stream, slot_mapping=slot_mapping)
+               stream=stream, slot_mapping=slot_mapping, check=False)
+
+
+def check_dense_args(q, k, v, mask=None, dout=None, out=None):
+    """q, out, dout [B, HQ, SQ, D]; k, v [B, HK, SK, D]; same dtype (fp16 or bf16)
+    and device, contiguous; mask 4-D [mb, mh, mq, mw] on that device, each dim 1
+    or the full size (mw up to SK), uint8/bool or float32, contiguous."""
+    import torch
+    if q is None or k is None or q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q [B, HQ, SQ, D] and k [B, HK, SK, D] must be 4-D tensors")
+    B, HQ, SQ, D = q.shape
+    _, HK, SK, _ = k.shape
+    dt, dev = q.dtype, q.device
+    if dt not in (torch.float16, torch.bfloat16):
+        raise TypeError(f"dense attention takes float16 or bfloat16, not {dt}")
+    _expect(q, "q", (B, HQ, SQ, D), dt, dev)
+    _expect(k, "k", (B, HK, SK, D), dt, dev)
+    _expect(v, "v", (B, HK, SK, D), dt, dev)
+    if dout is not None:
+        _expect(dout, "dout", (B, HQ, SQ, D), dt, dev)
+    if out is not None:
+        _expect(out, "out", (B, HQ, SQ, D), dt, dev)
+    if mask is not None:
+        if mask.dim() != 4:
+            raise ValueError("mask must be 4-D [mb, mh, mq, mw]")
+        if mask.dtype not in (torch.bool, torch.uint8, torch.float32):
+            raise TypeError(f"mask dtype {mask.dtype}: bool/uint8 (visible) or float32 (bias)")
+        if mask.device != dev or not mask.is_contiguous():
+            raise ValueError("mask must be contiguous and on q's device")
 
 
 def make_dense_problem(q, k, *, causal: bool = False, mask=None) -> PaDenseProblem:
@@ -350,6 +447,7 @@ def dense_attention(q, k, v, scale: float, *, mask=None, causal: bool = False, o
     if mask is not None:
         mask = mask.to(torch.uint8) if mask.dtype == torch.bool else mask.to(torch.float32)
         mask = mask.contiguous()
+    check_dense_args(q, k, v, mask, out=out)
     prob = make_dense_problem(q, k, causal=causal, mask=mask)
     out = torch.empty_like(q) if out is None else out
     if stream is None:
@@ -368,6 +466,7 @@ def dense_attention_backward(q, k, v, dout, scale: float, *, mask=None, causal: 
     if mask is not None:
         mask = mask.to(torch.uint8) if mask.dtype == torch.bool else mask.to(torch.float32)
         mask = mask.contiguous()
+    check_dense_args(q, k, v, mask, dout=dout)
     prob = make_dense_problem(q, k, causal=causal, mask=mask)
     _, need = pa_dense_backward_workspace_size(prob)
     if workspace is None:

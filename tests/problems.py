@@ -237,3 +237,36 @@ def staircase_decode(w: W.Workload, jumps_per_seq, seed=0) -> W.Workload:
                  + 0.05 * torch.randn(s.KV, s.NQ, s.D, generator=g)).to(dt)
     return W.Workload(s, w.context_lens, w.block_table, w.num_blocks, q, kp, w.v_pool, nk,
                       w.new_v, float(np.float32(1.0 / np.sqrt(s.D))))
+
+
+# ---------------------------------------------------------------------------
+# Argmax probe: one cached key per sequence dominates every query row
+# ---------------------------------------------------------------------------
+def argmax_probe(w: W.Workload, ts, lead: float = 12.0, seed: int = 0):
+    """Inputs where logical position ts[b] of sequence b wins every row by far.
+
+    Each KV head kh gets a direction u_kh in {-1, 1}^D; every query row of the
+    heads that read kh is u_kh, and the key at position ts[b] of head kh is
+    lead * u_kh, so its score is lead * D * scale (D = 128, scale 1/sqrt(D):
+    about 136 natural-log units for lead 12, 196 in log2 units) while the other
+    keys, N(0, 1), score a few units: every other softmax weight is below
+    2^-150, which is 0 in binary32. Returns (workload, expect) with expect[b]
+    [H, NQ, D] = the stored v row of position ts[b] for each head's KV head,
+    in the I/O dtype (what an exact argmax returns)."""
+    s = w.spec
+    G = s.H // s.KV
+    g = torch.Generator().manual_seed(seed)
+    u = torch.where(torch.rand(s.KV, s.D, generator=g) < 0.5, -1.0, 1.0)
+    q = u.repeat_interleave(G, dim=0)[None, :, None, :].expand(s.B, s.H, s.NQ, s.D)
+    q = q.to(w.q.dtype).contiguous()
+    kp = w.k_pool.clone()
+    expect = []
+    for b, t in enumerate(ts):
+        assert 0 <= t < int(w.context_lens[b])
+        phys = int(w.block_table[b, t // s.BS])
+        kp[phys, t % s.BS] = (lead * u).to(kp.dtype)
+        vrow = w.v_pool[phys, t % s.BS]                       # [KV, D]
+        expect.append(vrow.repeat_interleave(G, dim=0)[:, None, :].expand(s.H, s.NQ, s.D).clone())
+    w2 = W.Workload(s, w.context_lens, w.block_table, w.num_blocks, q, kp, w.v_pool, w.new_k,
+                    w.new_v, float(np.float32(1.0 / np.sqrt(s.D))))
+    return w2, expect

@@ -253,3 +253,100 @@ def test_dense_backward_empty_problem_is_a_no_op(lib):
     for kw in (dict(batch=0), dict(q_len=0, kv_len=0)):
         assert pa.pa_dense_attention_backward(_dense_problem(**kw), None, None, None, None, None,
                                               0.1, None, None, None, None, 0) == 0
+
+
+# ---------------------------------------------------------------------------
+# Torch layer: tensors the C ABI would misread are rejected before any call
+# ---------------------------------------------------------------------------
+def _decode_tensors(dtype=None, B=2, H=8, KV=2, NQ=3, D=64, NB=5, BS=16, MB=4):
+    import torch
+    dtype = dtype or torch.float16
+    g = torch.Generator().manual_seed(0)
+    t = dict(
+        q=torch.randn(B, H, NQ, D, generator=g).to(dtype),
+        k_pool=torch.randn(NB, BS, KV, D, generator=g).to(dtype),
+        v_pool=torch.randn(NB, BS, KV, D, generator=g).to(dtype),
+        block_table=torch.zeros(B, MB, dtype=torch.int32),
+        context_lens=torch.tensor([5, 17], dtype=torch.int32),
+        new_k=torch.randn(B, KV, NQ, D, generator=g).to(dtype),
+        new_v=torch.randn(B, KV, NQ, D, generator=g).to(dtype),
+    )
+    return t
+
+
+def test_torch_layer_accepts_well_formed_tensors():
+    import torch
+    t = _decode_tensors()
+    pa.check_decode_args(**t, out=torch.empty_like(t["q"]),
+                         slot_mapping=torch.zeros(2, 3, dtype=torch.int32))
+    prob = pa.make_problem(t["q"], t["k_pool"], t["block_table"], max_context_len=17)
+    assert (prob.batch, prob.num_heads, prob.nq, prob.num_kv_heads, prob.max_blocks_per_seq) == \
+        (2, 8, 3, 2, 4)
+
+
+@pytest.mark.parametrize("what", [
+    "table_int64", "lens_int64", "q_transposed", "pool_dtype", "new_k_shape", "lens_shape",
+    "out_dtype", "slots_int64", "q_float64", "table_1d", "v_pool_shape", "new_v_strided",
+])
+def test_torch_layer_rejects_misread_tensors(what):
+    import torch
+    t = _decode_tensors()
+    extra = {}
+    if what == "table_int64":
+        t["block_table"] = t["block_table"].long()
+    elif what == "lens_int64":
+        t["context_lens"] = t["context_lens"].long()
+    elif what == "q_transposed":
+        t["q"] = t["q"].transpose(1, 2).contiguous().transpose(1, 2)  # same shape, strided
+    elif what == "pool_dtype":
+        t["k_pool"] = t["k_pool"].bfloat16()
+    elif what == "new_k_shape":
+        t["new_k"] = t["new_k"][:, :, :2].contiguous()
+    elif what == "lens_shape":
+        t["context_lens"] = torch.zeros(3, dtype=torch.int32)
+    elif what == "out_dtype":
+        extra["out"] = torch.empty_like(t["q"]).float()
+    elif what == "slots_int64":
+        extra["slot_mapping"] = torch.zeros(2, 3, dtype=torch.int64)
+    elif what == "q_float64":
+        t["q"] = t["q"].double()
+    elif what == "table_1d":
+        t["block_table"] = t["block_table"].flatten()
+    elif what == "v_pool_shape":
+        t["v_pool"] = t["v_pool"][:4].contiguous()
+    elif what == "new_v_strided":
+        t["new_v"] = torch.randn(2, 2, 64, 3).to(torch.float16).transpose(2, 3)
+    with pytest.raises((ValueError, TypeError)):
+        pa.check_decode_args(**t, **extra)
+    if "out" not in extra and "slot_mapping" not in extra:
+        # decode() checks before it plans or launches anything
+        with pytest.raises((ValueError, TypeError)):
+            pa.decode(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["context_lens"],
+                      t["new_k"], t["new_v"], 0.1, max_context_len=17)
+
+
+@pytest.mark.parametrize("what", ["k_dtype", "v_shape", "q_strided", "dout_shape", "mask_3d",
+                                  "mask_int32", "fp32"])
+def test_torch_layer_rejects_misread_dense_tensors(what):
+    import torch
+    g = torch.Generator().manual_seed(1)
+    q = torch.randn(1, 4, 10, 64, generator=g).half()
+    k = torch.randn(1, 2, 12, 64, generator=g).half()
+    v = torch.randn(1, 2, 12, 64, generator=g).half()
+    dout, mask = None, None
+    if what == "k_dtype":
+        k = k.bfloat16()
+    elif what == "v_shape":
+        v = v[:, :, :11].contiguous()
+    elif what == "q_strided":
+        q = torch.randn(1, 10, 4, 64, generator=g).half().transpose(1, 2)
+    elif what == "dout_shape":
+        dout = torch.randn(1, 4, 9, 64, generator=g).half()
+    elif what == "mask_3d":
+        mask = torch.ones(1, 10, 12, dtype=torch.bool)
+    elif what == "mask_int32":
+        mask = torch.ones(1, 1, 10, 12, dtype=torch.int32)
+    elif what == "fp32":
+        q, k, v = q.float(), k.float(), v.float()
+    with pytest.raises((ValueError, TypeError)):
+        pa.check_dense_args(q, k, v, mask, dout=dout)

@@ -141,6 +141,11 @@ GEOMETRIES = [
     (1, 32, 2, 128, 16, 8, True, "bf16", (500,)),      # 128 rows per KV head
     (2, 4, 2, 64, 16, 2, True, "f32", (129, 1)),
     (2, 4, 2, 128, 32, 1, True, "f32", (700, 64)),
+    # more than 16 new rows: the new rows span two sub-pages, and rows below
+    # the second one's first row see none of its keys (causal limit <= 0)
+    (2, 4, 4, 128, 16, 32, True, "f16", (0, 77)),      # MHA, NQ = 32: two row tiles
+    (2, 8, 4, 64, 32, 20, True, "bf16", (45, 300)),    # G = 2, NQ = 20: cooperative kernel
+    (2, 4, 2, 128, 16, 24, False, "f16", (19, 130)),   # G = 2, NQ = 24, non-causal
 ]
 
 
@@ -178,6 +183,8 @@ APPEND_GPU = [
     (2, 16, 2, 64, 32, 3, True, "bf16", (40, 250), pa.PA_KERNEL_MFMA),      # 24 rows, D=64, BS=32
     (2, 4, 2, 64, 16, 2, True, "f32", (129, 1), pa.PA_KERNEL_AUTO),         # fp32: vector ALU
     (2, 8, 2, 128, 32, 3, False, "f16", (31, 64), pa.PA_KERNEL_VALU),       # forced vector ALU
+    (2, 4, 4, 128, 16, 32, True, "f16", (3, 77), pa.PA_KERNEL_MFMA),       # NQ = 32: two sub-pages
+    (2, 8, 4, 64, 32, 20, True, "bf16", (45, 300), pa.PA_KERNEL_MFMA),     # NQ = 20, cooperative
 ]
 APPEND_SCENARIOS = {
     "natural": dict(seed=3),
@@ -377,6 +384,54 @@ def test_dense_backward_empty_sides(causal):
     assert (dq == 0).all()
 
 
+def _oracle_backward_by_head(q, k, v, dout, scale, causal):
+    """The oracle's gradients of a one-KV-head problem, one query head per call
+    (calls run in parallel threads: the library releases the interpreter lock),
+    dk and dv of the group summed over its query heads in float64 (a KV head's
+    gradient is the sum of its query heads' contributions)."""
+    from concurrent.futures import ThreadPoolExecutor
+    assert k.shape[1] == 1
+    HQ = q.shape[1]
+
+    def one(h):
+        return oracle.dense_attention_backward(q[:, h:h + 1].contiguous(), k, v,
+                                               dout[:, h:h + 1].contiguous(), scale,
+                                               causal=causal)
+
+    with ThreadPoolExecutor(max_workers=HQ) as ex:
+        parts = list(ex.map(one, range(HQ)))
+    dq = np.concatenate([p[0] for p in parts], axis=1)
+    dk = sum(p[1] for p in parts)
+    dv = sum(p[2] for p in parts)
+    return dq, dk, dv
+
+
+def test_dense_prefill_one_group_every_element():
+    # One KV head of the prefill the bench times (2048 positions, 4 query heads
+    # per KV head, D = 128, causal, fp16): every element of the forward output
+    # and of dq, dk and dv against the oracle
+    B, HQ, HK, S, D = 1, 4, 1, 2048, 128
+    g = torch.Generator().manual_seed(75)
+    q = torch.randn(B, HQ, S, D, generator=g).half()
+    k = torch.randn(B, HK, S, D, generator=g).half()
+    v = torch.randn(B, HK, S, D, generator=g).half()
+    dout = torch.randn(B, HQ, S, D, generator=g).half()
+    scale = 0.088
+    print("[gpu] dense prefill, one group: forward", flush=True)
+    out = pa.dense_attention(q.to(DEV), k.to(DEV), v.to(DEV), scale, causal=True)
+    print("[gpu] dense prefill, one group: backward", flush=True)
+    dq, dk, dv = pa.dense_attention_backward(q.to(DEV), k.to(DEV), v.to(DEV), dout.to(DEV),
+                                             scale, causal=True)
+    torch.cuda.synchronize()
+    print("[gpu] dense prefill, one group: oracle forward", flush=True)
+    check_dense(out, oracle.dense_attention(q, k, v, scale, causal=True), "f16")
+    print("[gpu] dense prefill, one group: oracle backward", flush=True)
+    edq, edk, edv = _oracle_backward_by_head(q, k, v, dout, scale, True)
+    check_grad("dq", dq, edq, "f16")
+    check_grad("dk", dk, edk, "f16")
+    check_grad("dv", dv, edv, "f16")
+
+
 def test_dense_backward_prefill_sampled():
     # 1 x 32 query heads over 8 KV heads, 2048 positions, causal, fp16 (the
     # prefill the bench times): dq of three blocks of rows against the oracle on
@@ -442,24 +497,40 @@ def test_decode_score_staircase(case):
 
 
 # ---------------------------------------------------------------------------
-# Block-table indexing: bit-exact invariants
+# Block-table indexing: bit-exact invariants, on every pass-1 kernel family
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-def test_block_order_is_bit_exact(dtype):
-    w = P.small(B=3, H=8, KV=2, D=128, BS=16, NQ=2, causal=True, dtype=dtype,
+# (H, KV, NQ, dtype): R = (H/KV)*NQ query rows per KV head selects the kernel:
+# R <= 16 one matrix-core row tile, 17..32 two tiles, 33..64 the cooperative
+# two-wave kernel, > 64 the 16-bit vector-ALU kernel; fp32 the vector-ALU one.
+BITEXACT = [
+    (8, 2, 1, "f16"), (8, 2, 1, "bf16"),     # R = 4
+    (16, 2, 3, "f16"), (16, 2, 3, "bf16"),   # R = 24
+    (16, 2, 8, "f16"), (16, 2, 8, "bf16"),   # R = 64
+    (32, 2, 8, "f16"), (32, 2, 8, "bf16"),   # R = 128
+    (8, 2, 1, "f32"),                        # R = 4, fp32
+]
+BITEXACT_IDS = [f"h{h}-kv{kv}-nq{nq}-{dt}" for h, kv, nq, dt in BITEXACT]
+
+
+@pytest.mark.parametrize("case", BITEXACT, ids=BITEXACT_IDS)
+def test_block_order_is_bit_exact(case):
+    H, KV, NQ, dtype = case
+    w = P.small(B=3, H=H, KV=KV, D=128, BS=16, NQ=NQ, causal=True, dtype=dtype,
                 lens=(70, 16, 333), seed=3)
-    base = gpu_decode(to_device(w), num_partitions=2)
-    for seed in (1, 2):
-        w2 = to_device(P.relayout(w, shuffle_seed=seed, extra_blocks=7))
-        assert torch.equal(gpu_decode(w2, num_partitions=2), base)
-    check(to_device(w), base)
+    expect = ref(w)
+    for parts in (0, 3):
+        base = gpu_decode(to_device(w), num_partitions=parts)
+        check(w, base, expect)
+        for seed in (1, 2):
+            w2 = to_device(P.relayout(w, shuffle_seed=seed, extra_blocks=7))
+            assert torch.equal(gpu_decode(w2, num_partitions=parts), base), (parts, seed)
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_unused_pool_space_and_table_entries_are_never_read(dtype):
-    w = P.small(B=3, H=8, KV=2, D=128, BS=16, NQ=1, dtype=dtype, lens=(45, 3, 160), seed=4)
+@pytest.mark.parametrize("case", BITEXACT, ids=BITEXACT_IDS)
+def test_unused_pool_space_and_table_entries_are_never_read(case):
+    H, KV, NQ, dtype = case
+    w = P.small(B=3, H=H, KV=KV, D=128, BS=16, NQ=NQ, dtype=dtype, lens=(45, 3, 160), seed=4)
     clean = to_device(P.relayout(w, shuffle_seed=5, extra_blocks=6))
-    base = gpu_decode(clean, num_partitions=3)
     poisoned = P.relayout(w, shuffle_seed=5, extra_blocks=6, fill=float("nan"))
     # table entries past each sequence's last page point at poisoned blocks
     spare = sorted(set(range(poisoned.num_blocks)) - set(
@@ -472,25 +543,29 @@ def test_unused_pool_space_and_table_entries_are_never_read(dtype):
         wide[b, used:] = spare[b % len(spare)]
     poisoned.block_table = wide
     poisoned.spec = poisoned.spec.replace(max_blocks=wide.shape[1])
-    out = gpu_decode(to_device(poisoned), num_partitions=3)
-    assert torch.isfinite(out.float()).all()
-    assert torch.equal(out, base)
+    for parts in (0, 3):
+        base = gpu_decode(clean, num_partitions=parts)
+        out = gpu_decode(to_device(poisoned), num_partitions=parts)
+        assert torch.isfinite(out.float()).all()
+        assert torch.equal(out, base), parts
 
 
-def test_argmax_probe_maps_every_position():
-    # Sequence b makes logical position t_b dominate for head 0: out must be v_t.
+@pytest.mark.parametrize("case", BITEXACT, ids=BITEXACT_IDS)
+def test_argmax_probe_maps_every_position(case):
+    # Every query row of sequence b scores logical position t_b above all other
+    # visible keys by more than 150 in log2 units, so every other weight is 0
+    # in fp32 and the output is v_t bit for bit, whichever page holds it.
+    H, KV, NQ, dtype = case
     ts = [0, 1, 15, 16, 17, 31, 63, 100, 255]
-    lens = [256] * len(ts)
-    w = P.small(B=len(ts), H=2, KV=1, D=128, BS=16, NQ=1, dtype="f16", lens=lens, seed=8)
-    w = P.relayout(w, shuffle_seed=12, extra_blocks=3)
-    expect = []
-    for b, t in enumerate(ts):
-        phys = int(w.block_table[b, t // 16])
-        w.k_pool[phys, t % 16, 0] = (w.q[b, 0, 0].float() * 8.0).to(torch.float16)
-        expect.append(w.v_pool[phys, t % 16, 0].float())
-    out = gpu_decode(to_device(w), num_partitions=1).cpu().float()
-    for b in range(len(ts)):
-        assert (out[b, 0, 0] - expect[b]).abs().max() < 2e-3, ts[b]
+    w = P.small(B=len(ts), H=H, KV=KV, D=128, BS=16, NQ=NQ, dtype=dtype, lens=[256] * len(ts),
+                seed=8)
+    w = P.relayout(w, shuffle_seed=12, extra_blocks=3, fill=float("nan"))
+    w, expect = P.argmax_probe(w, ts)
+    wd = to_device(w)
+    for parts in (0, 1, 3):
+        out = gpu_decode(wd, num_partitions=parts).cpu()
+        for b, t in enumerate(ts):
+            assert torch.equal(out[b], expect[b]), (parts, b, t)
 
 
 # ---------------------------------------------------------------------------
