@@ -29,7 +29,8 @@ import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(HERE, "liboracle.so")
+# PAGED_ATTN_ORACLE_LIB selects another build of oracle.c (the sanitizer test's)
+_LIB_PATH = os.environ.get("PAGED_ATTN_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 _lib = None
 
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}

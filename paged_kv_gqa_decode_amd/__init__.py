@@ -15,7 +15,9 @@ import os
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpaged_attn.so")
+# PAGED_ATTN_LIBRARY selects another build of the library (e.g. a sanitizer build
+# of the host code for CPU tests)
+LIB_PATH = os.environ.get("PAGED_ATTN_LIBRARY") or os.path.join(HERE, "libpaged_attn.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_DEVICE, PA_ERR_LAUNCH = range(6)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2

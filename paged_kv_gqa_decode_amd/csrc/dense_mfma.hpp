@@ -222,7 +222,10 @@ void dense_mfma(DenseArgs<T> d) {
         }
         rows.accumulate(vt, valid);
     }
-    if (q_pending) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no keys: Q was never waited for
+    // Q is still in flight when there were no keys; otherwise nothing is (the
+    // loop waited for every sub-page), so this costs nothing and leaves no path
+    // on which the rows' registers are read before a wait.
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     rows.flush();
     auto row_off = [&](int r) -> int64_t {  // element offset of row r from head0's first row
         if (r >= R || r % g.P >= pend) return -1;
