@@ -231,7 +231,8 @@ __device__ __forceinline__ void fetch_rows(const T* k, const T* v, int rmax, cha
 }
 
 // ---- the stream of one wave's sub-pages: cursor, table entries, fetches ----
-template <typename T, int D, int BS>
+// SEQ: the sequence table (SeqTableLds or SeqTableRegs).
+template <typename T, int D, int BS, typename SEQ = SeqTableLds>
 struct SubPageStream {
     using Lay = SlotLayout<T, D>;
     static constexpr int KS = D / 32;    // load instructions per half (K or V)
@@ -253,8 +254,7 @@ struct SubPageStream {
     const SplitArgs<T>& a;
     const int32_t* __restrict__ table;  // block table; entries are read with scalar loads
     const int32_t* __restrict__ slots;  // slot-patched step: [B][NQ] (a.ap.slots), else nullptr
-    const int* s_pref;
-    const int* s_len;
+    SEQ seq;
     int KV, NQ, kh, nnew, tbytes, lane;
     int kfb;  // per-lane K fetch offset of a cached sub-page (instruction 0)
     int pre_phys = 0;  // table entry of the last prefetch_table() position
@@ -263,22 +263,22 @@ struct SubPageStream {
 
     __device__ __forceinline__ SubPageStream(const SplitArgs<T>& args,
                                              const int32_t* __restrict__ tab,
-                                             const int32_t* __restrict__ sl, const int* pref,
-                                             const int* lens, int head, int ln)
-        : a(args), table(tab), slots(sl), s_pref(pref), s_len(lens), KV(args.g.KV), NQ(args.g.NQ), kh(head),
+                                             const int32_t* __restrict__ sl, const SEQ& sq,
+                                             int head, int ln)
+        : a(args), table(tab), slots(sl), seq(sq), KV(args.g.KV), NQ(args.g.NQ), kh(head),
           nnew((args.g.NQ + 15) / 16), tbytes(args.g.KV * D * (int)sizeof(T)), lane(ln) {
         kfb = Lay::k_fetch_base(lane, tbytes);
     }
     __device__ __forceinline__ void enter_seq(Cur& c) const {
-        c.nsub = s_pref[c.b + 1] - s_pref[c.b];
+        c.nsub = seq.pref(c.b + 1) - seq.pref(c.b);
         c.nc = c.nsub - nnew;
-        c.L = s_len[c.b];
+        c.L = seq.len(c.b);
     }
     __device__ __forceinline__ Cur seek(int64_t x) const {  // the sub-page at axis position x
         Cur c;
-        c.b = split_find_seq(a.g, s_pref, x);
+        c.b = seq.find(a.g, x);
         enter_seq(c);
-        c.j = (int)(x - s_pref[c.b]);
+        c.j = (int)(x - seq.pref(c.b));
         return c;
     }
     __device__ __forceinline__ void step(Cur& c) const {  // next position along the axis
@@ -861,7 +861,8 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table,
     int* s_pref = reinterpret_cast<int*>(smem + 4 * NS * Lay::kBytes);
     int* s_len = s_pref + a.g.B + 1;
     build_prefix(a.context_lens, a.g, s_pref, s_len);
-    const Cut cut(a.g, s_pref[a.g.B]);
+    const SeqTableLds seq{s_pref, s_len, a.g.B};
+    const Cut cut(a.g, seq.total());
 
     // The wave index is uniform within a wave; saying so keeps every per-wave
     // quantity (group, head, sequence, page, descriptors, LDS slot) scalar.
@@ -875,7 +876,7 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table,
     const int n_total = (int)(cut.start(grp + 1) - x0);  // sub-pages this wave attends (>= 1)
     char* const ring = smem + wave * NS * Lay::kBytes;
 
-    Stream st(a, table, slots, s_pref, s_len, kh, lane);
+    Stream st(a, table, slots, seq, kh, lane);
     Rows rows(a, lane, 0);
     Cur cc = st.seek(x0);  // the sub-page being attended
     Cur pc = cc;           // the next sub-page to fetch
@@ -906,7 +907,7 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table,
         const bool more = i + 1 < n_total;
         if (cc.j == 0 && kh == 0 && lane == 0 && a.meta) {
             // the first piece of a sequence records the groups it spans
-            const int64_t s0 = s_pref[cc.b];
+            const int64_t s0 = seq.pref(cc.b);
             a.meta[2 * cc.b] = (int32_t)cut.group_of(s0);
             a.meta[2 * cc.b + 1] = (int32_t)cut.group_of(s0 + cc.nsub - 1);
         }
@@ -987,12 +988,14 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table,
 // sub-pages per workgroup stay in flight during the arithmetic. A sequence
 // switch loads the waves' new Q after the arithmetic (it is waited for at the
 // next iteration, a rare full drain).
-template <typename T, int D, int BS, int NW, int NRT, int kRing, int WPS, bool APPEND>
+template <typename T, int D, int BS, int NW, int NRT, int kRing, int WPS, bool APPEND,
+          bool REGSEQ>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPS, WPS)))
 void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table,
                       const int32_t* __restrict__ slots) {
     using Lay = SlotLayout<T, D>;
-    using Stream = SubPageStream<T, D, BS>;
+    using Seq = typename std::conditional<REGSEQ, SeqTableRegs, SeqTableLds>::type;
+    using Stream = SubPageStream<T, D, BS, Seq>;
     using Rows = RowTiles<T, D, NRT, true>;
     using Cur = typename Stream::Cur;
     constexpr int KS = D / 32;
@@ -1002,10 +1005,17 @@ void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table,
     static_assert(kRing >= 3 && 2 * IPW * (kRing - 2) <= 63, "ring");
 
     extern __shared__ __attribute__((aligned(1024))) char smem[];  // slots start 1 KiB aligned (XOR addressing)
-    int* s_pref = reinterpret_cast<int*>(smem + kRing * Lay::kBytes);
-    int* s_len = s_pref + a.g.B + 1;
-    build_prefix(a.context_lens, a.g, s_pref, s_len);
-    const Cut cut(a.g, s_pref[a.g.B]);
+    const Seq seq = [&]() {
+        if constexpr (REGSEQ) {
+            return SeqTableRegs(a.context_lens, a.g);  // no LDS beyond the ring
+        } else {
+            int* s_pref = reinterpret_cast<int*>(smem + kRing * Lay::kBytes);
+            int* s_len = s_pref + a.g.B + 1;
+            build_prefix(a.context_lens, a.g, s_pref, s_len);
+            return SeqTableLds{s_pref, s_len, a.g.B};
+        }
+    }();
+    const Cut cut(a.g, seq.total());
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1017,7 +1027,7 @@ void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table,
     const bool issues = wave < NWI;  // this wave loads instructions wave, wave + NWI, ...
     const bool has_rows = 16 * NRT * wave < a.R;
 
-    Stream st(a, table, slots, s_pref, s_len, kh, lane);
+    Stream st(a, table, slots, seq, kh, lane);
     Rows rows(a, lane, wave * NRT);
     Cur cc = st.seek(x0);
     Cur pc = cc;  // next sub-page to fetch: kRing - 1 ahead of cc once primed
@@ -1047,7 +1057,7 @@ void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table,
     for (int i = 0; i < n_total; ++i) {
         const int ahead = min(kRing - 2, n_total - 1 - i);  // sub-pages fetched after i
         if (cc.j == 0 && lane == 0 && wave == 0 && kh == 0 && a.meta) {
-            const int64_t s0 = s_pref[cc.b];
+            const int64_t s0 = seq.pref(cc.b);
             a.meta[2 * cc.b] = (int32_t)cut.group_of(s0);
             a.meta[2 * cc.b + 1] = (int32_t)cut.group_of(s0 + cc.nsub - 1);
         }
@@ -1089,11 +1099,10 @@ void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table,
             const typename Stream::Src sn = st.locate(pc);
             if (issues)
                 st.template fetch<IPW>(sn, smem + (nxt % kRing) * Lay::kBytes, pc.j < pc.nc, wave, NWI);
-            if (nxt + 1 < n_total) {
-                st.step(pc);
-                st.prefetch_table(pc);
-            }
         }
+        // the next fetch position and its table entry; the scalar load is
+        // issued after this iteration's LDS wait (which would also wait for it)
+        const bool adv = nxt + 1 < n_total;
         const char* slot = smem + (i % kRing) * Lay::kBytes;
         const bool is_new = cc.j >= cc.nc;
         const int t0 = 16 * (cc.j - cc.nc);
@@ -1106,6 +1115,10 @@ void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table,
             rows.read_k(slot, kop);
             rows.read_v(slot, vt);
             Rows::lds_wait(vt);
+            if (adv) {
+                st.step(pc);
+                st.prefetch_table(pc);
+            }
             int lim[NRT];
             rows.limits(valid, is_new, t0, lim);
             rows.scores(kop, lim, !is_new && valid == 16);
@@ -1115,6 +1128,9 @@ void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table,
                 rows.emit(cc.b, kh, grp, piece_from_start && seq_ends);
                 rows.reset();
             }
+        } else if (adv) {
+            st.step(pc);
+            st.prefetch_table(pc);
         }
         if (piece_ends) piece_from_start = true;
         if (i + 1 < n_total) {

@@ -146,24 +146,31 @@ struct Plan {
 //   rt = 1: decode_mfma, one wave per (group, head) with one row tile;
 //   rt = 2: decode_mfma with two row tiles per wave;
 //   rt = 4: decode_mfma_coop, two waves of two row tiles per (group, head)
-//           sharing a ring of four slots;
+//           sharing a ring of slots: five when the batch's sequence table fits
+//           in registers (batch <= 64: no LDS beside the ring, so four
+//           workgroups of five slots fill the CU's 160 KiB), else four;
 // all at 2 waves per SIMD, each keeping about 128 KiB of sub-pages in flight
 // per CU (slots double for D = 64, whose slots are half as large). Measured
 // on the Llama-3-8B-shaped and ragged-serving workloads: 2 waves per SIMD with
 // 2 slots each beat 4 waves with 1 slot (oldest waves hog the memory path,
 // the last quarter of the kernel runs thin) and 1 wave with 4 slots; for 64
-// rows, 2 waves x 2 tiles beat 4 waves x 1 tile and 1 wave x 4 tiles.
+// rows, 2 waves x 2 tiles beat 4 waves x 1 tile and 1 wave x 4 tiles, and
+// four workgroups per CU beat fewer with deeper rings (two of nine slots,
+// three of six).
 struct MfmaShape {
-    int nw;     // waves per (group, head): 1, or the cooperative workgroup
-    int nrt;    // row tiles per wave
-    int slots;  // LDS slots per wave (nw = 1) or ring slots per workgroup
-    int wps;    // waves per SIMD the kernel is built for
+    int nw;      // waves per (group, head): 1, or the cooperative workgroup
+    int nrt;     // row tiles per wave
+    int slots;   // LDS slots per wave (nw = 1) or ring slots per workgroup
+    int wps;     // waves per SIMD the kernel is built for
+    bool regseq; // sequence table in registers (no prefix in LDS)
 };
-MfmaShape mfma_shape(int rt, int head_dim) {
-    const int s1 = head_dim == 128 ? 1 : 2;  // a D = 64 slot is half as large
-    if (rt == 1) return {1, 1, 2 * s1, 2};
-    if (rt == 2) return {1, 2, 2 * s1, 2};
-    return {2, 2, 4 * s1, 2};
+bool regseq_batch(const pa_problem* p) { return p->batch <= pa::kRegTableMaxBatch; }
+MfmaShape mfma_shape(const pa_problem* p, int rt) {
+    const int s1 = p->head_dim == 128 ? 1 : 2;  // a D = 64 slot is half as large
+    if (rt == 1) return {1, 1, 2 * s1, 2, false};
+    if (rt == 2) return {1, 2, 2 * s1, 2, false};
+    if (regseq_batch(p)) return {2, 2, 5 * s1, 2, true};
+    return {2, 2, 4 * s1, 2, false};
 }
 int mfma_slot_bytes(int head_dim) {
     return head_dim == 64 ? pa::SlotLayout<_Float16, 64>::kBytes
@@ -173,15 +180,16 @@ int mfma_slot_bytes(int head_dim) {
 // Dynamic LDS of one matrix-core workgroup: its slots (4 single waves' slots,
 // or the cooperative ring), then the per-sequence prefix and lengths.
 size_t mfma_lds_bytes(const pa_problem* p, int rt) {
-    const MfmaShape sh = mfma_shape(rt, p->head_dim);
+    const MfmaShape sh = mfma_shape(p, rt);
     const size_t slots = sh.nw == 1 ? 4 * (size_t)sh.slots : (size_t)sh.slots;
-    return slots * mfma_slot_bytes(p->head_dim) + (2 * (size_t)p->batch + 1) * sizeof(int);
+    const size_t table = sh.regseq ? 0 : (2 * (size_t)p->batch + 1) * sizeof(int);
+    return slots * mfma_slot_bytes(p->head_dim) + table;
 }
 
 // Streams (waves for nw = 1, workgroups otherwise) one CU holds at once: the
 // kernel's occupancy, lowered by LDS.
 int mfma_streams_per_cu(const pa_problem* p, int rt) {
-    const MfmaShape sh = mfma_shape(rt, p->head_dim);
+    const MfmaShape sh = mfma_shape(p, rt);
     const int wg_waves = sh.nw == 1 ? 4 : sh.nw;
     int groups = (int)(kLdsPerCu / mfma_lds_bytes(p, rt));  // workgroups by LDS
     const int by_regs = 4 * sh.wps / wg_waves;
@@ -397,8 +405,11 @@ void launch_mfma_k(const pa_problem* p, const Plan& pl, size_t lds, hipStream_t 
         const dim3 grid((unsigned)ceil_div(streams, 4));
         hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 2, 2 * S1, 2, APPEND>), grid, dim3(256), lds,
                            s, a, table, a.ap.slots);
+    } else if (regseq_batch(p)) {
+        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2, 2, 5 * S1, 2, APPEND, true>),
+                           dim3((unsigned)streams), dim3(128), lds, s, a, table, a.ap.slots);
     } else {
-        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2, 2, 4 * S1, 2, APPEND>),
+        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2, 2, 4 * S1, 2, APPEND, false>),
                            dim3((unsigned)streams), dim3(128), lds, s, a, table, a.ap.slots);
     }
 }

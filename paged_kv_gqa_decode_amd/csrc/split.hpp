@@ -106,4 +106,53 @@ __device__ __forceinline__ int split_find_seq(const SplitGeometry& g, const int*
     return lo;
 }
 
+// The batch's sequence table as the streams read it: pref(b) = sum of n_sub
+// over sequences before b (pref(B) = W), len(b) = the clamped cached length,
+// find(x) = the sequence holding axis position x.
+// SeqTableLds: built in LDS by build_prefix, any batch size.
+struct SeqTableLds {
+    const int* s_pref;
+    const int* s_len;
+    int B;
+    __device__ __forceinline__ int pref(int b) const { return s_pref[b]; }
+    __device__ __forceinline__ int len(int b) const { return s_len[b]; }
+    __device__ __forceinline__ int total() const { return s_pref[B]; }
+    __device__ __forceinline__ int find(const SplitGeometry& g, int64_t x) const {
+        return split_find_seq(g, s_pref, x);
+    }
+};
+
+// SeqTableRegs: batches of at most 64 sequences, held in registers: lane b of
+// each wave keeps sequence b's prefix and length (every wave builds its own
+// copy with one load and a wave scan: no LDS and no barrier), read back with
+// readlane at the wave-uniform sequence index.
+constexpr int kRegTableMaxBatch = 64;
+struct SeqTableRegs {
+    int v_pref, v_len;  // this lane's sequence (lane < B)
+    int W, B;
+    __device__ __forceinline__ SeqTableRegs(const int32_t* context_lens, const SplitGeometry& g)
+        : B(g.B) {
+        const int lane = threadIdx.x & 63;
+        const int nnew = (g.NQ + 15) / 16;
+        const int raw = lane < g.B ? context_lens[lane] : 0;
+        const int L = lane < g.B ? min(max(raw, 0), g.max_tokens) : 0;
+        const int n = lane < g.B ? (L + 15) / 16 + nnew : 0;
+        const int incl = wave_inclusive_scan(n);
+        v_pref = incl - n;
+        v_len = L;
+        W = __builtin_amdgcn_readlane(incl, 63);
+    }
+    __device__ __forceinline__ int pref(int b) const {
+        return b < B ? __builtin_amdgcn_readlane(v_pref, b) : W;
+    }
+    __device__ __forceinline__ int len(int b) const { return __builtin_amdgcn_readlane(v_len, b); }
+    __device__ __forceinline__ int total() const { return W; }
+    __device__ __forceinline__ int find(const SplitGeometry&, int64_t x) const {
+        const int lane = threadIdx.x & 63;
+        // lanes of sequences starting at or before x; lane 0 always (pref(0) = 0)
+        const uint64_t m = __ballot(lane < B && (int64_t)v_pref <= x);
+        return 63 - __builtin_clzll(m);
+    }
+};
+
 }  // namespace pa

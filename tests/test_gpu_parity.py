@@ -159,6 +159,18 @@ def test_geometries(case):
         check(w, gpu_decode(w, num_partitions=parts), expect)
 
 
+@pytest.mark.parametrize("B,dtype", [(1, "f16"), (64, "bf16"), (65, "f16"), (130, "bf16")])
+def test_cooperative_kernel_sequence_tables(B, dtype):
+    # 64 rows per KV head (the cooperative kernel): batches of up to 64
+    # sequences keep the sequence table in registers, larger ones in LDS
+    lens = tuple(int(x) for x in np.random.default_rng(B).integers(0, 200, size=B))
+    w = to_device(P.small(B=B, H=16, KV=2, D=128, BS=16, NQ=8, causal=True, dtype=dtype,
+                          lens=lens, seed=23))
+    expect = ref(w)
+    for parts in (0, 1, 3, 40):
+        check(w, gpu_decode(w, num_partitions=parts), expect)
+
+
 def test_many_short_sequences():
     # 4200 sequences of 0..39 cached keys: an LDS prefix of 33 KiB beside the
     # slots, most sequences inside one group, several per wave
