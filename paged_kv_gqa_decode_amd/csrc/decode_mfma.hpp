@@ -131,6 +131,17 @@ constexpr int kStreamPolicy = 2;
 // Slack of the lazy reference max, in log2 units (probabilities stay <= 256).
 constexpr float kSlack = 8.0f;
 
+// Logical workgroup index: the hardware hands workgroups to the 8 XCDs in turn
+// (workgroup n to XCD n % 8), so logical index (n % 8) * (N / 8) + n / 8 puts
+// consecutive logical indices, i.e. the KV heads of one group, on one XCD. The
+// last N % 8 workgroups keep their index (the map is a bijection of [0, N)).
+__device__ __forceinline__ int64_t xcd_local_block() {
+    const int64_t n = gridDim.x, b = blockIdx.x;
+    const int64_t full = n / 8 * 8;
+    if (b >= full) return b;
+    return (b % 8) * (n / 8) + b / 8;
+}
+
 template <typename T>
 struct SplitArgs {
     const T* q;
@@ -258,8 +269,8 @@ struct SubPageStream {
     int KV, NQ, kh, nnew, tbytes, lane;
     int kfb;  // per-lane K fetch offset of a cached sub-page (instruction 0)
     int pre_phys = 0;  // table entry of the last prefetch_table() position
-    int pat_b = -1;    // slot-patched step: sequence whose slot range is held
-    int64_t pat_lo = 0, pat_hi = -1;  // smallest and largest slot its new rows name
+    int pat_b = -1;    // slot-patched step: sequence whose block range is held
+    int pat_blo = 0, pat_bhi = -1;  // smallest and largest block its new rows' slots are in
 
     __device__ __forceinline__ SubPageStream(const SplitArgs<T>& args,
                                              const int32_t* __restrict__ tab,
@@ -374,18 +385,20 @@ struct SubPageStream {
     __device__ __forceinline__ bool patched(const Cur& c, int64_t phys) {
         if (c.j >= c.nc) return false;
         const int32_t* sl = slots + (int64_t)c.b * NQ;
-        if (c.b != pat_b) {
+        if (c.b != pat_b) {  // the blocks the sequence's stored rows fall in
             pat_b = c.b;
-            pat_lo = INT64_MAX;
-            pat_hi = -1;
+            pat_blo = 0x7fffffff;
+            pat_bhi = -1;
             for (int j = 0; j < NQ; ++j) {
-                pat_lo = min(pat_lo, (int64_t)sl[j]);
-                pat_hi = max(pat_hi, (int64_t)sl[j]);
+                const int32_t sj = sl[j];
+                if (sj < 0 || sj >= a.ap.n_slot) continue;  // neither stored nor read
+                pat_blo = min(pat_blo, sj / BS);
+                pat_bhi = max(pat_bhi, sj / BS);
             }
         }
+        if ((int)phys < pat_blo || (int)phys > pat_bhi) return false;
         const int64_t base = phys * BS + 16 * (c.j % SUB);
         const int valid = min(16, c.L - 16 * c.j);
-        if (base + valid <= pat_lo || base > pat_hi) return false;
         bool any = false;
         for (int j = 0; j < NQ; ++j) {
             const int64_t t = (int64_t)sl[j] - base;
@@ -419,40 +432,60 @@ struct SubPageStream {
         }
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
     }
+    // Copies new row t of the sub-page in LDS slot `slot` (head kh) to pool
+    // slot s: lanes 0 .. kChunks - 1 move the K row's 16-byte chunks, the next
+    // kChunks lanes the V row's. Not waited for.
+    __device__ __forceinline__ void store_row(const char* slot, int t, int64_t s) const {
+        typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
+        const uint32_t slot_lds = (uint32_t)reinterpret_cast<uintptr_t>(slot);
+        const int64_t row = (s * KV + kh) * D;
+        if (lane < Lay::kChunks) {
+            const u32x4_t v = *(lds_u32x4*)(uintptr_t)(slot_lds + Lay::k_addr(t, lane));
+            *reinterpret_cast<u32x4_t*>(static_cast<T*>(a.ap.k_dst) + row + 8 * lane) = v;
+        } else if (lane < 2 * Lay::kChunks) {
+            const int ch = lane - Lay::kChunks;
+            const u32x4_t v = *(lds_u32x4*)(uintptr_t)(slot_lds + Lay::kKBytes + Lay::v_addr(t, ch));
+            *reinterpret_cast<u32x4_t*>(static_cast<T*>(a.ap.v_dst) + row + 8 * ch) = v;
+        }
+    }
     // Stores the new rows of sub-page c (new rows, in LDS slot `slot`) that the
     // step keeps into their pool slots, head kh of each: row j goes to slot s =
     // slots[b][j] when 0 <= s < n_slot and no later row of the sequence names
-    // s. The sequence's slots are loaded once, lane l holding rows l and 64 + l,
-    // and the later rows are found with a ballot (nq <= 128). Their load is
-    // waited for at once on every path (one drain of the wave's loads per unit);
-    // the stores are not waited for.
+    // s; the stores are not waited for. Up to 16 rows (one new-row sub-page) the
+    // sequence's slots are scalar loads (the wait for them does not drain the
+    // wave's pool loads in flight); beyond, they are loaded once, lane l holding
+    // rows l and 64 + l, the later rows found with a ballot (nq <= 128), and
+    // that load is waited for at once (one drain of the wave's loads per unit).
     __device__ __forceinline__ void store_new(const Cur& c, const char* slot) const {
-        typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
         const int t0 = 16 * (c.j - c.nc);
         const int valid = min(16, NQ - t0);
         const int32_t* sl = slots + (int64_t)c.b * NQ;
+        if (NQ <= 16) {
+            int32_t sm[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) sm[j] = j < NQ ? sl[j] : -1;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (j >= NQ) break;
+                const int32_t sj = sm[j];
+                bool later = false;
+#pragma unroll
+                for (int jj = j + 1; jj < 16; ++jj) later = later || (jj < NQ && sm[jj] == sj);
+                if (sj < 0 || sj >= a.ap.n_slot || later) continue;
+                store_row(slot, j, sj);
+            }
+            return;
+        }
         int32_t m0 = lane < NQ ? sl[lane] : -1;
         int32_t m1 = 64 + lane < NQ ? sl[64 + lane] : -1;
         asm volatile("" : "+v"(m0), "+v"(m1));  // consumed here, whatever the loop below does
-        const uint32_t slot_lds = (uint32_t)reinterpret_cast<uintptr_t>(slot);
-        T* const kd = static_cast<T*>(a.ap.k_dst);
-        T* const vd = static_cast<T*>(a.ap.v_dst);
         for (int t = 0; t < valid; ++t) {
             const int j = t0 + t;
             const int32_t s = __builtin_amdgcn_readlane(j < 64 ? m0 : m1, j & 63);
             const bool later = __ballot(lane > j && lane < NQ && m0 == s) != 0 ||
                                __ballot(64 + lane > j && 64 + lane < NQ && m1 == s) != 0;
             if (s < 0 || s >= a.ap.n_slot || later) continue;
-            const int64_t row = ((int64_t)s * KV + kh) * D;
-            if (lane < Lay::kChunks) {
-                const u32x4_t v = *(lds_u32x4*)(uintptr_t)(slot_lds + Lay::k_addr(t, lane));
-                *reinterpret_cast<u32x4_t*>(kd + row + 8 * lane) = v;
-            } else if (lane < 2 * Lay::kChunks) {
-                const int ch = lane - Lay::kChunks;
-                const u32x4_t v =
-                    *(lds_u32x4*)(uintptr_t)(slot_lds + Lay::kKBytes + Lay::v_addr(t, ch));
-                *reinterpret_cast<u32x4_t*>(vd + row + 8 * ch) = v;
-            }
+            store_row(slot, t, s);
         }
     }
 };
@@ -868,7 +901,10 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table,
     // quantity (group, head, sequence, page, descriptors, LDS slot) scalar.
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+    // (measured: 0.6 us faster on the Llama-3-8B batch, 1.5 us on ragged
+    // serving; the cooperative kernel, whose groups span eight workgroups,
+    // keeps the hardware order, which measured faster for it)
+    const int64_t gw = xcd_local_block() * 4 + wave;
     const int64_t grp = gw / a.g.KV;  // the KV waves of a group are consecutive
     const int kh = (int)(gw - grp * a.g.KV);
     if (grp >= cut.n) return;  // no barrier follows
@@ -942,28 +978,34 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table,
         } else {
             Rows::lds_wait(vt);
         }
+        const bool seq_ends = cc.j + 1 == cc.nsub;
+        // NS > 1: the slot is read out, so it is refilled at once, unless this
+        // sub-page ends its sequence: the next sequence's Q, loaded after the
+        // scores (it overwrites this one's), must then be older than the refill
+        const bool late = more && seq_ends;
+        auto refill_slot = [&]() {
+            if constexpr (APPEND) {
+                const uint32_t bit = 1u << (i % NS);
+                pmask = st.patched(pc, st.pre_phys) ? (pmask | bit) : (pmask & ~bit);
+            }
+            st.fetch(st.locate(pc), slot, pc.j < pc.nc);
+            ++q_younger;
+        };
+        if constexpr (NS > 1)
+            if (refill && !late) refill_slot();
         const bool is_new = cc.j >= cc.nc;
         const int t0 = 16 * (cc.j - cc.nc);
         const int valid = is_new ? min(16, st.NQ - t0) : min(16, cc.L - 16 * cc.j);
         int lim[NRT];
         rows.limits(valid, is_new, t0, lim);
         rows.scores(kop, lim, !is_new && valid == 16);
-        const bool seq_ends = cc.j + 1 == cc.nsub;
-        if (more && seq_ends) {  // Q of the next sequence
+        if (late) {  // Q of the next sequence
             rows.load_q(cc.b + 1, kh);
             q_pending = true;
             q_younger = 0;
         }
-        if constexpr (NS > 1) {
-            if (refill) {
-                if constexpr (APPEND) {
-                    const uint32_t bit = 1u << (i % NS);
-                    pmask = st.patched(pc, st.pre_phys) ? (pmask | bit) : (pmask & ~bit);
-                }
-                st.fetch(st.locate(pc), slot, pc.j < pc.nc);  // slot already read out
-                ++q_younger;
-            }
-        }
+        if constexpr (NS > 1)
+            if (refill && late) refill_slot();
         if (refill && i + NS + 1 < n_total) {
             st.step(pc);
             st.prefetch_table(pc);
