@@ -129,6 +129,8 @@ int validate_problem(const pa_problem* p) {
     return PA_OK;
 }
 
+constexpr int kCoopSeqPad = 3;  // a sequence's fixed cost in the cooperative kernel, positions
+
 struct Plan {
     // VALU family: parts = key partitions per sequence, chunk = cached tokens per
     // partition (multiple of block_size). Matrix-core family (balanced split):
@@ -137,6 +139,7 @@ struct Plan {
     int parts;
     int chunk;
     int min_seg;  // matrix-core family: minimum group length in 16-key positions
+    int seq_pad;  // matrix-core family: a sequence's fixed cost, in 16-key positions
     int kernel;   // pa_kernel
     int rt;       // VALU: query rows per workgroup (power of two <= 8); MFMA: 16-row tiles (1, 2, 4)
     int n_tiles;  // workgroups per KV head along the rows (1 for MFMA)
@@ -209,6 +212,7 @@ int plan_impl(const pa_problem* p, int num_cus, Plan* pl) {
                      : PA_KERNEL_VALU;
     pl->kernel = kernel;
     pl->min_seg = 1;
+    pl->seq_pad = 0;
     if (kernel == PA_KERNEL_MFMA) {
         pl->rt = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
         pl->n_tiles = 1;
@@ -226,6 +230,12 @@ int plan_impl(const pa_problem* p, int num_cus, Plan* pl) {
             const int64_t groups = streams / p->num_kv_heads;
             pl->parts = (int)(groups < 1 ? 1 : (groups > (1 << 22) ? (1 << 22) : groups));
             pl->min_seg = (int)ceil_div(kStateRatio * state, kv_per_group);
+            // the cooperative kernel's fixed work per sequence (a drain of its
+            // ring for the next Q, a 64-row piece state, the new rows) costs
+            // about 3 sub-pages: charged to the sequence, the groups that hold a
+            // sequence start finish with the others (multi-row causal pass 1
+            // 68 -> 66 us); the one-wave kernels measured best without
+            pl->seq_pad = pl->rt == 4 ? kCoopSeqPad : 0;
         }
         pl->chunk = 16 * pl->min_seg;
         return PA_OK;
@@ -431,6 +441,7 @@ pa::SplitGeometry split_geometry(const pa_problem* p, const Plan& pl) {
     g.max_tokens = p->max_blocks_per_seq * p->block_size;
     g.n_grp = pl.parts;
     g.min_seg = pl.min_seg;
+    g.seq_pad = pl.seq_pad;
     return g;
 }
 

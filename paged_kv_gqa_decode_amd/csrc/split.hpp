@@ -29,6 +29,7 @@ struct SplitGeometry {
     int B, KV, NQ, max_tokens;  // max_tokens = max_blocks_per_seq * block_size
     int n_grp;                  // groups the grid provides (KV waves each)
     int min_seg;                // minimum group length, in positions
+    int seq_pad;                // cost of a sequence beyond its positions, in positions
 };
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
@@ -80,27 +81,49 @@ __device__ __forceinline__ void build_prefix(const int32_t* context_lens, const 
     __syncthreads();
 }
 
-// The cut of an axis of W positions into groups.
+// The cut of the axis into groups by cost: a sequence costs its n_sub
+// positions plus seq_pad (its fixed work: Q loads, the piece's state, the
+// switch), so the axis is C = W + seq_pad * B cost units, sequence b taking
+// [pref(b) + seq_pad * b, pref(b + 1) + seq_pad * b + seq_pad) with its pad
+// after its positions. Group g takes the cost units from floor(g*C/n): its
+// first position is that of cost unit floor(g*C/n), a unit of a pad standing
+// for the next sequence's first position. Groups differ by at most one cost
+// unit; a group inside a pad has no position (and is skipped).
 struct Cut {
-    int64_t W;
+    int64_t W, C;
     int64_t n;  // groups in use: n_grp, fewer when groups would be shorter than min_seg
-    __device__ __forceinline__ Cut(const SplitGeometry& g, int64_t total) : W(total) {
-        int64_t m = g.min_seg > 1 ? total / g.min_seg : total;
+    int pad;
+    __device__ __forceinline__ Cut(const SplitGeometry& g, int64_t total)
+        : W(total), C(total + (int64_t)g.seq_pad * g.B), pad(g.seq_pad) {
+        int64_t m = g.min_seg > 1 ? C / g.min_seg : C;
         if (m < 1) m = 1;
         n = m < g.n_grp ? m : g.n_grp;
     }
-    __device__ __forceinline__ int64_t start(int64_t grp) const { return grp * W / n; }
-    // the group holding position x (largest g with start(g) <= x)
-    __device__ __forceinline__ int64_t group_of(int64_t x) const { return ((x + 1) * n - 1) / W; }
+    // first position of group grp (grp <= n; start(n) = W)
+    template <typename SEQ>
+    __device__ __forceinline__ int64_t start(int64_t grp, const SEQ& seq, const SplitGeometry& g) const {
+        const int64_t c = grp * C / n;
+        if (pad == 0 || c >= C) return c >= C ? W : c;
+        const int b = seq.find_cost(g, c, pad);
+        const int64_t p0 = seq.pref(b);
+        const int64_t p1 = seq.pref(b + 1);
+        const int64_t off = c - (p0 + (int64_t)pad * b);
+        return off < p1 - p0 ? p0 + off : p1;
+    }
+    // the group holding position x of sequence b (largest g with start(g) <= x)
+    __device__ __forceinline__ int64_t group_of(int64_t x, int b) const {
+        return ((x + (int64_t)pad * b + 1) * n - 1) / C;
+    }
 };
 
-// Sequence holding position x: largest b with s_pref[b] <= x.
+// Sequence holding position x: largest b with s_pref[b] + pad*b <= x (pad = 0:
+// the position axis; pad > 0: the cost axis of Cut).
 __device__ __forceinline__ int split_find_seq(const SplitGeometry& g, const int* s_pref,
-                                              int64_t x) {
+                                              int64_t x, int pad = 0) {
     int lo = 0, hi = g.B - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if ((int64_t)s_pref[mid] <= x) lo = mid;
+        if ((int64_t)s_pref[mid] + (int64_t)pad * mid <= x) lo = mid;
         else hi = mid - 1;
     }
     return lo;
@@ -119,6 +142,9 @@ struct SeqTableLds {
     __device__ __forceinline__ int total() const { return s_pref[B]; }
     __device__ __forceinline__ int find(const SplitGeometry& g, int64_t x) const {
         return split_find_seq(g, s_pref, x);
+    }
+    __device__ __forceinline__ int find_cost(const SplitGeometry& g, int64_t c, int pad) const {
+        return split_find_seq(g, s_pref, c, pad);
     }
 };
 
@@ -151,6 +177,12 @@ struct SeqTableRegs {
         const int lane = threadIdx.x & 63;
         // lanes of sequences starting at or before x; lane 0 always (pref(0) = 0)
         const uint64_t m = __ballot(lane < B && (int64_t)v_pref <= x);
+        return 63 - __builtin_clzll(m);
+    }
+    // the sequence holding cost unit c of Cut (largest b with pref(b) + pad*b <= c)
+    __device__ __forceinline__ int find_cost(const SplitGeometry&, int64_t c, int pad) const {
+        const int lane = threadIdx.x & 63;
+        const uint64_t m = __ballot(lane < B && (int64_t)v_pref + (int64_t)pad * lane <= c);
         return 63 - __builtin_clzll(m);
     }
 };

@@ -80,24 +80,27 @@ def logical_rows(w: W.Workload, b: int, kh: int, r: int):
     return ks, vs
 
 
-def split_single_piece_units(context_lens, KV, NQ, n_grp, min_seg, max_tokens):
+def split_single_piece_units(context_lens, KV, NQ, n_grp, min_seg, max_tokens, seq_pad=0):
     """Units (b, kh) that the balanced split leaves in one group.
 
-    Integer model of the split: sequence b spans ceil(L_b/16) + ceil(NQ/16)
-    positions of 16 keys along one axis of W positions; n = min(n_grp,
-    max(1, W // min_seg)) groups start at floor(g*W/n), and every KV head of a
-    sequence shares its groups."""
+    Integer model of the split: sequence b spans n_b = ceil(L_b/16) +
+    ceil(NQ/16) positions of 16 keys along one axis, and costs n_b + seq_pad
+    units of a cost axis of C units (seq_pad = 0 for plans with an explicit
+    number of partitions); n = min(n_grp, max(1, C // min_seg)) groups start at
+    cost unit floor(g*C/n), and every KV head of a sequence shares its groups.
+    Position x of sequence b is cost unit x + seq_pad*b, in group
+    floor(((x + seq_pad*b + 1)*n - 1) / C)."""
     nnew = (NQ + 15) // 16
     nsub = [(min(max(int(L), 0), max_tokens) + 15) // 16 + nnew for L in context_lens]
-    W = sum(nsub)
-    n = min(n_grp, max(1, W // min_seg if min_seg > 1 else W))
+    C = sum(nsub) + seq_pad * len(nsub)
+    n = min(n_grp, max(1, C // min_seg if min_seg > 1 else C))
 
-    def group_of(x):
-        return ((x + 1) * n - 1) // W
+    def group_of(x, b):
+        return ((x + seq_pad * b + 1) * n - 1) // C
 
     out, start = set(), 0
     for b, m in enumerate(nsub):
-        if group_of(start) == group_of(start + m - 1):
+        if group_of(start, b) == group_of(start + m - 1, b):
             out.update((b, kh) for kh in range(KV))
         start += m
     return out

@@ -649,6 +649,38 @@ def test_combine_remerges_the_workspace(kernel):
     assert torch.equal(again, out)
 
 
+def test_combine_remerges_the_workspace_cooperative_auto_plan():
+    # 64 rows per KV head (the cooperative kernel) and the plan's own group
+    # count: each sequence also costs 3 positions of the cut (the
+    # cooperative family's fixed cost per sequence), which the model follows
+    lens = tuple(int(x) for x in np.random.default_rng(31).integers(0, 700, size=12))
+    w = to_device(P.small(B=12, H=16, KV=2, D=128, BS=16, NQ=8, causal=True, dtype="f16",
+                          lens=lens, seed=32))
+    table = torch.from_numpy(w.block_table).to(DEV)
+    lens_t = torch.from_numpy(w.context_lens).to(DEV)
+    dec = pa.Decoder(w.q, w.k_pool, table, max_context_len=w.max_context_len, causal=True,
+                     kernel=pa.PA_KERNEL_MFMA)
+    assert dec.partitions > 1
+    out = dec(w.q, w.k_pool, w.v_pool, table, lens_t, w.new_k, w.new_v, w.scale).clone()
+    torch.cuda.synchronize()
+    check(w, out)
+    s = w.spec
+    G = s.H // s.KV
+    whole = P.split_single_piece_units(w.context_lens, s.KV, s.NQ, dec.partitions,
+                                       dec.chunk_tokens // 16, s.max_blocks * s.BS, seq_pad=3)
+    merged = torch.zeros(s.B, s.H, dtype=torch.bool)
+    for b in range(s.B):
+        for h in range(s.H):
+            merged[b, h] = (b, h // G) not in whole
+    assert merged.any() and not merged.all()
+    again = out.clone()
+    again[merged.to(DEV)] = 0
+    pa.paged_attn_combine(dec.problem, lens_t, dec.workspace, dec.workspace_bytes, again,
+                          stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert torch.equal(again, out)
+
+
 def test_workspace_too_small_is_rejected():
     w = to_device(W.make_workload(SMALL[1], device="cpu"))
     table = torch.from_numpy(w.block_table).to(DEV)
