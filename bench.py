@@ -70,6 +70,134 @@ def measured_traffic(workload: str, kv_bytes: int):
     return entry.get("hbm_bytes_per_launch")
 
 
+def _counter_rows(d):
+    """Rows of a rocprofv3 --pmc run's counter CSV under directory d."""
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(rows, match):
+    """Mean Counter_Value per dispatch of the kernels whose name contains `match`."""
+    vals = {}
+    for r in rows:
+        if match in r["Kernel_Name"]:
+            vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return (sum(vals.values()) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def summarize_traffic(d: str):
+    """profiles/traffic_counters.json and a markdown table from the counter runs
+    under d: fetch_<workload>/ and write_<workload>/ (FETCH_SIZE, WRITE_SIZE of a
+    `--configs N --lean` bench run, its stdout JSON in <dir>.out), cal_fetch/ and
+    cal_write/ (a --calibrate-copy run: 256 MiB device copies). Counter KiB are
+    scaled by what the same counter reads for the copy."""
+    import statistics
+    cal = {}
+    for ctr, sub in (("FETCH_SIZE", "cal_fetch"), ("WRITE_SIZE", "cal_write")):
+        vals = {}
+        for r in _counter_rows(os.path.join(d, sub)):
+            vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        big = [v for v in vals.values() if v > 1024]  # the copies (setup kernels are tiny)
+        cal[ctr] = (256 << 20) / (statistics.median(big) * 1024)
+    out = {"kernel_source_sha": kernel_source_hash(), "copy_scale": cal,
+           "command_fetch": "rocprofv3 --pmc FETCH_SIZE -d <dir>/fetch_<workload> -o pmc "
+                            "--output-format csv -- python3 bench.py --configs N --headline N "
+                            "--lean --steps 10 --warmup 2 --repeats 1 --no-cpu-baseline",
+           "command_write": "(the same with --pmc WRITE_SIZE -d <dir>/write_<workload>)",
+           "command_calibration": "rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE -d <dir>/cal_fetch|"
+                                  "cal_write -o pmc --output-format csv -- python3 bench.py "
+                                  "--calibrate-copy",
+           "command_summary": "python3 bench.py --summarize-traffic <dir>"}
+    lines = ["| workload | kernel | dispatches | FETCH_SIZE KiB/dispatch (raw) | read bytes (scaled) "
+             "| WRITE_SIZE KiB/dispatch (raw) | written bytes (scaled) | algorithmic KV bytes "
+             "| read / algorithmic |", "|---|---|---|---|---|---|---|---|---|"]
+    for sub in sorted(os.listdir(d)):
+        if not sub.startswith("fetch_") or not os.path.isdir(os.path.join(d, sub)):
+            continue
+        name = sub[len("fetch_"):]
+        with open(os.path.join(d, sub + ".out")) as fh:
+            line = [l for l in fh.read().splitlines() if l.startswith("{")][-1]
+        kvb = json.loads(line)["configs"][name]["kv_bytes_per_step"]
+        frows = _counter_rows(os.path.join(d, sub))
+        wrows = _counter_rows(os.path.join(d, "write_" + name))
+        entry = {"kernel_source_sha": kernel_source_hash(), "kv_bytes": kvb}
+        total = 0.0
+        for kname, match in (("pass 1", "decode_"), ("combine", "combine_")):
+            fk, n = _per_dispatch(frows, match)
+            wk, _ = _per_dispatch(wrows, match)
+            if fk is None:
+                continue
+            rd, wr = fk * 1024 * cal["FETCH_SIZE"], (wk or 0.0) * 1024 * cal["WRITE_SIZE"]
+            entry[kname] = {"fetch_kib_raw": fk, "write_kib_raw": wk, "read_bytes": rd,
+                            "write_bytes": wr, "dispatches": n}
+            if kname == "pass 1":
+                total = rd + wr
+            lines.append(f"| {name} | {kname} | {n} | {fk:.1f} | {rd / 1e6:.2f} MB | {wk or 0:.1f} "
+                         f"| {wr / 1e6:.2f} MB | {kvb / 1e6:.2f} MB | "
+                         + (f"{rd / kvb:.3f} |" if kname == "pass 1" else "- |"))
+        entry["hbm_bytes_per_launch"] = total
+        out[name] = entry
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(f"kernel sources sha256[:16]: {kernel_source_hash()}")
+    print(f"copy calibration (256 MiB device copy, median dispatch): FETCH_SIZE x "
+          f"{cal['FETCH_SIZE']:.4f}, WRITE_SIZE x {cal['WRITE_SIZE']:.4f}\n")
+    print("\n".join(lines))
+
+
+def _kernel_name(name: str) -> str:
+    """The library's kernels as pa::name<args> when the trace gives them mangled
+    (template arguments: _Float16, bf16_t, float, integers, booleans)."""
+    import re
+    m = re.match(r"_ZN2pa(\d+)", name)
+    if not m:
+        return name
+    pos = m.end()
+    n = int(m.group(1))
+    base, pos = name[pos:pos + n], pos + n
+    if not name.startswith("I", pos):
+        return "pa::" + base
+    pos += 1
+    args = []
+    while pos < len(name) and name[pos] != "E":
+        for pat, fmt in ((r"DF16_", lambda g: "_Float16"), (r"NS_6bf16_tE", lambda g: "pa::bf16_t"),
+                         (r"f", lambda g: "float"), (r"Li(\d+)E", lambda g: g.group(1)),
+                         (r"Lb([01])E", lambda g: "true" if g.group(1) == "1" else "false")):
+            t = re.match(pat, name[pos:])
+            if t:
+                args.append(fmt(t))
+                pos += t.end()
+                break
+        else:
+            return name
+    return f"pa::{base}<{', '.join(args)}>"
+
+
+def summarize_trace(d: str):
+    """A markdown table of the kernel statistics of a rocprofv3 --kernel-trace
+    --stats run under d."""
+    import csv
+    import glob
+    f = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))[0]
+    with open(f, newline="") as fh:
+        rows = list(csv.DictReader(fh))
+    names = [_kernel_name(r["Name"]) for r in rows]
+    print("| kernel | calls | avg us | min us | max us | share of GPU time |")
+    print("|---|---|---|---|---|---|")
+    for r, name in zip(rows, names):
+        short = name.split("(")[0]
+        if short.startswith("void "):
+            short = short[5:]
+        print(f"| {short[:110]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+              f"{float(r['Percentage']):.1f}% |")
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -406,7 +534,19 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run device-to-device copies of a known size (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters of a profiler run)")
+    ap.add_argument("--summarize-traffic", metavar="DIR",
+                    help="write profiles/traffic_counters.json from the FETCH_SIZE / WRITE_SIZE "
+                         "counter runs under DIR and print their table (no GPU)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print the kernel statistics of a rocprofv3 kernel-trace run under DIR "
+                         "as a table (no GPU)")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -309,7 +309,11 @@ int pa_dense_attention_backward(const pa_dense_problem* problem, const void* q, 
                                 size_t workspace_bytes, pa_stream_t stream);
 
 /* Message of the last failing call on this thread ("" if none). Valid until the
- * next call on this thread. */
+ * next call on this thread. Each message names what was wrong and ends with
+ * what to verify, the form of the errors that the dispatch() function and the
+ * device checks of docs.rs page "onnxruntime-ep-mlx 0.31.1:
+ * src/ops/paged_attention.rs" return; here they are a pa_status code plus this
+ * thread-local text (no allocation is returned to the caller). */
 const char* paged_attn_last_error(void);
 
 /* ABI version of this header (major * 100 + minor). */

@@ -138,17 +138,19 @@ constexpr float kSlack = 8.0f;
 // sub-pages, so the waves that are behind are issued first (measured: multi-row
 // causal pass 1 68 -> 66 us, ragged serving 284 -> 281 us).
 struct ProgressPrio {
-    int level, t1, t2, t3;  // the positions where the level drops to 2, 1, 0
-    __device__ __forceinline__ explicit ProgressPrio(int n)
-        : level(3), t1(n / 4), t2(n / 2), t3(n - n / 4) {
+    int level, next, n;  // level holds while i < next = n * (4 - level) / 4
+    __device__ __forceinline__ explicit ProgressPrio(int n_total)
+        : level(3), next(n_total / 4), n(n_total) {
         __builtin_amdgcn_s_setprio(3);
     }
     __device__ __forceinline__ void update(int i) {
-        const int want = 3 - (i >= t1) - (i >= t2) - (i >= t3);
-        if (want == level) return;
-        level = want;
-        if (want == 2) __builtin_amdgcn_s_setprio(2);
-        else if (want == 1) __builtin_amdgcn_s_setprio(1);
+        if (i < next) return;  // one compare per sub-page; the rest three times a wave
+        do {
+            --level;
+            next = n * (4 - level) / 4;
+        } while (level > 0 && i >= next);
+        if (level == 2) __builtin_amdgcn_s_setprio(2);
+        else if (level == 1) __builtin_amdgcn_s_setprio(1);
         else __builtin_amdgcn_s_setprio(0);
     }
 };
