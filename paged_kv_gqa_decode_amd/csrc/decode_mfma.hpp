@@ -139,9 +139,9 @@ constexpr float kSlack = 8.0f;
 // causal pass 1 68 -> 66 us, ragged serving 284 -> 281 us).
 struct ProgressPrio {
     int level, next, n;  // level holds while i < next = n * (4 - level) / 4
-    __device__ __forceinline__ explicit ProgressPrio(int n_total)
+    __device__ __forceinline__ ProgressPrio(int n_total, bool on)
         : level(3), next(n_total / 4), n(n_total) {
-        __builtin_amdgcn_s_setprio(3);
+        if (on) __builtin_amdgcn_s_setprio(3);
     }
     __device__ __forceinline__ void update(int i) {
         if (i < next) return;  // one compare per sub-page; the rest three times a wave
@@ -964,9 +964,9 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table,
     bool piece_from_start = cc.j == 0;
     bool q_pending = true;   // load_q issued, q_ready not yet called
     int q_younger = NS;      // fetches issued after the pending Q loads (upper bound)
-    ProgressPrio prio(n_total);
+    ProgressPrio prio(n_total, !APPEND);
     for (int i = 0; i < n_total; ++i) {
-        prio.update(i);
+        if constexpr (!APPEND) prio.update(i);  // the slot-patched step measured better without
         const bool more = i + 1 < n_total;
         if (cc.j == 0 && kh == 0 && lane == 0 && a.meta) {
             // the first piece of a sequence records the groups it spans
@@ -1124,9 +1124,9 @@ void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table,
     bool q_pending = has_rows;  // load_q issued, q_ready not yet called
     bool q_drain = false;       // pending Q is younger than the ring's loads
     bool piece_from_start = cc.j == 0;
-    ProgressPrio prio(n_total);
+    ProgressPrio prio(n_total, !APPEND);
     for (int i = 0; i < n_total; ++i) {
-        prio.update(i);
+        if constexpr (!APPEND) prio.update(i);  // the slot-patched step measured better without
         const int ahead = min(kRing - 2, n_total - 1 - i);  // sub-pages fetched after i
         if (cc.j == 0 && lane == 0 && wave == 0 && kh == 0 && a.meta) {
             const int64_t s0 = seq.pref(cc.b);
