@@ -901,24 +901,31 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
 // before the arithmetic; otherwise after the scores, so that the next
 // sequence's Q, loaded after the scores, is older than the refill), then
 // computes. NS sub-pages per wave stay in flight.
-template <typename T, int D, int BS, int NRT, int NS, int WPS, bool APPEND>
+template <typename T, int D, int BS, int NRT, int NS, int WPS, bool APPEND, bool REGSEQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPS, WPS)))
 void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table,
                  const int32_t* __restrict__ slots) {
     using Lay = SlotLayout<T, D>;
-    using Stream = SubPageStream<T, D, BS>;
+    using Seq = typename std::conditional<REGSEQ, SeqTableRegs, SeqTableLds>::type;
+    using Stream = SubPageStream<T, D, BS, Seq>;
     using Rows = RowTiles<T, D, NRT>;
     using Cur = typename Stream::Cur;
     constexpr int KS = D / 32;
     static_assert(D % 32 == 0 && BS % 16 == 0 && Lay::kOps == KS, "shape");
     static_assert(Stream::kOps * (NS - 1) <= 63, "vmcnt range");
 
-    // LDS: per wave NS slots, then the prefix and lengths.
+    // LDS: per wave NS slots, then (REGSEQ false) the prefix and lengths.
     extern __shared__ __attribute__((aligned(1024))) char smem[];  // slots start 1 KiB aligned (XOR addressing)
-    int* s_pref = reinterpret_cast<int*>(smem + 4 * NS * Lay::kBytes);
-    int* s_len = s_pref + a.g.B + 1;
-    build_prefix(a.context_lens, a.g, s_pref, s_len);
-    const SeqTableLds seq{s_pref, s_len, a.g.B};
+    const Seq seq = [&]() {
+        if constexpr (REGSEQ) {
+            return SeqTableRegs(a.context_lens, a.g);  // each wave its own copy: no barrier
+        } else {
+            int* s_pref = reinterpret_cast<int*>(smem + 4 * NS * Lay::kBytes);
+            int* s_len = s_pref + a.g.B + 1;
+            build_prefix(a.context_lens, a.g, s_pref, s_len);
+            return SeqTableLds{s_pref, s_len, a.g.B};
+        }
+    }();
     const Cut cut(a.g, seq.total());
 
     // The wave index is uniform within a wave; saying so keeps every per-wave

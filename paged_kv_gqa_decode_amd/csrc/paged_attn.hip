@@ -152,7 +152,9 @@ struct Plan {
 //           sharing a ring of slots: five when the batch's sequence table fits
 //           in registers (batch <= 64: no LDS beside the ring, so four
 //           workgroups of five slots fill the CU's 160 KiB), else four;
-// all at 2 waves per SIMD, each keeping about 128 KiB of sub-pages in flight
+// batches of at most 64 sequences keep the sequence table in registers in every
+// shape (each wave loads and scans the lengths itself: no barrier before the
+// first fetch); all at 2 waves per SIMD, each keeping about 128 KiB of sub-pages in flight
 // per CU (slots double for D = 64, whose slots are half as large). Measured
 // on the Llama-3-8B-shaped and ragged-serving workloads: 2 waves per SIMD with
 // 2 slots each beat 4 waves with 1 slot (oldest waves hog the memory path,
@@ -170,8 +172,8 @@ struct MfmaShape {
 bool regseq_batch(const pa_problem* p) { return p->batch <= pa::kRegTableMaxBatch; }
 MfmaShape mfma_shape(const pa_problem* p, int rt) {
     const int s1 = p->head_dim == 128 ? 1 : 2;  // a D = 64 slot is half as large
-    if (rt == 1) return {1, 1, 2 * s1, 2, false};
-    if (rt == 2) return {1, 2, 2 * s1, 2, false};
+    if (rt == 1) return {1, 1, 2 * s1, 2, regseq_batch(p)};
+    if (rt == 2) return {1, 2, 2 * s1, 2, regseq_batch(p)};
     if (regseq_batch(p)) return {2, 2, 5 * s1, 2, true};
     return {2, 2, 4 * s1, 2, false};
 }
@@ -407,15 +409,22 @@ void launch_mfma_k(const pa_problem* p, const Plan& pl, size_t lds, hipStream_t 
                    const pa::SplitArgs<T>& a, const int32_t* table) {
     constexpr int S1 = D == 128 ? 1 : 2;  // slot counts of mfma_shape
     const int64_t streams = (int64_t)pl.parts * p->num_kv_heads;
-    if (pl.rt == 1) {
+    const bool regseq = regseq_batch(p);
+    if (pl.rt <= 2) {
         const dim3 grid((unsigned)ceil_div(streams, 4));
-        hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 1, 2 * S1, 2, APPEND>), grid, dim3(256), lds,
-                           s, a, table, a.ap.slots);
-    } else if (pl.rt == 2) {
-        const dim3 grid((unsigned)ceil_div(streams, 4));
-        hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 2, 2 * S1, 2, APPEND>), grid, dim3(256), lds,
-                           s, a, table, a.ap.slots);
-    } else if (regseq_batch(p)) {
+        if (pl.rt == 1 && regseq)
+            hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 1, 2 * S1, 2, APPEND, true>), grid,
+                               dim3(256), lds, s, a, table, a.ap.slots);
+        else if (pl.rt == 1)
+            hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 1, 2 * S1, 2, APPEND, false>), grid,
+                               dim3(256), lds, s, a, table, a.ap.slots);
+        else if (regseq)
+            hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 2, 2 * S1, 2, APPEND, true>), grid,
+                               dim3(256), lds, s, a, table, a.ap.slots);
+        else
+            hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 2, 2 * S1, 2, APPEND, false>), grid,
+                               dim3(256), lds, s, a, table, a.ap.slots);
+    } else if (regseq) {
         hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2, 2, 5 * S1, 2, APPEND, true>),
                            dim3((unsigned)streams), dim3(128), lds, s, a, table, a.ap.slots);
     } else {

@@ -160,11 +160,14 @@ def test_geometries(case):
 
 
 @pytest.mark.parametrize("B,dtype", [(1, "f16"), (64, "bf16"), (65, "f16"), (130, "bf16")])
-def test_cooperative_kernel_sequence_tables(B, dtype):
-    # 64 rows per KV head (the cooperative kernel): batches of up to 64
-    # sequences keep the sequence table in registers, larger ones in LDS
+@pytest.mark.parametrize("rows", [4, 24, 64])
+def test_sequence_tables(B, dtype, rows):
+    # batches of up to 64 sequences keep the sequence table in registers,
+    # larger ones in LDS; 4 rows per KV head: the one-wave kernel with one row
+    # tile, 24: with two, 64: the cooperative kernel
+    H, NQ = {4: (8, 1), 24: (16, 3), 64: (16, 8)}[rows]
     lens = tuple(int(x) for x in np.random.default_rng(B).integers(0, 200, size=B))
-    w = to_device(P.small(B=B, H=16, KV=2, D=128, BS=16, NQ=8, causal=True, dtype=dtype,
+    w = to_device(P.small(B=B, H=H, KV=2, D=128, BS=16, NQ=NQ, causal=True, dtype=dtype,
                           lens=lens, seed=23))
     expect = ref(w)
     for parts in (0, 1, 3, 40):
