@@ -94,12 +94,13 @@ namespace pa {
 // The merge is PARTIALS_REDUCE of the docs.rs page "onnxruntime-ep-mlx 0.31.1:
 // src/ops/paged_attention.rs" in base 2: out = sum_g 2^(m_g - M) o_g /
 // sum_g 2^(m_g - M) l_g with M = max_g m_g.
-// WPR waves share one output row (WPR = 1: a workgroup takes 4 rows of a
-// (sequence, head); WPR = 4: one row, its pieces dealt to 4 waves in contiguous
-// runs and the four partial merges combined through LDS). Each wave loads the
-// (m, l) of up to 64 pieces lane-parallel and the partial outputs of up to
-// kBatch pieces at once, so a row costs two dependent memory latencies after
-// the metadata.
+// WPR waves share one output row (WPR = 1: a workgroup takes 4*RPW rows of a
+// (sequence, head), RPW per wave; WPR = 4: one row, its pieces dealt to 4 waves
+// in contiguous runs and the four partial merges combined through LDS). Each
+// wave loads the (m, l) of up to 64 pieces lane-parallel and the partial outputs
+// of up to kBatch pieces at once, for all of its rows before any is reduced, so
+// a wave's rows cost two dependent memory latencies after the metadata together
+// (RPW = 2: half the waves, each with twice the loads in flight).
 template <typename T>
 struct SplitCombineArgs {
     const typename Partial<T>::type* ws_o;  // [slots][R][D] (Partial<T>)
@@ -127,99 +128,126 @@ __device__ __forceinline__ void load_partial(const _Float16* src, float (&o)[PER
     }
 }
 
-template <typename T, int D, int WPR>
+template <typename T, int D, int WPR, int RPW = 1>
 __global__ __launch_bounds__(256) void combine_split(SplitCombineArgs<T> a) {
     using E = Elem<T>;
     constexpr int PER = D / 64;      // output elements per lane
-    constexpr int kBatch = 16;       // partial outputs in flight per wave
-    constexpr int RPB = 4 / WPR;     // rows per workgroup
-    static_assert(D % 64 == 0 && (WPR == 1 || WPR == 4), "shape");
+    constexpr int kBatch = 16;       // partial outputs in flight per wave and row
+    constexpr int RPB = 4 * RPW / WPR;  // rows per workgroup
+    static_assert(D % 64 == 0 && (WPR == 1 || (WPR == 4 && RPW == 1)), "shape");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int R = a.R;
     const int tiles = (R + RPB - 1) / RPB;
     const int64_t u = blockIdx.x / tiles;  // b * KV + kh
-    const int rho = (int)(blockIdx.x % tiles) * RPB + (WPR == 1 ? wave : 0);
+    const int rho0 = (int)(blockIdx.x % tiles) * RPB + (WPR == 1 ? wave * RPW : 0);
     const int64_t b = u / a.KV;
     const int s0 = a.meta[2 * b], s1 = a.meta[2 * b + 1];
     if (s0 == s1) return;  // finished by pass 1 (whole workgroup)
     const int n = s1 - s0 + 1;
-    const bool active = rho < R;  // WPR = 1: the last tile of rows may be short
+    // WPR = 1: rows past R (the last tile may be short) read row R - 1 and store nothing
+    bool active[RPW];
+    int rho[RPW];
+    bool any = false;
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+        active[k] = rho0 + k < R;
+        rho[k] = min(rho0 + k, R - 1);
+        any = any || active[k];
+    }
     // this wave's pieces [p0, p1) of the row
     const int per_w = (n + WPR - 1) / WPR;
     const int p0 = WPR == 1 ? 0 : min(n, wave * per_w), p1 = WPR == 1 ? n : min(n, p0 + per_w);
     const int64_t first = (b + s0) * a.KV + (u - b * a.KV);  // slot of piece g0
-    const float* ml = a.ws_ml + (first * R + rho) * 2;
-    const auto* po = a.ws_o + (first * R + rho) * D + lane * PER;
+    const float* ml[RPW];
+    const typename Partial<T>::type* po[RPW];
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+        ml[k] = a.ws_ml + (first * R + rho[k]) * 2;
+        po[k] = a.ws_o + (first * R + rho[k]) * D + lane * PER;
+    }
     // consecutive groups of one (sequence, head) are KV slots apart
     const int64_t mstride = (int64_t)a.KV * R * 2, ostride = (int64_t)a.KV * R * D;
 
-    float M = kNegMax, Lw = 0.f;
-    float acc[PER];
+    float M[RPW], Lw[RPW];
+    float acc[RPW][PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    if (active) {
+    for (int k = 0; k < RPW; ++k) {
+        M[k] = kNegMax;
+        Lw[k] = 0.f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[k][e] = 0.f;
+    }
+    auto load_batch = [&](int k, int c0, int j0, int cn, float (&ov)[kBatch][PER]) {
+        // (fp16: pieces past the run read the last one again, with weight 0)
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if constexpr (Partial<T>::kNorm)
+                load_partial<PER>(po[k] + (c0 + min(j0 + j, cn - 1)) * ostride, ov[j]);
+            else
+#pragma unroll
+                for (int e = 0; e < PER; ++e)
+                    ov[j][e] = j0 + j < cn ? po[k][(c0 + j0 + j) * ostride + e] : 0.f;
+        }
+    };
+    if (WPR == 4 || any) {
         for (int c0 = p0; c0 < p1; c0 += 64) {  // runs of up to 64 pieces
             const int cn = min(64, p1 - c0);
-            // partial outputs of the first batch, issued before the (m, l) are used
-            float ov[kBatch][PER];
-            // (fp16: pieces past the run read the last one again, with weight 0)
+            // partial outputs of every row's first batch, issued before the (m, l) are used
+            float ov[RPW][kBatch][PER];
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                if constexpr (Partial<T>::kNorm)
-                    load_partial<PER>(po + (c0 + min(j, cn - 1)) * ostride, ov[j]);
-                else
-#pragma unroll
-                    for (int e = 0; e < PER; ++e)
-                        ov[j][e] = j < cn ? po[(c0 + j) * ostride + e] : 0.f;
-            }
+            for (int k = 0; k < RPW; ++k) load_batch(k, c0, 0, cn, ov[k]);
             const bool mine = lane < cn;
-            const float mp = mine ? ml[(c0 + lane) * mstride] : kNegMax;
-            const float lp = mine ? ml[(c0 + lane) * mstride + 1] : 0.f;
-            const float Mr = wave_max(mp);
-            const float Mn = fmaxf(M, Mr);
-            const float sc = fast_exp2(M - Mn);  // rescale what earlier runs gathered
-            Lw *= sc;
+            float mp[RPW], lp[RPW], wo[RPW];
 #pragma unroll
-            for (int e = 0; e < PER; ++e) acc[e] *= sc;
-            M = Mn;
-            const float wp = mine ? fast_exp2(mp - M) : 0.f;
-            Lw += wave_sum(wp * lp);
-            const float wo = Partial<T>::kNorm ? wp * lp : wp;  // weight of the stored o
+            for (int k = 0; k < RPW; ++k) {
+                mp[k] = mine ? ml[k][(c0 + lane) * mstride] : kNegMax;
+                lp[k] = mine ? ml[k][(c0 + lane) * mstride + 1] : 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < RPW; ++k) {
+                const float Mr = wave_max(mp[k]);
+                const float Mn = fmaxf(M[k], Mr);
+                const float sc = fast_exp2(M[k] - Mn);  // rescale what earlier runs gathered
+                Lw[k] *= sc;
+#pragma unroll
+                for (int e = 0; e < PER; ++e) acc[k][e] *= sc;
+                M[k] = Mn;
+                const float wp = mine ? fast_exp2(mp[k] - M[k]) : 0.f;
+                Lw[k] += wave_sum(wp * lp[k]);
+                wo[k] = Partial<T>::kNorm ? wp * lp[k] : wp;  // weight of the stored o
+            }
             for (int j0 = 0; j0 < cn; j0 += kBatch) {
                 if (j0 > 0) {
 #pragma unroll
+                    for (int k = 0; k < RPW; ++k) load_batch(k, c0, j0, cn, ov[k]);
+                }
+#pragma unroll
+                for (int k = 0; k < RPW; ++k)
+#pragma unroll
                     for (int j = 0; j < kBatch; ++j) {
-                        if constexpr (Partial<T>::kNorm)
-                            load_partial<PER>(po + (c0 + min(j0 + j, cn - 1)) * ostride, ov[j]);
-                        else
+                        // weight of piece j0 + j (lane j0 + j; 0 past the run's end)
+                        const float w = __builtin_bit_cast(
+                            float,
+                            __builtin_amdgcn_readlane(__builtin_bit_cast(int, wo[k]), (j0 + j) & 63));
 #pragma unroll
-                            for (int e = 0; e < PER; ++e)
-                                ov[j][e] = j0 + j < cn ? po[(c0 + j0 + j) * ostride + e] : 0.f;
+                        for (int e = 0; e < PER; ++e) acc[k][e] = fmaf(w, ov[k][j][e], acc[k][e]);
                     }
-                }
-#pragma unroll
-                for (int j = 0; j < kBatch; ++j) {
-                    // weight of piece j0 + j (lane j0 + j; 0 past the run's end)
-                    const float w = __builtin_bit_cast(
-                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wo), (j0 + j) & 63));
-#pragma unroll
-                    for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, ov[j][e], acc[e]);
-                }
             }
         }
     }
+    const int kh = (int)(u % a.KV);
     if constexpr (WPR == 4) {
         __shared__ float s_m[4], s_l[4];
         __shared__ float s_o[4][D];
         if (lane == 0) {
-            s_m[wave] = M;
-            s_l[wave] = Lw;
+            s_m[wave] = M[0];
+            s_l[wave] = Lw[0];
         }
 #pragma unroll
-        for (int e = 0; e < PER; ++e) s_o[wave][lane * PER + e] = acc[e];
+        for (int e = 0; e < PER; ++e) s_o[wave][lane * PER + e] = acc[0][e];
         __syncthreads();
-        if (active && threadIdx.x < D) {
+        if (threadIdx.x < D) {
             const int d = threadIdx.x;
             const float Mt = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
             float o = 0.f, lt = 0.f;
@@ -229,16 +257,18 @@ __global__ __launch_bounds__(256) void combine_split(SplitCombineArgs<T> a) {
                 o = fmaf(f, s_o[w][d], o);
                 lt = fmaf(f, s_l[w], lt);
             }
-            const int b = (int)(u / a.KV), kh = (int)(u % a.KV);
-            const int64_t grow = ((int64_t)b * a.H + (int64_t)kh * (a.H / a.KV)) * a.NQ + rho;
+            const int64_t grow = (b * a.H + (int64_t)kh * (a.H / a.KV)) * a.NQ + rho[0];
             E::store(a.out + grow * D + d, lt != 0.f ? o / lt : 0.f);
         }
-    } else if (active) {
-        const int b = (int)(u / a.KV), kh = (int)(u % a.KV);
-        const int64_t grow = ((int64_t)b * a.H + (int64_t)kh * (a.H / a.KV)) * a.NQ + rho;
-        T* dst = a.out + grow * D + lane * PER;
+    } else {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) E::store(dst + e, Lw != 0.f ? acc[e] / Lw : 0.f);
+        for (int k = 0; k < RPW; ++k) {
+            if (!active[k]) continue;
+            const int64_t grow = (b * a.H + (int64_t)kh * (a.H / a.KV)) * a.NQ + rho[k];
+            T* dst = a.out + grow * D + lane * PER;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) E::store(dst + e, Lw[k] != 0.f ? acc[k][e] / Lw[k] : 0.f);
+        }
     }
 }
 

@@ -146,6 +146,9 @@ GEOMETRIES = [
     (2, 4, 4, 128, 16, 32, True, "f16", (0, 77)),      # MHA, NQ = 32: two row tiles
     (2, 8, 4, 64, 32, 20, True, "bf16", (45, 300)),    # G = 2, NQ = 20: cooperative kernel
     (2, 4, 2, 128, 16, 24, False, "f16", (19, 130)),   # G = 2, NQ = 24, non-causal
+    # 36 and 33 rows: the merge's last tile of 8 rows (two per wave) is short
+    (2, 8, 2, 64, 16, 9, True, "f16", (33, 210)),
+    (3, 6, 2, 128, 32, 11, True, "bf16", (0, 140, 77)),
 ]
 
 
