@@ -128,11 +128,11 @@ __device__ __forceinline__ void load_partial(const _Float16* src, float (&o)[PER
     }
 }
 
-template <typename T, int D, int WPR, int RPW = 1>
+template <typename T, int D, int WPR, int RPW = 1, int kBatch = 16>
 __global__ __launch_bounds__(256) void combine_split(SplitCombineArgs<T> a) {
     using E = Elem<T>;
     constexpr int PER = D / 64;      // output elements per lane
-    constexpr int kBatch = 16;       // partial outputs in flight per wave and row
+    // kBatch: partial outputs in flight per wave and row
     constexpr int RPB = 4 * RPW / WPR;  // rows per workgroup
     static_assert(D % 64 == 0 && (WPR == 1 || (WPR == 4 && RPW == 1)), "shape");
     const int lane = threadIdx.x & 63;

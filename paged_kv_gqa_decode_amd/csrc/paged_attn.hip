@@ -539,12 +539,20 @@ void launch_combine(const pa_problem* p, const Plan& pl, hipStream_t s, const fl
                 hipLaunchKernelGGL((pa::combine_split<T, 64, 1, 2>), grid, dim3(256), 0, s, c);
             else
                 hipLaunchKernelGGL((pa::combine_split<T, 128, 1, 2>), grid, dim3(256), 0, s, c);
-        } else {
+        } else if (pieces > 8) {
             const dim3 grid((unsigned)(units * ((c.R + 3) / 4)));
             if (p->head_dim == 64)
                 hipLaunchKernelGGL((pa::combine_split<T, 64, 1>), grid, dim3(256), 0, s, c);
             else
                 hipLaunchKernelGGL((pa::combine_split<T, 128, 1>), grid, dim3(256), 0, s, c);
+        } else {
+            // few pieces per row: batches of 8 keep the waves small (38 VGPRs on
+            // ragged serving, 8 waves per SIMD): its merge 10.7 -> 8.6 us
+            const dim3 grid((unsigned)(units * ((c.R + 3) / 4)));
+            if (p->head_dim == 64)
+                hipLaunchKernelGGL((pa::combine_split<T, 64, 1, 1, 8>), grid, dim3(256), 0, s, c);
+            else
+                hipLaunchKernelGGL((pa::combine_split<T, 128, 1, 1, 8>), grid, dim3(256), 0, s, c);
         }
         return;
     }

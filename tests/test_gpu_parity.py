@@ -177,6 +177,17 @@ def test_sequence_tables(B, dtype, rows):
         check(w, gpu_decode(w, num_partitions=parts), expect)
 
 
+@pytest.mark.parametrize("B,parts,dtype", [(9, 40, "bf16"), (20, 150, "f16"), (9, 100, "f16")])
+def test_merge_of_many_pieces(B, parts, dtype):
+    # one long sequence among short ones: the merge picks its batch of pieces
+    # from groups / sequences + 1 (here 5, 8 and 12), while the long sequence
+    # has about `parts` pieces: several batches per run, and runs of 64 pieces
+    lens = (5000,) + tuple(range(3, 3 + 2 * (B - 1), 2))
+    w = to_device(P.small(B=B, H=8, KV=2, D=128, BS=16, NQ=1, causal=True, dtype=dtype,
+                          lens=lens, seed=41))
+    check(w, gpu_decode(w, num_partitions=parts))
+
+
 def test_many_short_sequences():
     # 4200 sequences of 0..39 cached keys: an LDS prefix of 33 KiB beside the
     # slots, most sequences inside one group, several per wave
