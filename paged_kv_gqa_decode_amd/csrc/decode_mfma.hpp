@@ -971,9 +971,9 @@ void decode_mfma(SplitArgs<T> a, const int32_t* __restrict__ table,
     bool piece_from_start = cc.j == 0;
     bool q_pending = true;   // load_q issued, q_ready not yet called
     int q_younger = NS;      // fetches issued after the pending Q loads (upper bound)
-    ProgressPrio prio(n_total, !APPEND);
+    ProgressPrio prio(n_total, true);
     for (int i = 0; i < n_total; ++i) {
-        if constexpr (!APPEND) prio.update(i);  // the slot-patched step measured better without
+        prio.update(i);
         const bool more = i + 1 < n_total;
         if (cc.j == 0 && kh == 0 && lane == 0 && a.meta) {
             // the first piece of a sequence records the groups it spans
@@ -1133,7 +1133,7 @@ void decode_mfma_coop(SplitArgs<T> a, const int32_t* __restrict__ table,
     bool piece_from_start = cc.j == 0;
     ProgressPrio prio(n_total, !APPEND);
     for (int i = 0; i < n_total; ++i) {
-        if constexpr (!APPEND) prio.update(i);  // the slot-patched step measured better without
+        if constexpr (!APPEND) prio.update(i);  // the slot-patched cooperative step measured better without
         const int ahead = min(kRing - 2, n_total - 1 - i);  // sub-pages fetched after i
         if (cc.j == 0 && lane == 0 && wave == 0 && kh == 0 && a.meta) {
             const int64_t s0 = seq.pref(cc.b);
