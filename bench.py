@@ -550,7 +550,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build runs every kernel on a single "
+        print("bench.py measures one GPU only: the library runs every kernel on a single "
               "MI355X and has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
