@@ -10,6 +10,8 @@ bit-exact: outputs for the same logical cache stored in another physical block
 order are compared with torch.equal, and poisoned (NaN) unused pool space must
 not change a bit.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -615,6 +617,23 @@ def test_equal_scores_give_the_mean():
     wd = to_device(w)
     expect = ref(w)
     for parts in (1, 4):
+        check(wd, gpu_decode(wd, num_partitions=parts), expect)
+
+
+# scale 0 (every visible key weighted equally: the mean of V), a negative scale
+# (the row max is the most negative q.k) and a sharp one, on every decode family:
+# one-wave matrix-core kernel (R = 4), its two-tile form (R = 24), the
+# cooperative kernel (R = 64), the 16-bit vector kernel (R = 128), fp32 vector
+@pytest.mark.parametrize("H,KV,NQ,dtype", [(8, 2, 1, "f16"), (16, 2, 3, "bf16"), (16, 2, 8, "f16"),
+                                           (32, 2, 8, "bf16"), (8, 2, 1, "f32")])
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.6])
+def test_scale_edge_cases(H, KV, NQ, dtype, scale):
+    w = P.small(B=3, H=H, KV=KV, D=128, NQ=NQ, causal=True, lens=(0, 77, 300), dtype=dtype,
+                seed=21)
+    w = dataclasses.replace(w, scale=float(np.float32(scale)))
+    wd = to_device(w)
+    expect = ref(w)
+    for parts in (0, 5):
         check(wd, gpu_decode(wd, num_partitions=parts), expect)
 
 
