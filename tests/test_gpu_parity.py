@@ -179,6 +179,22 @@ def test_sequence_tables(B, dtype, rows):
         check(w, gpu_decode(w, num_partitions=parts), expect)
 
 
+# The batch limits of the balanced split: 8192 sequences (the largest batch the
+# matrix-core kernels take; the sequence table then fills 64 KiB of LDS beside
+# the slots), for the one-wave and the cooperative kernel, and 8193 (the plan
+# moves to the vector kernel)
+@pytest.mark.parametrize("B,H,NQ,dtype", [(8192, 8, 1, "f16"), (8192, 16, 8, "bf16"),
+                                          (8193, 8, 1, "bf16")])
+def test_batch_limits(B, H, NQ, dtype):
+    lens = np.random.default_rng(B + NQ).integers(0, 41, size=B)
+    w = P.small(B=B, H=H, KV=2, D=128, NQ=NQ, causal=True, lens=tuple(lens), dtype=dtype,
+                seed=23)
+    wd = to_device(w)
+    expect = ref(w)
+    for parts in (0, 3):
+        check(wd, gpu_decode(wd, num_partitions=parts), expect)
+
+
 @pytest.mark.parametrize("B,parts,dtype", [(9, 40, "bf16"), (20, 150, "f16"), (9, 100, "f16")])
 def test_merge_of_many_pieces(B, parts, dtype):
     # one long sequence among short ones: the merge picks its batch of pieces
