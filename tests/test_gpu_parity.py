@@ -166,13 +166,15 @@ def test_geometries(case):
 
 @pytest.mark.parametrize("B,dtype", [(1, "f16"), (64, "bf16"), (65, "f16"), (130, "bf16")])
 @pytest.mark.parametrize("rows", [4, 24, 64])
-def test_sequence_tables(B, dtype, rows):
+@pytest.mark.parametrize("D,BS", [(128, 16), (64, 32)])
+def test_sequence_tables(B, dtype, rows, D, BS):
     # batches of up to 64 sequences keep the sequence table in registers,
     # larger ones in LDS; 4 rows per KV head: the one-wave kernel with one row
-    # tile, 24: with two, 64: the cooperative kernel
+    # tile, 24: with two, 64: the cooperative kernel; D = 64 slots are half as
+    # large, so those kernels hold twice as many
     H, NQ = {4: (8, 1), 24: (16, 3), 64: (16, 8)}[rows]
     lens = tuple(int(x) for x in np.random.default_rng(B).integers(0, 200, size=B))
-    w = to_device(P.small(B=B, H=H, KV=2, D=128, BS=16, NQ=NQ, causal=True, dtype=dtype,
+    w = to_device(P.small(B=B, H=H, KV=2, D=D, BS=BS, NQ=NQ, causal=True, dtype=dtype,
                           lens=lens, seed=23))
     expect = ref(w)
     for parts in (0, 1, 3, 40):
