@@ -224,6 +224,7 @@ def test_many_short_sequences():
 # Slot-patched step (paged_attn_decode_append): out against the oracle, and
 # the pools afterwards bit for bit against the oracle's stored rows
 # ---------------------------------------------------------------------------
+_LENS70 = tuple(int(x) for x in np.random.default_rng(70).integers(0, 60, size=70))
 APPEND_GPU = [
     # B, H, KV, D, BS, NQ, causal, dtype, lens, kernel
     (3, 8, 2, 128, 16, 1, True, "f16", (0, 15, 300), pa.PA_KERNEL_MFMA),    # one row tile
@@ -234,6 +235,10 @@ APPEND_GPU = [
     (2, 8, 2, 128, 32, 3, False, "f16", (31, 64), pa.PA_KERNEL_VALU),       # forced vector ALU
     (2, 4, 4, 128, 16, 32, True, "f16", (3, 77), pa.PA_KERNEL_MFMA),       # NQ = 32: two sub-pages
     (2, 8, 4, 64, 32, 20, True, "bf16", (45, 300), pa.PA_KERNEL_MFMA),     # NQ = 20, cooperative
+    # 70 sequences: the sequence table in LDS (one tile, two tiles, cooperative)
+    (70, 8, 2, 128, 16, 1, True, "f16", _LENS70, pa.PA_KERNEL_MFMA),
+    (70, 16, 2, 128, 16, 3, True, "bf16", _LENS70, pa.PA_KERNEL_MFMA),
+    (70, 16, 2, 64, 32, 8, True, "f16", _LENS70, pa.PA_KERNEL_MFMA),
 ]
 APPEND_SCENARIOS = {
     "natural": dict(seed=3),
