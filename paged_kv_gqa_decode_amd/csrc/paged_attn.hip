@@ -149,13 +149,13 @@ struct Plan {
 //   rt = 1: decode_mfma, one wave per (group, head) with one row tile;
 //   rt = 2: decode_mfma with two row tiles per wave;
 //   rt = 4: decode_mfma_coop, two waves of two row tiles per (group, head)
-//           sharing a ring of slots: five when the batch's sequence table fits
-//           in registers (batch <= 64: no LDS beside the ring, so four
-//           workgroups of five slots fill the CU's 160 KiB), else four;
+//           sharing a ring of three slots (four workgroups per CU, set by
+//           registers; three slots ran 1-3 % faster than four and five on
+//           batches of 16, 128 and 256 sequences);
 // batches of at most 64 sequences keep the sequence table in registers in every
 // shape (each wave loads and scans the lengths itself: no barrier before the
-// first fetch); all at 2 waves per SIMD, each keeping about 128 KiB of sub-pages in flight
-// per CU (slots double for D = 64, whose slots are half as large). Measured
+// first fetch); all at 2 waves per SIMD (slots double for D = 64, whose slots
+// are half as large). Measured
 // on the Llama-3-8B-shaped and ragged-serving workloads: 2 waves per SIMD with
 // 2 slots each beat 4 waves with 1 slot (oldest waves hog the memory path,
 // the last quarter of the kernel runs thin) and 1 wave with 4 slots; for 64
@@ -174,8 +174,7 @@ MfmaShape mfma_shape(const pa_problem* p, int rt) {
     const int s1 = p->head_dim == 128 ? 1 : 2;  // a D = 64 slot is half as large
     if (rt == 1) return {1, 1, 2 * s1, 2, regseq_batch(p)};
     if (rt == 2) return {1, 2, 2 * s1, 2, regseq_batch(p)};
-    if (regseq_batch(p)) return {2, 2, 5 * s1, 2, true};
-    return {2, 2, 4 * s1, 2, false};
+    return {2, 2, 3 * s1, 2, regseq_batch(p)};
 }
 int mfma_slot_bytes(int head_dim) {
     return head_dim == 64 ? pa::SlotLayout<_Float16, 64>::kBytes
@@ -425,10 +424,10 @@ void launch_mfma_k(const pa_problem* p, const Plan& pl, size_t lds, hipStream_t 
             hipLaunchKernelGGL((pa::decode_mfma<T, D, BS, 2, 2 * S1, 2, APPEND, false>), grid,
                                dim3(256), lds, s, a, table, a.ap.slots);
     } else if (regseq) {
-        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2, 2, 5 * S1, 2, APPEND, true>),
+        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2, 2, 3 * S1, 2, APPEND, true>),
                            dim3((unsigned)streams), dim3(128), lds, s, a, table, a.ap.slots);
     } else {
-        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2, 2, 4 * S1, 2, APPEND, false>),
+        hipLaunchKernelGGL((pa::decode_mfma_coop<T, D, BS, 2, 2, 3 * S1, 2, APPEND, false>),
                            dim3((unsigned)streams), dim3(128), lds, s, a, table, a.ap.slots);
     }
 }
